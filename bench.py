@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""HGA hot-path benchmark on one MI355X.
+
+One step = one whole segmented pass of one attention layer over the
+16,384-token training workload (Qwen3-8B attention shape: 32 query heads,
+8 KV heads, head_dim 128; segments of 1,024, history blocks of 64, top-k
+32): for every segment, summarize the newly closed blocks, select, forward
+and backward, through hga_segment_step.  Inputs are synthetic
+(planted-direction N(0,1), seeded) and already resident in HBM when the
+timed region starts.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HGA fwd+bwd tokens/s per layer at 16K (Qwen3-8B shape); % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="train_16k")
+    ap.add_argument("--mode", default="planted", choices=["planted", "diverse"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense-self", action="store_true")
+    ap.add_argument("--dense-sdpa", action="store_true",
+                    help="also time torch SDPA (flash backend) dense causal fwd+bwd")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    return ap.parse_args()
+
+
+def timed_passes(buf, dev, bwd, n, profile_classes=None):
+    import torch
+    import sparse_long_context_query_amd as hga
+    torch.cuda.synchronize()
+    if profile_classes:
+        hga.profile_begin(profile_classes)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(n):
+        buf.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=bwd)
+    end.record()
+    torch.cuda.synchronize()
+    prof = hga.profile_end() if profile_classes else None
+    return start.elapsed_time(end) / n, prof
+
+
+def cpu_baseline(inp, shape, budget_s):
+    """The fp64 oracle on the host over a bounded sample of the workload:
+    whole segments of one (sequence, KV head) group, forward + backward,
+    scaled to the full pass by the sample's share of the algorithmic FLOPs."""
+    import numpy as np
+    from oracle import hga_oracle as orc
+    from sparse_long_context_query_amd import work
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    total = work.flops(shape)
+    kbar = orc.block_summaries(inp["k"], shape.hist_block)
+    done = []
+    t_start = time.perf_counter()
+    order = [1, shape.nseg - 1] + list(range(2, shape.nseg - 1))
+    for s in order:
+        if time.perf_counter() - t_start > budget_s and done:
+            break
+        sel = orc.select_segment(inp["q"], inp["k"], shape, s, kbar=kbar)
+        O, LSE = orc.segment_forward(inp["q"], inp["k"], inp["v"], sel, shape, s, groups=[(0, 0)])
+        if shape.bwd:
+            orc.segment_backward(inp["q"], inp["k"], inp["v"], inp["do"], sel, shape, s, O, LSE,
+                                 groups=[(0, 0)])
+        done.append(s)
+    elapsed = time.perf_counter() - t_start
+    sample = work.flops(shape, segments=done, groups=1)
+    key = "fwd"
+    frac = (sample["fwd"] + (sample["bwd"] if shape.bwd else 0)) / (
+        total["fwd"] + (total["bwd"] if shape.bwd else 0))
+    t_full = elapsed / frac
+    del np
+    return {
+        "value": shape.batch * shape.seq_len / t_full,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle, {key}+bwd of segments {done} for KV head 0 of sequence 0 "
+                   f"({elapsed:.1f} s), scaled by its {frac:.4f} share of the pass FLOPs"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the HGA hot "
+              "path here has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_long_context_query_amd as hga
+    from sparse_long_context_query_amd import work
+    from synth import WORKLOADS, make_inputs
+
+    if not os.path.exists(hga.LIB_PATH):
+        from sparse_long_context_query_amd import build_lib
+        build_lib.build()
+    hga.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    shape = WORKLOADS[args.workload]
+    bwd = shape.bwd
+    log(f"[bench] generating {shape.name} inputs ({args.mode})")
+    inp = make_inputs(shape, seed=0, mode=args.mode)
+    dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    dev = {k: torch.from_numpy(inp[k]).cuda().to(dt)
+           for k in ("q", "k", "v", "do") if inp.get(k) is not None}
+    cfg = hga.Config.from_shape(shape)
+    buf = hga.Buffers(cfg, bwd=bwd)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        buf.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=bwd)
+    torch.cuda.synchronize()
+
+    # one profiled pass with every kernel bracketed: per-class breakdown and
+    # the dominant kernel
+    _, prof_all = timed_passes(buf, dev, bwd, 1, profile_classes=hga.KERNEL_CLASSES)
+    dominant = max(prof_all, key=lambda c: prof_all[c][0])
+    log(f"[bench] per-kernel ms (one pass): "
+        + ", ".join(f"{c}={v[0]:.3f}/{v[1]}" for c, v in prof_all.items() if v[1]))
+
+    log(f"[bench] timing {args.steps} passes (events around {dominant})")
+    ms, prof = timed_passes(buf, dev, bwd, args.steps, profile_classes=[dominant])
+    dom_ms, dom_n = prof[dominant]
+
+    fl = work.flops(shape)
+    tokens = shape.batch * shape.seq_len
+    value = tokens / (ms / 1e3)
+    dom_flops = {"fwd": fl["fwd"], "bwd_dq": fl["bwd_dq"], "bwd_dkdv": fl["bwd_dkdv"]}.get(dominant)
+    per_launch_flop = dom_flops * args.steps / dom_n if dom_flops else None
+    avg_launch_ms = dom_ms / dom_n
+    achieved = per_launch_flop / (avg_launch_ms * 1e-3) / 1e12 if per_launch_flop else None
+
+    fwd_ms = prof_all["fwd"][0]
+    bwd_ms = sum(prof_all[c][0] for c in ("bwd_pre", "bwd_dq", "bwd_dkdv"))
+    extras = {
+        "kernels_ms_per_pass": {c: round(v[0], 4) for c, v in prof_all.items() if v[1]},
+        "launches_per_pass": {c: v[1] for c, v in prof_all.items() if v[1]},
+        "fwd_tflops": round(fl["fwd"] / (fwd_ms * 1e-3) / 1e12, 1),
+        "fwd_frac_peak": round(fl["fwd"] / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+    }
+    if bwd:
+        extras["bwd_tflops"] = round(fl["bwd"] / (bwd_ms * 1e-3) / 1e12, 1)
+        extras["bwd_frac_peak"] = round(fl["bwd"] / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    extras["pass_tflops_algorithmic"] = round(
+        (fl["fwd"] + (fl["bwd"] if bwd else 0)) / (ms * 1e-3) / 1e12, 1)
+
+    if not args.no_dense_self:
+        dshape = shape.replace(seg_len=shape.seq_len, top_k=1)
+        dcfg = hga.Config.from_shape(dshape)
+        dbuf = hga.Buffers(dcfg, bwd=bwd)
+        for _ in range(2):
+            dbuf.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=bwd)
+        dms, _ = timed_passes(dbuf, dev, bwd, 3)
+        extras["dense_causal_same_kernels_ms"] = round(dms, 3)
+        extras["speedup_vs_dense_same_kernels"] = round(dms / ms, 2)
+        del dbuf
+    if args.dense_sdpa:
+        extras.update(dense_sdpa(dev, shape, bwd, ms))
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if shape.dtype == "bf16" else "f32",
+        "data": f"synthetic ({args.mode}-direction N(0,1), seed 0)",
+        "config": {"workload": shape.name, "batch": shape.batch, "seq_len": shape.seq_len,
+                   "seg_len": shape.seg_len, "hist_block": shape.hist_block,
+                   "query_block": shape.query_block, "top_k": shape.top_k,
+                   "n_q_heads": shape.n_q_heads, "n_kv_heads": shape.n_kv_heads,
+                   "head_dim": shape.head_dim, "segments": shape.nseg,
+                   "step": "summarize+select+fwd" + ("+bwd" if bwd else "") + " over all segments"},
+        "roofline": {
+            "kernel": dominant,
+            "bound": "mfma",
+            "achieved": round(achieved, 1) if achieved else None,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
+            "traffic": None,
+            "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+            "launches": dom_n,
+            "algorithmic_flop_per_launch": per_launch_flop,
+        },
+    }
+    out.update(extras)
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+        out["cpu_baseline"] = cpu_baseline(inp, shape, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def dense_sdpa(dev, shape, bwd, hga_ms):
+    """torch SDPA, flash backend only (errors instead of falling back to the
+    math path), dense causal over the whole sequence at the same shape."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    G = shape.group
+    try:
+        q = dev["q"].detach().clone().requires_grad_(bwd)
+        k = dev["k"].repeat_interleave(G, 1).contiguous().requires_grad_(bwd)
+        v = dev["v"].repeat_interleave(G, 1).contiguous().requires_grad_(bwd)
+        do = dev.get("do")
+
+        def once():
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+                if bwd:
+                    o.backward(do)
+
+        for _ in range(2):
+            once()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(3):
+            once()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / 3
+        return {"dense_sdpa_flash_ms": round(ms, 3), "speedup_vs_dense_sdpa": round(ms / hga_ms, 2)}
+    except Exception as ex:  # noqa: BLE001
+        return {"dense_sdpa_flash_ms": None, "dense_sdpa_error": str(ex)[:200]}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+/*
+ * hga.h - C ABI of the Hierarchical Global Attention (HGA) hot path with
+ * segmented backpropagation, for AMD Instinct MI355X (gfx950).
+ *
+ * Page keys used in citations:
+ *   [JA] 「低VRAM長文脈ファインチューニング：階層的グローバル注意と分割バック
+ *        プロpagationの実践」, sns.style (Japanese edition)
+ *   [FR] « Ajustement fin long-contexte à faible VRAM : une approche
+ *        d'optimisation avec attention globale hiérarchique », sns.style
+ *
+ * The method ([JA] 背景と概要; [FR] Contexte, Analyse approfondie): a long
+ * sequence is processed segment by segment; only the active segment is
+ * differentiable and history KV is detached; resident per-block summaries
+ * of the history stay on the GPU ([JA] 深掘り分析); for every query block
+ * a bounded, exact set of history tokens is loaded and attended together
+ * with the active segment.  The summary is the mean key of a block per KV
+ * head, the score is its dot product with the query block's mean query, and
+ * top-k ties go to the lower block index.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Shapes: B batch, S sequence length, L segment length, Bh history block,
+ *  Bq query block, k top-k, Hq query heads, Hkv KV heads, G = Hq/Hkv,
+ *  D head dim.  Query head h reads KV head h / G.
+ *  Segment s covers tokens [s*L, (s+1)*L); its history is the whole blocks
+ *  [0, s*L/Bh); it has L/Bq query blocks.
+ *
+ *  Layouts (all row-major, dense, device memory, allocated by the caller):
+ *    q, o, dO, dq      [B, Hq,  S, D]        dtype of the config
+ *    k, v, dk, dv      [B, Hkv, S, D]        dtype of the config
+ *    lse               [B, Hq,  S]           float32, natural log
+ *    summ              [B, Hkv, S/Bh, D]     float32 block-mean keys
+ *    sel               [B, Hkv, S/Bq, k]     int32, ascending, -1 padded
+ *  Every call reads and writes only the rows of the segment it is given
+ *  (history K/V and summaries are read as well).  Gradients are written,
+ *  not accumulated.  Work is enqueued on `stream` (a hipStream_t, NULL =
+ *  the default stream); no entry point synchronizes, allocates device
+ *  memory or keeps state between calls, except the optional profiling
+ *  hooks at the end of this file.  Scratch space comes from `ws`, of at
+ *  least hga_workspace_size() bytes.  Results are bitwise deterministic
+ *  (no floating-point atomics).
+ *
+ *  Errors: every entry point returns HGA_OK (0) or a negative code.  The
+ *  arguments are validated on the host before anything is enqueued; on an
+ *  error nothing is enqueued and hga_last_error() returns a message
+ *  (thread-local, valid until the next call on the same thread).  No C++
+ *  exception crosses this interface.
+ */
+#ifndef HGA_H
+#define HGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  HGA_OK = 0,
+  HGA_ERR_ARG = -1,          /* null pointer, bad size or index           */
+  HGA_ERR_UNSUPPORTED = -2,  /* dtype, head_dim or size the kernels lack  */
+  HGA_ERR_WORKSPACE = -3,    /* ws too small                               */
+  HGA_ERR_HIP = -4           /* a HIP runtime call or launch failed        */
+};
+
+typedef enum { HGA_F32 = 0, HGA_BF16 = 1 } hga_dtype;
+
+/* One attention layer's HGA problem.  Requirements (else HGA_ERR_ARG):
+ * all sizes >= 1, S % L == 0, L % Bh == 0, L % Bq == 0, Hq % Hkv == 0.
+ * Supported (else HGA_ERR_UNSUPPORTED): head_dim 64 or 128; dtype F32 or
+ * BF16; S/Bh <= 8192; top_k <= 1024; bf16 kernels need Bh and Bq to be
+ * multiples of 16. */
+typedef struct hga_config {
+  int32_t batch;
+  int32_t seq_len;
+  int32_t seg_len;
+  int32_t hist_block;
+  int32_t query_block;
+  int32_t top_k;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;          /* hga_dtype */
+  float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim) */
+} hga_config;
+
+/* a1 - resident block summaries ([JA] 深掘り分析: per-block summaries of the
+ * history stay resident and grow with length).
+ * summ[b,g,i,:] = (1/Bh) * sum over the Bh keys of block i of k[b,g,t,:],
+ * for blk_begin <= i < blk_end (0 <= blk_begin <= blk_end <= S/Bh).
+ * Accumulates in float32.  Other rows of summ are left untouched. */
+int hga_summarize(const hga_config* cfg, const void* k, int32_t blk_begin,
+                  int32_t blk_end, float* summ, void* stream);
+
+/* a2 + a3 - query-block mean and top-k selection for segment `seg`
+ * ([JA] 背景と概要: a bounded set of history tokens per query block;
+ * [FR] Contexte: targeted loading of a bounded set of relevant tokens).
+ * For every (b, g, query block j): qbar = mean of q over the G query heads
+ * of group g and the Bq tokens of the block (float32); score_i = qbar .
+ * summ[b,g,i,:] for the nb = seg*L/Bh history blocks; if nb <= k all blocks
+ * are taken, else the k best by (score descending, index ascending).  The
+ * chosen indices are written ascending to sel[b,g,seg*L/Bq + j, :] and
+ * padded with -1.  Reads summ rows [0, nb), which must be current. */
+int hga_select(const hga_config* cfg, const void* q, const float* summ,
+               int32_t seg, int32_t* sel, void* stream);
+
+/* a4 - standalone block-sparse gather of the selected history K and V of
+ * segment `seg` ([FR] Analyse approfondie: targeted loading of the chosen
+ * history tokens rather than a full scan).  k_out and v_out are
+ * [B, Hkv, L/Bq, k, Bh, D] in the config dtype; slot t of query block j
+ * receives block sel[b,g,seg*L/Bq+j,t] of k (resp. v), or zeros when that
+ * entry is -1.  The attention kernels below read the same blocks directly
+ * and do not need this copy; it exists to measure and check the gather. */
+int hga_gather(const hga_config* cfg, const void* k, const void* v,
+               const int32_t* sel, int32_t seg, void* k_out, void* v_out,
+               void* stream);
+
+/* a5 - forward attention of segment `seg` ([JA] 背景と概要: exact attention
+ * over the bounded history set; [DE]/[KO] same).  For each (b, h, t) of
+ * the segment, the key set is the tokens of the selected blocks of
+ * (b, h/G, query block of t) together with the local tokens seg*L .. t;
+ * one softmax with scale over that joint set; o = softmax . v, lse = log of
+ * the softmax denominator (natural log, including the scale).  `lse` may
+ * be NULL (inference).  ws: hga_workspace_size(cfg, HGA_OP_FWD) bytes
+ * (currently 0; ws may be NULL). */
+int hga_attn_fwd(const hga_config* cfg, const void* q, const void* k,
+                 const void* v, const int32_t* sel, int32_t seg, void* o,
+                 float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* a6 + a7 + a8 - backward of segment `seg` for the loss whose gradient
+ * with respect to o is dO ([FR] Analyse approfondie: only the active
+ * segment's gradients are computed; history KV is detached).
+ *   delta = rowsum(dO * o);  p = exp(scale*q.k - lse);
+ *   dS = p * (dO.v - delta);  dq = scale * sum dS k   (history and local);
+ *   dk[t'] = scale * sum dS q, dv[t'] = sum p dO, for local keys t' only,
+ *   summed over the queries t >= t' of the segment and the G heads.
+ * History rows of dk/dv are not written.  ws: hga_workspace_size(cfg,
+ * HGA_OP_BWD) bytes. */
+int hga_attn_bwd(const hga_config* cfg, const void* q, const void* k,
+                 const void* v, const void* o, const float* lse,
+                 const void* dO, const int32_t* sel, int32_t seg, void* dq,
+                 void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
+
+/* a9 - one step of the segment loop ([FR] Analyse approfondie: segments
+ * processed one after another): summarize the blocks that segment seg-1
+ * closed (none for seg 0), select, forward, and with HGA_STEP_BWD the
+ * backward.  Calling it for seg = 0, 1, ..., S/L-1 in order runs the whole
+ * segmented pass; summ must hold the blocks of earlier segments (which the
+ * earlier steps wrote).  dO, dq, dk, dv may be NULL without HGA_STEP_BWD;
+ * lse may be NULL without HGA_STEP_BWD.  ws: hga_workspace_size(cfg,
+ * HGA_OP_STEP) bytes. */
+enum { HGA_STEP_BWD = 1 };
+int hga_segment_step(const hga_config* cfg, int32_t seg, int32_t flags,
+                     const void* q, const void* k, const void* v,
+                     const void* dO, float* summ, int32_t* sel, void* o,
+                     float* lse, void* dq, void* dk, void* dv, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Workspace bytes for an operation (0 if none is needed), or 0 with
+ * hga_last_error() set if the config is invalid. */
+enum { HGA_OP_FWD = 0, HGA_OP_BWD = 1, HGA_OP_STEP = 2 };
+size_t hga_workspace_size(const hga_config* cfg, int32_t op);
+
+/* Message of the last failure on this thread ("" if none). */
+const char* hga_last_error(void);
+
+/* Library version string. */
+const char* hga_version(void);
+
+/* ---- optional profiling hooks (timing only, never change results) ----
+ * hga_profile_begin(mask) makes later launches on this thread record a HIP
+ * event pair on the launch stream around each kernel whose class bit
+ * (1 << class) is set in mask.  hga_profile_end() waits for those events,
+ * writes per-class total milliseconds and launch counts into ms[] and
+ * count[] (arrays of HGA_KCLASS_COUNT entries), stops recording and
+ * releases the events.  Kernel classes: */
+enum {
+  HGA_K_SUMMARIZE = 0,
+  HGA_K_SELECT = 1,
+  HGA_K_GATHER = 2,
+  HGA_K_FWD = 3,
+  HGA_K_BWD_PRE = 4,
+  HGA_K_BWD_DQ = 5,
+  HGA_K_BWD_DKDV = 6,
+  HGA_KCLASS_COUNT = 7
+};
+int hga_profile_begin(uint32_t mask);
+int hga_profile_end(double* ms, int64_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HGA_H */

@@ -180,9 +180,15 @@ def _block_mask(n_hist: int, seg_start: int, seg_len: int, q_pos: np.ndarray) ->
     return np.concatenate([vis_hist, vis_local], axis=1)
 
 
-def segment_forward(q, k, v, sel, shape, seg: int, scale: Optional[float] = None):
+def _all_groups(B: int, Hkv: int):
+    return [(b, g) for b in range(B) for g in range(Hkv)]
+
+
+def segment_forward(q, k, v, sel, shape, seg: int, scale: Optional[float] = None,
+                    groups=None):
     """O [B,Hq,L,D] and natural-log LSE [B,Hq,L] of segment `seg`, given
-    its selection `sel` [B,Hkv,nqb,k]."""
+    its selection `sel` [B,Hkv,nqb,k].  `groups` (list of (b, g)) limits the
+    work to those sequences / KV heads; other rows stay zero."""
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
@@ -192,23 +198,22 @@ def segment_forward(q, k, v, sel, shape, seg: int, scale: Optional[float] = None
     nqb = L // Bq
     O = np.zeros((B, Hq, L, D))
     LSE = np.zeros((B, Hq, L))
-    for b in range(B):
-        for g in range(Hkv):
-            for j in range(nqb):
-                keys, nh = key_indices(sel[b, g, j], Bh, t0, L)
-                Kset = _f64(k[b, g, keys])
-                Vset = _f64(v[b, g, keys])
-                qpos = t0 + j * Bq + np.arange(Bq)
-                mask = _block_mask(nh, t0, L, qpos)
-                qrows = slice(t0 + j * Bq, t0 + (j + 1) * Bq)
-                Qj = _f64(q[b, g * G:(g + 1) * G, qrows])         # [G,Bq,D]
-                Z = sc * (Qj @ Kset.T)                            # [G,Bq,nk]
-                Z = np.where(mask[None], Z, -np.inf)
-                m = Z.max(axis=-1, keepdims=True)
-                lse = m[..., 0] + np.log(np.exp(Z - m).sum(axis=-1))
-                P = np.exp(Z - lse[..., None])
-                O[b, g * G:(g + 1) * G, j * Bq:(j + 1) * Bq] = P @ Vset
-                LSE[b, g * G:(g + 1) * G, j * Bq:(j + 1) * Bq] = lse
+    for b, g in (groups if groups is not None else _all_groups(B, Hkv)):
+        for j in range(nqb):
+            keys, nh = key_indices(sel[b, g, j], Bh, t0, L)
+            Kset = _f64(k[b, g, keys])
+            Vset = _f64(v[b, g, keys])
+            qpos = t0 + j * Bq + np.arange(Bq)
+            mask = _block_mask(nh, t0, L, qpos)
+            qrows = slice(t0 + j * Bq, t0 + (j + 1) * Bq)
+            Qj = _f64(q[b, g * G:(g + 1) * G, qrows])         # [G,Bq,D]
+            Z = sc * (Qj @ Kset.T)                            # [G,Bq,nk]
+            Z = np.where(mask[None], Z, -np.inf)
+            m = Z.max(axis=-1, keepdims=True)
+            lse = m[..., 0] + np.log(np.exp(Z - m).sum(axis=-1))
+            P = np.exp(Z - lse[..., None])
+            O[b, g * G:(g + 1) * G, j * Bq:(j + 1) * Bq] = P @ Vset
+            LSE[b, g * G:(g + 1) * G, j * Bq:(j + 1) * Bq] = lse
     return O, LSE
 
 
@@ -218,7 +223,7 @@ def segment_forward(q, k, v, sel, shape, seg: int, scale: Optional[float] = None
 # are kept out of the differentiable state)
 # --------------------------------------------------------------------------
 def segment_backward(q, k, v, do, sel, shape, seg: int, O=None, LSE=None,
-                     scale: Optional[float] = None):
+                     scale: Optional[float] = None, groups=None):
     """dQ [B,Hq,L,D], dK and dV [B,Hkv,L,D] of segment `seg` for the loss
     sum(O * dO).  History keys receive no gradient; dK/dV of a local key sum
     the contributions of every query of the segment and every query head of
@@ -231,35 +236,34 @@ def segment_backward(q, k, v, do, sel, shape, seg: int, O=None, LSE=None,
     sc = softmax_scale(D, scale)
     nqb = L // Bq
     if O is None or LSE is None:
-        O, LSE = segment_forward(q, k, v, sel, shape, seg, scale)
+        O, LSE = segment_forward(q, k, v, sel, shape, seg, scale, groups)
     dQ = np.zeros((B, Hq, L, D))
     dK = np.zeros((B, Hkv, L, D))
     dV = np.zeros((B, Hkv, L, D))
-    for b in range(B):
-        for g in range(Hkv):
-            for j in range(nqb):
-                keys, nh = key_indices(sel[b, g, j], Bh, t0, L)
-                Kset = _f64(k[b, g, keys])
-                Vset = _f64(v[b, g, keys])
-                qpos = t0 + j * Bq + np.arange(Bq)
-                mask = _block_mask(nh, t0, L, qpos)
-                hs = slice(g * G, (g + 1) * G)
-                rows = slice(j * Bq, (j + 1) * Bq)
-                qrows = slice(t0 + j * Bq, t0 + (j + 1) * Bq)
-                Qj = _f64(q[b, hs, qrows])
-                dOj = _f64(do[b, hs, qrows])
-                Oj = _f64(O[b, hs, rows])
-                lse = _f64(LSE[b, hs, rows])
-                Z = sc * (Qj @ Kset.T)
-                P = np.where(mask[None], np.exp(Z - lse[..., None]), 0.0)
-                dP = dOj @ Vset.T
-                delta = (dOj * Oj).sum(axis=-1)
-                dS = P * (dP - delta[..., None])
-                dQ[b, hs, rows] = sc * (dS @ Kset)
-                dS_loc = dS[..., nh:]                             # [G,Bq,L]
-                P_loc = P[..., nh:]
-                dK[b, g] += sc * np.einsum("hqk,hqd->kd", dS_loc, Qj)
-                dV[b, g] += np.einsum("hqk,hqd->kd", P_loc, dOj)
+    for b, g in (groups if groups is not None else _all_groups(B, Hkv)):
+        for j in range(nqb):
+            keys, nh = key_indices(sel[b, g, j], Bh, t0, L)
+            Kset = _f64(k[b, g, keys])
+            Vset = _f64(v[b, g, keys])
+            qpos = t0 + j * Bq + np.arange(Bq)
+            mask = _block_mask(nh, t0, L, qpos)
+            hs = slice(g * G, (g + 1) * G)
+            rows = slice(j * Bq, (j + 1) * Bq)
+            qrows = slice(t0 + j * Bq, t0 + (j + 1) * Bq)
+            Qj = _f64(q[b, hs, qrows])
+            dOj = _f64(do[b, hs, qrows])
+            Oj = _f64(O[b, hs, rows])
+            lse = _f64(LSE[b, hs, rows])
+            Z = sc * (Qj @ Kset.T)
+            P = np.where(mask[None], np.exp(Z - lse[..., None]), 0.0)
+            dP = dOj @ Vset.T
+            delta = (dOj * Oj).sum(axis=-1)
+            dS = P * (dP - delta[..., None])
+            dQ[b, hs, rows] = sc * (dS @ Kset)
+            dS_loc = dS[..., nh:]                             # [G,Bq,L]
+            P_loc = P[..., nh:]
+            dK[b, g] += sc * np.einsum("hqk,hqd->kd", dS_loc, Qj)
+            dV[b, g] += np.einsum("hqk,hqd->kd", P_loc, dOj)
     return dQ, dK, dV
 
 

@@ -1,0 +1,342 @@
+// C ABI of the HGA hot path: host-side validation, dispatch and the
+// optional per-kernel profiling hooks.  Every argument check happens here,
+// before anything is enqueued; no C++ exception leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "hga.h"
+#include "hga_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return HGA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(HGA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Builds the derived problem description, or returns an error code.
+int make_prob(const hga_config* c, hga::Prob* p) {
+  if (c == nullptr) return fail(HGA_ERR_ARG, "config is NULL");
+  if (c->batch < 1 || c->seq_len < 1 || c->seg_len < 1 || c->hist_block < 1 ||
+      c->query_block < 1 || c->top_k < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
+      c->head_dim < 1)
+    return fail(HGA_ERR_ARG, "every size in the config must be >= 1");
+  if (c->seq_len % c->seg_len)
+    return fail(HGA_ERR_ARG, "seq_len %d is not a multiple of seg_len %d", c->seq_len, c->seg_len);
+  if (c->seg_len % c->hist_block)
+    return fail(HGA_ERR_ARG, "seg_len %d is not a multiple of hist_block %d", c->seg_len,
+                c->hist_block);
+  if (c->seg_len % c->query_block)
+    return fail(HGA_ERR_ARG, "seg_len %d is not a multiple of query_block %d", c->seg_len,
+                c->query_block);
+  if (c->n_q_heads % c->n_kv_heads)
+    return fail(HGA_ERR_ARG, "n_q_heads %d is not a multiple of n_kv_heads %d", c->n_q_heads,
+                c->n_kv_heads);
+  if (c->dtype != HGA_F32 && c->dtype != HGA_BF16)
+    return fail(HGA_ERR_UNSUPPORTED, "dtype %d is not supported (F32=0, BF16=1)", c->dtype);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(HGA_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", c->head_dim);
+  if (c->seq_len / c->hist_block > hga::kMaxCandidates)
+    return fail(HGA_ERR_UNSUPPORTED, "seq_len/hist_block = %d exceeds %d history blocks",
+                c->seq_len / c->hist_block, hga::kMaxCandidates);
+  if (c->top_k > hga::kMaxTopK)
+    return fail(HGA_ERR_UNSUPPORTED, "top_k %d exceeds %d", c->top_k, hga::kMaxTopK);
+  if (c->dtype == HGA_BF16 && (c->hist_block % 16 || c->query_block % 16))
+    return fail(HGA_ERR_UNSUPPORTED,
+                "bf16 kernels need hist_block and query_block to be multiples of 16");
+  if (c->dtype == HGA_F32 && c->hist_block % 4)
+    return fail(HGA_ERR_UNSUPPORTED, "f32 kernels need hist_block to be a multiple of 4");
+  const double elems = (double)c->batch * c->n_q_heads * c->seq_len * c->head_dim;
+  if (elems > 2147483647.0 * 64)
+    return fail(HGA_ERR_UNSUPPORTED, "tensor too large");
+  if (!(std::isfinite(c->softmax_scale)))
+    return fail(HGA_ERR_ARG, "softmax_scale is not finite");
+  p->B = c->batch;
+  p->S = c->seq_len;
+  p->L = c->seg_len;
+  p->Bh = c->hist_block;
+  p->Bq = c->query_block;
+  p->K = c->top_k;
+  p->Hq = c->n_q_heads;
+  p->Hkv = c->n_kv_heads;
+  p->D = c->head_dim;
+  p->G = c->n_q_heads / c->n_kv_heads;
+  p->dtype = c->dtype;
+  p->scale = c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / std::sqrt((float)c->head_dim);
+  p->nqb = p->L / p->Bq;
+  p->nqb_all = p->S / p->Bq;
+  p->nblk = p->S / p->Bh;
+  return HGA_OK;
+}
+
+int check_seg(const hga::Prob& p, int32_t seg) {
+  if (seg < 0 || seg >= p.S / p.L)
+    return fail(HGA_ERR_ARG, "segment %d out of range [0, %d)", seg, p.S / p.L);
+  return HGA_OK;
+}
+
+#define HGA_REQUIRE(ptr)                                              \
+  do {                                                                \
+    if ((ptr) == nullptr) return fail(HGA_ERR_ARG, #ptr " is NULL");  \
+  } while (0)
+
+// ---- profiling -----------------------------------------------------------
+struct ProfEvent {
+  int kclass;
+  hipEvent_t start, stop;
+};
+thread_local bool g_prof_on = false;
+thread_local uint32_t g_prof_mask = 0;
+thread_local std::vector<ProfEvent> g_prof_events;
+thread_local std::vector<hipEvent_t> g_prof_pool;
+thread_local hipEvent_t g_prof_pending_start = nullptr;
+
+hipEvent_t pool_get() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+namespace hga {
+void prof_mark_begin(int kclass, hipStream_t st) {
+  if (!g_prof_on || !((g_prof_mask >> kclass) & 1u)) return;
+  g_prof_pending_start = pool_get();
+  if (g_prof_pending_start) hipEventRecord(g_prof_pending_start, st);
+}
+void prof_mark_end(int kclass, hipStream_t st) {
+  if (!g_prof_on || g_prof_pending_start == nullptr) return;
+  hipEvent_t stop = pool_get();
+  if (stop == nullptr) return;
+  hipEventRecord(stop, st);
+  g_prof_events.push_back({kclass, g_prof_pending_start, stop});
+  g_prof_pending_start = nullptr;
+}
+}  // namespace hga
+
+extern "C" {
+
+const char* hga_last_error(void) { return g_last_error.c_str(); }
+
+const char* hga_version(void) { return "hga-mi355x 0.1 (gfx950)"; }
+
+size_t hga_workspace_size(const hga_config* cfg, int32_t op) {
+  hga::Prob p;
+  if (make_prob(cfg, &p) != HGA_OK) return 0;
+  switch (op) {
+    case HGA_OP_FWD:
+      ok();
+      return 0;
+    case HGA_OP_BWD:
+    case HGA_OP_STEP:
+      ok();
+      return hga::bwd_workspace_bytes(p);
+    default:
+      fail(HGA_ERR_ARG, "unknown op %d", op);
+      return 0;
+  }
+}
+
+int hga_summarize(const hga_config* cfg, const void* k, int32_t blk_begin, int32_t blk_end,
+                  float* summ, void* stream) {
+  hga::Prob p;
+  int rc = make_prob(cfg, &p);
+  if (rc) return rc;
+  HGA_REQUIRE(k);
+  HGA_REQUIRE(summ);
+  if (blk_begin < 0 || blk_end < blk_begin || blk_end > p.nblk)
+    return fail(HGA_ERR_ARG, "block range [%d, %d) outside [0, %d]", blk_begin, blk_end, p.nblk);
+  hipError_t e = hga::launch_summarize(p, k, blk_begin, blk_end, summ, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "summarize launch");
+  return ok();
+}
+
+int hga_select(const hga_config* cfg, const void* q, const float* summ, int32_t seg,
+               int32_t* sel, void* stream) {
+  hga::Prob p;
+  int rc = make_prob(cfg, &p);
+  if (rc) return rc;
+  if ((rc = check_seg(p, seg))) return rc;
+  HGA_REQUIRE(q);
+  HGA_REQUIRE(summ);
+  HGA_REQUIRE(sel);
+  hipError_t e = hga::launch_select(p, q, summ, seg, sel, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return ok();
+}
+
+int hga_gather(const hga_config* cfg, const void* k, const void* v, const int32_t* sel,
+               int32_t seg, void* k_out, void* v_out, void* stream) {
+  hga::Prob p;
+  int rc = make_prob(cfg, &p);
+  if (rc) return rc;
+  if ((rc = check_seg(p, seg))) return rc;
+  HGA_REQUIRE(k);
+  HGA_REQUIRE(v);
+  HGA_REQUIRE(sel);
+  HGA_REQUIRE(k_out);
+  HGA_REQUIRE(v_out);
+  hipError_t e = hga::launch_gather(p, k, v, sel, seg, k_out, v_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return ok();
+}
+
+int hga_attn_fwd(const hga_config* cfg, const void* q, const void* k, const void* v,
+                 const int32_t* sel, int32_t seg, void* o, float* lse, void* ws,
+                 size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  hga::Prob p;
+  int rc = make_prob(cfg, &p);
+  if (rc) return rc;
+  if ((rc = check_seg(p, seg))) return rc;
+  HGA_REQUIRE(q);
+  HGA_REQUIRE(k);
+  HGA_REQUIRE(v);
+  HGA_REQUIRE(sel);
+  HGA_REQUIRE(o);
+  hipError_t e = hga::launch_fwd(p, q, k, v, sel, seg, o, lse, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return ok();
+}
+
+int hga_attn_bwd(const hga_config* cfg, const void* q, const void* k, const void* v,
+                 const void* o, const float* lse, const void* dO, const int32_t* sel,
+                 int32_t seg, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                 void* stream) {
+  hga::Prob p;
+  int rc = make_prob(cfg, &p);
+  if (rc) return rc;
+  if ((rc = check_seg(p, seg))) return rc;
+  HGA_REQUIRE(q);
+  HGA_REQUIRE(k);
+  HGA_REQUIRE(v);
+  HGA_REQUIRE(o);
+  HGA_REQUIRE(lse);
+  HGA_REQUIRE(dO);
+  HGA_REQUIRE(sel);
+  HGA_REQUIRE(dq);
+  HGA_REQUIRE(dk);
+  HGA_REQUIRE(dv);
+  HGA_REQUIRE(ws);
+  const size_t need = hga::bwd_workspace_bytes(p);
+  if (ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, need);
+  hipError_t e = hga::launch_bwd(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, (float*)ws,
+                                 (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return ok();
+}
+
+int hga_segment_step(const hga_config* cfg, int32_t seg, int32_t flags, const void* q,
+                     const void* k, const void* v, const void* dO, float* summ, int32_t* sel,
+                     void* o, float* lse, void* dq, void* dk, void* dv, void* ws,
+                     size_t ws_bytes, void* stream) {
+  hga::Prob p;
+  int rc = make_prob(cfg, &p);
+  if (rc) return rc;
+  if ((rc = check_seg(p, seg))) return rc;
+  if (flags & ~HGA_STEP_BWD) return fail(HGA_ERR_ARG, "unknown flags 0x%x", flags);
+  const bool bwd = (flags & HGA_STEP_BWD) != 0;
+  HGA_REQUIRE(q);
+  HGA_REQUIRE(k);
+  HGA_REQUIRE(v);
+  HGA_REQUIRE(summ);
+  HGA_REQUIRE(sel);
+  HGA_REQUIRE(o);
+  if (bwd) {
+    HGA_REQUIRE(lse);
+    HGA_REQUIRE(dO);
+    HGA_REQUIRE(dq);
+    HGA_REQUIRE(dk);
+    HGA_REQUIRE(dv);
+    HGA_REQUIRE(ws);
+    const size_t need = hga::bwd_workspace_bytes(p);
+    if (ws_bytes < need)
+      return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  ws_bytes, need);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (seg > 0) {
+    // blocks closed by segment seg-1 become history of segment seg
+    const int b0 = (seg - 1) * p.L / p.Bh, b1 = seg * p.L / p.Bh;
+    e = hga::launch_summarize(p, k, b0, b1, summ, st);
+    if (e != hipSuccess) return hip_fail(e, "summarize launch");
+  }
+  e = hga::launch_select(p, q, summ, seg, sel, st);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  e = hga::launch_fwd(p, q, k, v, sel, seg, o, lse, st);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  if (bwd) {
+    e = hga::launch_bwd(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, (float*)ws, st);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+  }
+  return ok();
+}
+
+int hga_profile_begin(uint32_t mask) {
+  g_prof_on = true;
+  g_prof_mask = mask;
+  return ok();
+}
+
+int hga_profile_end(double* ms, int64_t* count) {
+  if (ms == nullptr || count == nullptr) return fail(HGA_ERR_ARG, "ms/count is NULL");
+  for (int i = 0; i < HGA_KCLASS_COUNT; ++i) { ms[i] = 0.0; count[i] = 0; }
+  int rc = HGA_OK;
+  for (const ProfEvent& ev : g_prof_events) {
+    if (rc == HGA_OK) {
+      hipError_t e = hipEventSynchronize(ev.stop);
+      float t = 0.f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&t, ev.start, ev.stop);
+      if (e != hipSuccess) {
+        rc = hip_fail(e, "profiling event");
+      } else if (ev.kclass >= 0 && ev.kclass < HGA_KCLASS_COUNT) {
+        ms[ev.kclass] += t;
+        count[ev.kclass] += 1;
+      }
+    }
+    g_prof_pool.push_back(ev.start);
+    g_prof_pool.push_back(ev.stop);
+  }
+  g_prof_events.clear();
+  g_prof_on = false;
+  for (hipEvent_t e : g_prof_pool) hipEventDestroy(e);
+  g_prof_pool.clear();
+  if (rc == HGA_OK) ok();
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Internal declarations of the HGA HIP library (gfx950 only).
+//
+// Page keys used in citations across the sources:
+//   [JA] 「低VRAM長文脈ファインチューニング：階層的グローバル注意と分割バック
+//        プロpagationの実践」, sns.style (Japanese edition)
+//   [FR] « Ajustement fin long-contexte à faible VRAM : une approche
+//        d'optimisation avec attention globale hiérarchique », sns.style
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "hga.h"
+
+namespace hga {
+
+// Validated problem description (all derived sizes precomputed on the host).
+struct Prob {
+  int B, S, L, Bh, Bq, K, Hq, Hkv, D, G;
+  int dtype;      // HGA_F32 / HGA_BF16
+  float scale;    // softmax scale (natural-log units)
+  int nqb;        // query blocks per segment  = L / Bq
+  int nqb_all;    // query blocks per sequence = S / Bq
+  int nblk;       // history blocks per sequence = S / Bh
+};
+
+constexpr int kMaxCandidates = 8192;   // S / Bh limit of the selection sort
+constexpr int kMaxTopK = 1024;
+
+// ---- launchers (host side; return hipSuccess or the launch error) --------
+hipError_t launch_summarize(const Prob& p, const void* k, int blk_begin,
+                            int blk_end, float* summ, hipStream_t st);
+hipError_t launch_select(const Prob& p, const void* q, const float* summ,
+                         int seg, int32_t* sel, hipStream_t st);
+hipError_t launch_gather(const Prob& p, const void* k, const void* v,
+                         const int32_t* sel, int seg, void* ko, void* vo,
+                         hipStream_t st);
+hipError_t launch_fwd(const Prob& p, const void* q, const void* k,
+                      const void* v, const int32_t* sel, int seg, void* o,
+                      float* lse, hipStream_t st);
+hipError_t launch_bwd(const Prob& p, const void* q, const void* k,
+                      const void* v, const void* o, const float* lse,
+                      const void* dO, const int32_t* sel, int seg, void* dq,
+                      void* dk, void* dv, float* delta_ws, hipStream_t st);
+size_t bwd_workspace_bytes(const Prob& p);
+
+// ---- profiling hooks (no-ops unless hga_profile_begin() was called) -----
+void prof_mark_begin(int kclass, hipStream_t st);
+void prof_mark_end(int kclass, hipStream_t st);
+
+struct ProfScope {
+  int c;
+  hipStream_t s;
+  ProfScope(int cls, hipStream_t st) : c(cls), s(st) { prof_mark_begin(c, s); }
+  ~ProfScope() { prof_mark_end(c, s); }
+};
+
+}  // namespace hga
+
+// ---------------------------------------------------------------------------
+// Device helpers shared by the kernels
+// ---------------------------------------------------------------------------
+#if defined(__HIPCC__)
+namespace hga {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// 8 bf16 packed in a uint4 -> 8 floats
+__device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
+  f[0] = __uint_as_float(u.x << 16); f[1] = __uint_as_float(u.x & 0xffff0000u);
+  f[2] = __uint_as_float(u.y << 16); f[3] = __uint_as_float(u.y & 0xffff0000u);
+  f[4] = __uint_as_float(u.z << 16); f[5] = __uint_as_float(u.z & 0xffff0000u);
+  f[6] = __uint_as_float(u.w << 16); f[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
+// Loads 16 bytes of T-typed data and widens them to floats (8 bf16 or 4 f32).
+template <typename T> struct Vec16;
+template <> struct Vec16<__bf16> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void load(const __bf16* p, float* f) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    unpack_bf16x8(u, f);
+  }
+};
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void load(const float* p, float* f) {
+    float4 u = *reinterpret_cast<const float4*>(p);
+    f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
+  }
+};
+
+// Blocks of a 1-D grid are dealt round-robin over the 8 XCDs of the chip.
+// Map the hardware block id to a work id so that consecutive work ids share
+// an XCD (and therefore its L2): XCD x receives a contiguous range.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  int q = nblocks / kXcd, r = nblocks % kXcd;
+  int x = bid % kXcd, slot = bid / kXcd;
+  return (x < r) ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
+}
+
+__device__ __forceinline__ float wave_shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace hga
+#endif

@@ -1,0 +1,151 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+the header declares, and rejects bad arguments on the host with the
+documented status before anything is enqueued (only invalid calls are made
+here, so no kernel is ever launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_long_context_query_amd as hga
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(hga.LIB_PATH):
+        from sparse_long_context_query_amd import build_lib
+        build_lib.build()
+    return hga.lib()
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "hga.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hga_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_header_function(L):
+    names = header_functions()
+    assert {"hga_summarize", "hga_select", "hga_gather", "hga_attn_fwd", "hga_attn_bwd",
+            "hga_segment_step", "hga_workspace_size", "hga_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def good_cfg(**kw):
+    c = hga.Config(1, 16384, 1024, 64, 64, 32, 32, 8, 128, hga.HGA_BF16, 0.0)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value,code,frag", [
+    ("seq_len", 1000, hga.HGA_ERR_ARG, "multiple of seg_len"),
+    ("hist_block", 48, hga.HGA_ERR_ARG, "multiple of hist_block"),
+    ("query_block", 48, hga.HGA_ERR_ARG, "multiple of query_block"),
+    ("n_q_heads", 30, hga.HGA_ERR_ARG, "multiple of n_kv_heads"),
+    ("top_k", 0, hga.HGA_ERR_ARG, ">= 1"),
+    ("batch", 0, hga.HGA_ERR_ARG, ">= 1"),
+    ("head_dim", 96, hga.HGA_ERR_UNSUPPORTED, "head_dim"),
+    ("dtype", 7, hga.HGA_ERR_UNSUPPORTED, "dtype"),
+    ("top_k", 2000, hga.HGA_ERR_UNSUPPORTED, "top_k"),
+    ("hist_block", 8, hga.HGA_ERR_UNSUPPORTED, "multiples of 16"),
+])
+def test_bad_config_rejected(L, field, value, code, frag):
+    cfg = good_cfg(**{field: value})
+    rc = L.hga_select(ctypes.byref(cfg), FAKE, FAKE, 1, FAKE, None)
+    assert rc == code
+    assert frag in hga.last_error()
+    assert L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_STEP) == 0
+
+
+def test_too_many_history_blocks(L):
+    cfg = good_cfg(seq_len=1 << 20, seg_len=1024, hist_block=64)
+    rc = L.hga_attn_fwd(ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, 0, FAKE, None, None, 0, None)
+    assert rc == hga.HGA_ERR_UNSUPPORTED and "history blocks" in hga.last_error()
+
+
+def test_null_config(L):
+    assert L.hga_select(None, FAKE, FAKE, 0, FAKE, None) == hga.HGA_ERR_ARG
+    assert "config is NULL" in hga.last_error()
+
+
+@pytest.mark.parametrize("seg", [-1, 16, 1000])
+def test_segment_out_of_range(L, seg):
+    cfg = good_cfg()
+    assert L.hga_select(ctypes.byref(cfg), FAKE, FAKE, seg, FAKE, None) == hga.HGA_ERR_ARG
+    assert "out of range" in hga.last_error()
+    rc = L.hga_segment_step(ctypes.byref(cfg), seg, 0, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                            FAKE, None, None, None, None, None, 0, None)
+    assert rc == hga.HGA_ERR_ARG
+
+
+def test_null_pointers(L):
+    cfg = good_cfg()
+    assert L.hga_select(ctypes.byref(cfg), None, FAKE, 1, FAKE, None) == hga.HGA_ERR_ARG
+    assert "q is NULL" in hga.last_error()
+    assert L.hga_attn_fwd(ctypes.byref(cfg), FAKE, FAKE, FAKE, None, 1, FAKE, None, None, 0,
+                          None) == hga.HGA_ERR_ARG
+    assert "sel is NULL" in hga.last_error()
+    rc = L.hga_attn_bwd(ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, FAKE,
+                        FAKE, FAKE, FAKE, 1 << 30, None)
+    assert rc == hga.HGA_ERR_ARG and "dO is NULL" in hga.last_error()
+    # backward step needs its gradient buffers
+    rc = L.hga_segment_step(ctypes.byref(cfg), 1, hga.HGA_STEP_BWD, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert rc == hga.HGA_ERR_ARG and "dq is NULL" in hga.last_error()
+    assert L.hga_gather(ctypes.byref(cfg), FAKE, FAKE, FAKE, 1, None, FAKE, None) == hga.HGA_ERR_ARG
+
+
+def test_bad_summary_range(L):
+    cfg = good_cfg()
+    for b0, b1 in [(-1, 3), (5, 4), (0, 257)]:
+        assert L.hga_summarize(ctypes.byref(cfg), FAKE, b0, b1, FAKE, None) == hga.HGA_ERR_ARG
+        assert "block range" in hga.last_error()
+
+
+def test_workspace_too_small(L):
+    cfg = good_cfg()
+    need = L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_BWD)
+    assert need == 1 * 32 * 1024 * 4  # one fp32 row-sum per query row of a segment
+    rc = L.hga_attn_bwd(ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE,
+                        FAKE, FAKE, FAKE, need - 1, None)
+    assert rc == hga.HGA_ERR_WORKSPACE
+    rc = L.hga_segment_step(ctypes.byref(cfg), 1, hga.HGA_STEP_BWD, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert rc == hga.HGA_ERR_WORKSPACE
+    assert L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_FWD) == 0
+    assert L.hga_workspace_size(ctypes.byref(cfg), 9) == 0 and "unknown op" in hga.last_error()
+
+
+def test_unknown_step_flags(L):
+    cfg = good_cfg()
+    rc = L.hga_segment_step(ctypes.byref(cfg), 1, 6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert rc == hga.HGA_ERR_ARG and "flags" in hga.last_error()
+
+
+def test_profile_hooks_without_launches(L):
+    hga.profile_begin()
+    stats = hga.profile_end()
+    assert set(stats) == set(hga.KERNEL_CLASSES)
+    assert all(v == (0.0, 0) for v in stats.values())
+
+
+def test_binding_rejects_cpu_tensors(L):
+    import torch
+    cfg = good_cfg(seq_len=2048, seg_len=512, top_k=8)
+    s = hga.Shapes(cfg)
+    q = torch.zeros(s.q, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        hga.select(cfg, q, torch.zeros(s.summ), 1, torch.zeros(s.sel, dtype=torch.int32))
+
+
+def test_version(L):
+    assert "gfx950" in hga.version()

@@ -1,0 +1,260 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+the same seeded inputs.  Selection, gather and summaries-driven indices are
+compared bit for bit; floating-point outputs by max-abs-relative error,
+max|x - ref| / max|ref|, at 1e-5 (fp32) and 2e-2 (bf16)."""
+
+import numpy as np
+import pytest
+
+from oracle import hga_oracle as orc
+from synth import HGAShape, WORKLOADS, make_inputs
+
+from gpu_util import TOL, assert_close, run_pass, to_np, upload
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import sparse_long_context_query_amd as hga  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hga.lib()
+
+
+def shp(**kw):
+    base = dict(name="t", batch=1, seq_len=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                seg_len=128, hist_block=32, query_block=32, top_k=3, dtype="bf16")
+    base.update(kw)
+    return HGAShape(**base)
+
+
+def compare_all(shape, inp, buf, segments=None, tol=None):
+    tol = tol or TOL[shape.dtype]
+    ref = orc.run(inp, shape, segments=segments, bwd=buf.dq is not None)
+    np.testing.assert_array_equal(to_np(buf.sel), ref["sel"])
+    errs = {}
+    for key in ("o", "lse") + (("dq", "dk", "dv") if buf.dq is not None else ()):
+        errs[key] = assert_close(key, to_np(getattr(buf, key)), ref[key], tol)
+    nblk_hist = (shape.seq_len - shape.seg_len) // shape.hist_block
+    if nblk_hist > 0:
+        assert_close("summ", to_np(buf.summ)[:, :, :nblk_hist], ref["kbar"][:, :, :nblk_hist],
+                     1e-6)
+    return errs
+
+
+# ------------------------------------------------------------ whole passes
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_2k"])
+def test_workload_pass_full_parity(name):
+    shape = WORKLOADS[name]
+    inp = make_inputs(shape, seed=0)
+    for s in range(shape.nseg):
+        assert orc.selection_gap(inp["q"], inp["k"], shape, s) >= 1e-3
+    buf = run_pass(shape, upload(inp, shape))
+    errs = compare_all(shape, inp, buf)
+    print(name, {k: f"{v:.2e}" for k, v in errs.items()})
+
+
+@pytest.mark.parametrize("shape", [
+    shp(),                                                     # several tiles, G=4
+    shp(query_block=16, hist_block=16, top_k=5),               # half-filled 32-row waves
+    shp(query_block=48, hist_block=48, seg_len=96, seq_len=480, top_k=2),  # ragged tiles
+    shp(n_q_heads=2, n_kv_heads=2, top_k=2),                   # G = 1
+    shp(n_q_heads=16, n_kv_heads=2, top_k=4),                  # G = 8
+    shp(head_dim=64, query_block=64, hist_block=64, seg_len=128, top_k=2),  # D = 64
+    shp(batch=2, seq_len=256, top_k=2),                        # batch 2
+    shp(seq_len=128, seg_len=128),                             # one segment, no history
+    shp(top_k=40),                                             # k covers all history
+    shp(seq_len=1024, seg_len=256, hist_block=16, query_block=64, top_k=24),  # many candidates
+    shp(dtype="f32", head_dim=64, n_q_heads=4, n_kv_heads=2),
+    shp(dtype="f32", head_dim=128, query_block=16, hist_block=8, top_k=5, seq_len=256),
+])
+def test_shape_variants_full_parity(shape):
+    inp = make_inputs(shape, seed=5)
+    buf = run_pass(shape, upload(inp, shape))
+    compare_all(shape, inp, buf)
+
+
+def test_k_all_equals_dense_causal():
+    """With k covering every history block the HGA forward is dense causal
+    attention (checked against torch SDPA in float64 on the CPU)."""
+    shape = WORKLOADS["qwen3_2k"].replace(top_k=WORKLOADS["qwen3_2k"].seq_len // 64)
+    inp = make_inputs(shape, seed=0)
+    buf = run_pass(shape, upload(inp, shape))
+    G = shape.group
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(inp["q"], dtype=torch.float64),
+        torch.tensor(inp["k"], dtype=torch.float64).repeat_interleave(G, 1),
+        torch.tensor(inp["v"], dtype=torch.float64).repeat_interleave(G, 1),
+        is_causal=True).numpy()
+    assert_close("o vs dense", to_np(buf.o), ref, TOL["bf16"])
+    compare_all(shape, inp, buf)
+
+
+def test_forward_only_without_lse():
+    shape = shp(seq_len=256)
+    inp = make_inputs(shape, seed=1, with_do=False)
+    dev = upload(inp, shape)
+    cfg = hga.Config.from_shape(shape)
+    buf = hga.Buffers(cfg, bwd=False)
+    for s in range(shape.nseg):
+        if s > 0:
+            hga.summarize(cfg, dev["k"], (s - 1) * shape.seg_len // shape.hist_block,
+                          s * shape.seg_len // shape.hist_block, buf.summ)
+        hga.select(cfg, dev["q"], buf.summ, s, buf.sel)
+        hga.attn_fwd(cfg, dev["q"], dev["k"], dev["v"], buf.sel, s, buf.o, None)
+    torch.cuda.synchronize()
+    ref = orc.run(inp, shape, bwd=False)
+    np.testing.assert_array_equal(to_np(buf.sel), ref["sel"])
+    assert_close("o", to_np(buf.o), ref["o"], TOL["bf16"])
+
+
+# ------------------------------------------------------ kernels one by one
+def test_selection_crafted_ties_and_order():
+    """Integer-valued keys and queries make every score exact in fp32: many
+    equal scores, ties must go to the lower block index."""
+    shape = shp(seq_len=1024, seg_len=128, hist_block=32, query_block=32, top_k=5,
+                n_q_heads=4, n_kv_heads=2)
+    rng = np.random.default_rng(3)
+    q = rng.integers(-1, 2, size=(1, 4, 1024, 128)).astype(np.float32)
+    k = np.repeat(rng.integers(-1, 2, size=(1, 2, 32, 1, 128)), 32, axis=3).reshape(1, 2, 1024, 128)
+    k = k.astype(np.float32)
+    v = rng.standard_normal((1, 2, 1024, 128)).astype(np.float32)
+    inp = {"q": q, "k": k, "v": v, "do": None, "shape": shape}
+    dev = upload(inp, shape)
+    cfg = hga.Config.from_shape(shape)
+    buf = hga.Buffers(cfg, bwd=False)
+    hga.summarize(cfg, dev["k"], 0, 1024 // 32, buf.summ)
+    for s in range(shape.nseg):
+        hga.select(cfg, dev["q"], buf.summ, s, buf.sel)
+    torch.cuda.synchronize()
+    nqb = shape.n_qblocks
+    n_ties = 0
+    for s in range(shape.nseg):
+        want = orc.select_segment(q, k, shape, s)
+        got = to_np(buf.sel)[:, :, s * nqb:(s + 1) * nqb]
+        np.testing.assert_array_equal(got, want)
+        if s == 0:
+            continue
+        sc = orc.block_scores(orc.query_means(q, 2, s * 128, 128, 32),
+                              orc.block_summaries(k, 32), s * 128 // 32)
+        for row in sc.reshape(-1, sc.shape[-1]):
+            n_ties += len(row) - len(np.unique(row))
+    assert n_ties > 50  # the case really exercises ties
+
+
+def test_summarize_matches_closed_form():
+    """K[t, d] = t//64 + 0.25*(t%64) - (d%16)/8 (all bf16-exact): the mean of
+    block i is i + 7.875 - (d%16)/8 exactly; rows outside the requested
+    block range stay untouched."""
+    shape = shp(seq_len=1024, hist_block=64, query_block=64, seg_len=256)
+    t = np.arange(1024)[None, None, :, None]
+    d = np.arange(128)[None, None, None, :]
+    k = np.broadcast_to((t // 64) + 0.25 * (t % 64) - (d % 16) / 8.0, (1, 2, 1024, 128))
+    k = k.astype(np.float32).copy()
+    dev = upload({"k": k}, shape)
+    cfg = hga.Config.from_shape(shape)
+    summ = torch.full(hga.Shapes(cfg).summ, -7.0, device="cuda")
+    hga.summarize(cfg, dev["k"], 3, 11, summ)
+    torch.cuda.synchronize()
+    got = to_np(summ)
+    i = np.arange(16)[:, None]
+    want = i + 7.875 - (np.arange(128)[None, :] % 16) / 8.0
+    for g in range(2):
+        np.testing.assert_array_equal(got[0, g, 3:11], want[3:11])
+    assert np.all(got[0, :, :3] == -7.0) and np.all(got[0, :, 11:] == -7.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gather_bit_exact(dtype):
+    shape = shp(dtype=dtype, top_k=4, seq_len=1024, seg_len=256, hist_block=32,
+                query_block=64, head_dim=64 if dtype == "f32" else 128)
+    inp = make_inputs(shape, seed=2, with_do=False)
+    dev = upload(inp, shape)
+    cfg = hga.Config.from_shape(shape)
+    s_ = hga.Shapes(cfg)
+    seg = 3
+    sel = torch.full(s_.sel, -1, dtype=torch.int32, device="cuda")
+    nqb = shape.n_qblocks
+    rows = np.array([[5, 0, 17, -1], [23, 3, -1, -1], [1, 2, 3, 4], [-1, -1, -1, -1]],
+                    dtype=np.int32)
+    sel_np = np.full(s_.sel, -1, dtype=np.int32)
+    sel_np[:, :, seg * nqb:(seg + 1) * nqb] = rows[None, None]
+    sel_np[0, 1, seg * nqb] = [7, 99, -5, 2]  # out-of-range entries read as padding
+    sel.copy_(torch.from_numpy(sel_np))
+    ko = torch.empty(s_.gather, dtype=dev["k"].dtype, device="cuda")
+    vo = torch.empty_like(ko)
+    hga.gather(cfg, dev["k"], dev["v"], sel, seg, ko, vo)
+    torch.cuda.synchronize()
+    cleaned = sel_np[:, :, seg * nqb:(seg + 1) * nqb].copy()
+    cleaned[(cleaned < 0) | (cleaned >= seg * 256 // 32)] = -1
+    np.testing.assert_array_equal(to_np(ko), orc.gather_blocks(inp["k"], cleaned, 32))
+    np.testing.assert_array_equal(to_np(vo), orc.gather_blocks(inp["v"], cleaned, 32))
+
+
+def test_attention_with_arbitrary_selection():
+    """Forward/backward with a selection that is not top-k (unsorted,
+    repeated-free, padded): the kernels attend exactly the listed blocks."""
+    shape = shp(seq_len=512, seg_len=128, top_k=4)
+    inp = make_inputs(shape, seed=8)
+    dev = upload(inp, shape)
+    cfg = hga.Config.from_shape(shape)
+    buf = hga.Buffers(cfg)
+    seg = 3
+    rng = np.random.default_rng(0)
+    nqb = shape.n_qblocks
+    sel_np = np.full(hga.Shapes(cfg).sel, -1, dtype=np.int32)
+    for g in range(2):
+        for j in range(nqb):
+            n = rng.integers(0, 5)
+            sel_np[0, g, seg * nqb + j, :n] = rng.choice(12, size=n, replace=False)
+    buf.sel.copy_(torch.from_numpy(sel_np))
+    hga.attn_fwd(cfg, dev["q"], dev["k"], dev["v"], buf.sel, seg, buf.o, buf.lse)
+    hga.attn_bwd(cfg, dev["q"], dev["k"], dev["v"], buf.o, buf.lse, dev["do"], buf.sel, seg,
+                 buf.dq, buf.dk, buf.dv, buf.ws)
+    torch.cuda.synchronize()
+    sel_seg = sel_np[:, :, seg * nqb:(seg + 1) * nqb]
+    O, LSE = orc.segment_forward(inp["q"], inp["k"], inp["v"], sel_seg, shape, seg)
+    dQ, dK, dV = orc.segment_backward(inp["q"], inp["k"], inp["v"], inp["do"], sel_seg, shape,
+                                      seg, O, LSE)
+    t0, L = seg * 128, 128
+    assert_close("o", to_np(buf.o)[:, :, t0:t0 + L], O, TOL["bf16"])
+    assert_close("lse", to_np(buf.lse)[:, :, t0:t0 + L], LSE, TOL["bf16"])
+    assert_close("dq", to_np(buf.dq)[:, :, t0:t0 + L], dQ, TOL["bf16"])
+    assert_close("dk", to_np(buf.dk)[:, :, t0:t0 + L], dK, TOL["bf16"])
+    assert_close("dv", to_np(buf.dv)[:, :, t0:t0 + L], dV, TOL["bf16"])
+    # rows outside the segment untouched
+    assert not to_np(buf.o)[:, :, :t0].any() and not to_np(buf.dk)[:, :, :t0].any()
+
+
+# ------------------------------------------------------- determinism, resume
+def test_bitwise_deterministic():
+    shape = WORKLOADS["qwen3_2k"]
+    inp = make_inputs(shape, seed=0)
+    dev = upload(inp, shape)
+    a = run_pass(shape, dev)
+    b = run_pass(shape, dev)
+    for key in ("summ", "sel", "o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(getattr(a, key), getattr(b, key)), key
+
+
+def test_resume_from_segment_state():
+    """The resumable state of a segmented pass is the summary table (plus
+    the inputs): restarting at segment s with a copy of it gives the same
+    outputs as the uninterrupted pass."""
+    shape = WORKLOADS["qwen3_2k"]
+    inp = make_inputs(shape, seed=0)
+    dev = upload(inp, shape)
+    full = run_pass(shape, dev)
+    cfg = hga.Config.from_shape(shape)
+    first = hga.Buffers(cfg)
+    first.run_pass(dev["q"], dev["k"], dev["v"], dev["do"], segments=range(0, 2))
+    second = hga.Buffers(cfg)
+    second.summ.copy_(first.summ)
+    second.run_pass(dev["q"], dev["k"], dev["v"], dev["do"], segments=range(2, shape.nseg))
+    torch.cuda.synchronize()
+    t = 2 * shape.seg_len
+    for key in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(getattr(second, key)[:, :, t:], getattr(full, key)[:, :, t:]), key
