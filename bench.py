@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--dense-sdpa", action="store_true",
                     help="also time torch SDPA (flash backend) dense causal fwd+bwd")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device-to-device copy (a known-size "
+                         "reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -125,6 +128,14 @@ def main():
     hga.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     shape = WORKLOADS[args.workload]
     bwd = shape.bwd

@@ -63,16 +63,19 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o,
 }
 
 // ---------------------------------------------------------------------------
-// a7, bf16 MFMA: dq.  Same work split as the forward (4 waves of 32 query
-// rows sharing one (b, g, j) key set), 32-key tiles staged through LDS as
-// K row-major, V row-major and K transposed.  Per wave and tile:
+// a7, bf16 MFMA: dq.  Same work split as the forward: 512 threads = 8 waves,
+// up to 4 wave rows (32 queries of one head each) of one (b, g, j) unit per
+// block of threads; the key tiles (32 keys) are split in two halves walked
+// by waves 0-3 and 4-7, each half with its own double-buffered LDS stream
+// (K row-major, V row-major, K transposed).  Per wave and tile:
 //   S^T  = K . Q^T          (Q^T in registers as B operand)
 //   dP^T = V . dO^T         (dO^T in registers as B operand)
 //   dS^T = P^T * (dP^T - delta),  P^T = exp2(S^T c2 - lse2)
 //   dQ^T += K^T . dS^T      (dS^T straight from the accumulator)
+// The two halves' partial dQ^T are added through LDS at the end.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void dq_bf16_kernel(
+__global__ __launch_bounds__(512) void dq_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, const float* __restrict__ lse,
     const __bf16* __restrict__ dO, const float* __restrict__ delta,
@@ -83,10 +86,10 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int JOB_C = D / 8;
+  constexpr int STAGE = 2 * G_::ROW_ELEMS + G_::T_ELEMS;  // K rows, V rows, K^T
+  static_assert(4 * STAGE * 2 >= 4 * NDB * 16 * 64 * 4, "merge buffer fits");
 
-  __shared__ __bf16 s_k[2][G_::ROW_ELEMS];
-  __shared__ __bf16 s_v[2][G_::ROW_ELEMS];
-  __shared__ __bf16 s_kt[2][G_::T_ELEMS];
+  __shared__ __attribute__((aligned(16))) __bf16 s_tiles[2][2][STAGE];  // [half][buf]
   __shared__ int s_hlist[kMaxTopK];
   __shared__ int s_hcount;
 
@@ -99,10 +102,13 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
   const int nb = t0 / a.Bh;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lq = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
+  const int half = wave >> 2, wr = wave & 3;
+  const int htid = tid & 255;
 
   const int nwr = a.G * a.nq32;
-  const int idx = c * 4 + wave;
+  const int idx = c * 4 + wr;
   const bool active = idx < nwr;
   const int qs = idx / a.G, hh = idx % a.G;
   const int h = g * a.G + hh;
@@ -123,6 +129,9 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
   KeySource<TK> src;
   src.init(s_hlist, nsel, a.Bh, t0, t0 + a.L);
   const int ntiles = src.n_hist_tiles + (blk_qmax - t0) / TK + 1;
+  const int n0 = (ntiles + 1) / 2;
+  const int my_first = half ? n0 : 0;
+  const int my_count = half ? ntiles - n0 : n0;
 
   const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
   const __bf16* kg = k + kv_base;
@@ -134,79 +143,97 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
   bf16x8 qreg[NKK], doreg[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    if (row_ok) {
-      qreg[kk] = *reinterpret_cast<const bf16x8*>(q + qrow * D + 16 * kk + 8 * hi);
-      doreg[kk] = *reinterpret_cast<const bf16x8*>(dO + qrow * D + 16 * kk + 8 * hi);
-    } else {
-      qreg[kk] = bf16x8{};
-      doreg[kk] = bf16x8{};
-    }
+    qreg[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(q + qrow * D + 16 * kk + 8 * hi) : bf16x8{};
+    doreg[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(dO + qrow * D + 16 * kk + 8 * hi) : bf16x8{};
   }
   const float lse2 = row_ok ? lse[qrow] * kLog2e : 0.f;
   const float dlt = row_ok ? delta[(size_t)(b * a.Hq + h) * a.L + (tq - t0)] : 0.f;
 
-  const bool has_job = tid < G_::NJOB;
-  const int rq = tid / JOB_C, cc = tid % JOB_C;
-  uint4 kr[4], vr[4];
-  auto load_tile = [&](int it) {
+  const bool has_job = htid < G_::NJOB;
+  const int rq = htid / JOB_C, cc = htid % JOB_C;
+  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+
+#define HGA_DQ_LOAD(IT)                                                          \
+  do {                                                                           \
+    const int tok_ = has_job ? src.token4((IT), 4 * rq) : -1;                    \
+    if (tok_ >= 0) {                                                             \
+      const __bf16* kp_ = kg + (size_t)tok_ * D + 8 * cc;                         \
+      const __bf16* vp_ = vg + (size_t)tok_ * D + 8 * cc;                         \
+      k0 = *reinterpret_cast<const uint4*>(kp_);                                 \
+      k1 = *reinterpret_cast<const uint4*>(kp_ + D);                             \
+      k2 = *reinterpret_cast<const uint4*>(kp_ + 2 * D);                         \
+      k3 = *reinterpret_cast<const uint4*>(kp_ + 3 * D);                         \
+      v0 = *reinterpret_cast<const uint4*>(vp_);                                 \
+      v1 = *reinterpret_cast<const uint4*>(vp_ + D);                             \
+      v2 = *reinterpret_cast<const uint4*>(vp_ + 2 * D);                         \
+      v3 = *reinterpret_cast<const uint4*>(vp_ + 3 * D);                         \
+    } else {                                                                     \
+      k0 = k1 = k2 = k3 = v0 = v1 = v2 = v3 = z4;                                \
+    }                                                                            \
+  } while (0)
+
+  auto store_stage = [&](__bf16* st) {
     if (!has_job) return;
-    const int tok = src.token4(it, 4 * rq);
-    if (tok < 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { kr[i] = make_uint4(0, 0, 0, 0); vr[i] = kr[i]; }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kr[i] = *reinterpret_cast<const uint4*>(kg + (size_t)(tok + i) * D + 8 * cc);
-      vr[i] = *reinterpret_cast<const uint4*>(vg + (size_t)(tok + i) * D + 8 * cc);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    if (!has_job) return;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(&s_k[buf][(4 * rq + i) * KSTR + 8 * cc]) = kr[i];
-      *reinterpret_cast<uint4*>(&s_v[buf][(4 * rq + i) * KSTR + 8 * cc]) = vr[i];
-    }
+    __bf16* ks = st;
+    __bf16* vs = st + G_::ROW_ELEMS;
+    __bf16* kts = st + 2 * G_::ROW_ELEMS;
+    *reinterpret_cast<uint4*>(&ks[(4 * rq + 0) * KSTR + 8 * cc]) = k0;
+    *reinterpret_cast<uint4*>(&ks[(4 * rq + 1) * KSTR + 8 * cc]) = k1;
+    *reinterpret_cast<uint4*>(&ks[(4 * rq + 2) * KSTR + 8 * cc]) = k2;
+    *reinterpret_cast<uint4*>(&ks[(4 * rq + 3) * KSTR + 8 * cc]) = k3;
+    *reinterpret_cast<uint4*>(&vs[(4 * rq + 0) * KSTR + 8 * cc]) = v0;
+    *reinterpret_cast<uint4*>(&vs[(4 * rq + 1) * KSTR + 8 * cc]) = v1;
+    *reinterpret_cast<uint4*>(&vs[(4 * rq + 2) * KSTR + 8 * cc]) = v2;
+    *reinterpret_cast<uint4*>(&vs[(4 * rq + 3) * KSTR + 8 * cc]) = v3;
     const int pos = tpos(4 * rq);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<uint2*>(&s_kt[buf][toff<TK>(8 * cc + e, pos)]) =
-          quad_column(kr[0], kr[1], kr[2], kr[3], e);
+      *reinterpret_cast<uint2*>(&kts[toff<TK>(8 * cc + e, pos)]) = quad_column(k0, k1, k2, k3, e);
   };
 
   floatx16 dqacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqacc[db] = floatx16{};
 
-  load_tile(0);
-  store_tile(0);
+  if (my_count > 0) HGA_DQ_LOAD(my_first);
+  if (my_count > 0) store_stage(s_tiles[half][0]);
+  drain_vmem_loads();
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < ntiles) load_tile(it + 1);
+  for (int i = 0; i < n0; ++i) {
+    const int it = my_first + i;
+    const bool mine = i < my_count;
+    if (i + 1 < my_count) HGA_DQ_LOAD(it + 1);
     const bool is_local = it >= src.n_hist_tiles;
     const int local_first = t0 + (it - src.n_hist_tiles) * TK;
-    const bool work = active && (!is_local || local_first <= wave_qmax);
+    const bool work = mine && active && (!is_local || local_first <= wave_qmax);
     if (work) {
-      const __bf16* kt = s_k[buf];
-      const __bf16* vt = s_v[buf];
-      const __bf16* ktt = s_kt[buf];
+      const __bf16* kt = s_tiles[half][i & 1];
+      const __bf16* vt = kt + G_::ROW_ELEMS;
+      const __bf16* ktt = kt + 2 * G_::ROW_ELEMS;
       floatx16 sacc = floatx16{}, pacc = floatx16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         sacc = mfma32(lds_b128(kt + lq * KSTR + 16 * kk + 8 * hi), qreg[kk], sacc);
         pacc = mfma32(lds_b128(vt + lq * KSTR + 16 * kk + 8 * hi), doreg[kk], pacc);
       }
-      const int hist_first = it * TK;
+      const bool need_mask = is_local ? (local_first + TK - 1 > qfirst) : ((it + 1) * TK > src.nh);
+      if (need_mask) {
+        const int base = is_local ? local_first : it * TK;
+        const int lim = is_local ? tq : src.nh - 1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr_ = 8 * (r >> 2) + 4 * hi + (r & 3);
-        const bool ok = is_local ? (local_first + kr_ <= tq) : (hist_first + kr_ < src.nh);
-        const float p = ok ? exp2f(sacc[r] * a.c2 - lse2) : 0.f;
-        sacc[r] = p * (pacc[r] - dlt);  // dS^T
+        for (int r = 0; r < 16; ++r) {
+          const int kr_ = base + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const float p = (kr_ <= lim) ? exp2f(sacc[r] * a.c2 - lse2) : 0.f;
+          sacc[r] = p * (pacc[r] - dlt);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2f(sacc[r] * a.c2 - lse2);
+          sacc[r] = p * (pacc[r] - dlt);
+        }
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -219,21 +246,32 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
           dqacc[db] = mfma32(lds_b128(ktt + toff<TK>(32 * db + lq, pos)), sb, dqacc[db]);
       }
     }
-    if (it + 1 < ntiles) store_tile(buf ^ 1);
+    if (i + 1 < my_count) store_stage(s_tiles[half][(i + 1) & 1]);
     __syncthreads();
   }
+#undef HGA_DQ_LOAD
 
-  if (active && row_ok) {
+  // add the two halves' partial dQ^T through LDS, scale, round, store
+  float* park = reinterpret_cast<float*>(&s_tiles[0][0][0]) + wr * (NDB * 16 * 64);
+  if (half == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) park[(db * 16 + r) * 64 + lane] = dqacc[db][r];
+  }
+  __syncthreads();
+  if (half == 0 && active && row_ok) {
     __bf16* op = dq + qrow * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         bf16x4 pk;
-        pk[0] = (__bf16)(dqacc[db][4 * r4 + 0] * a.scale);
-        pk[1] = (__bf16)(dqacc[db][4 * r4 + 1] * a.scale);
-        pk[2] = (__bf16)(dqacc[db][4 * r4 + 2] * a.scale);
-        pk[3] = (__bf16)(dqacc[db][4 * r4 + 3] * a.scale);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          pk[e] = (__bf16)((dqacc[db][r] + park[(db * 16 + r) * 64 + lane]) * a.scale);
+        }
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * r4 + 4 * hi) = pk;
       }
     }
@@ -241,20 +279,22 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// a8, bf16 MFMA: dk/dv of the local keys.  One block of threads per
-// (b, g, 32-key tile kt of the segment); its 4 waves split the (query head,
-// 32-query tile) pairs that see the key tile (query tiles kt.. of every
-// head of the group) round-robin, each accumulating dK^T and dV^T for the
-// 32 keys in registers; the 4 partial sums are folded through LDS at the
-// end.  Per wave and pair (K and V rows of the tile in registers):
-//   S  = Q . K^T   (Q rows straight from memory as A operand)
-//   dP = dO . V^T  (dO rows likewise)
+// a8, bf16 MFMA: dk/dv of the local keys.  One block of threads (8 waves)
+// per (b, g, 32-key tile kt of the segment).  The (query head, 32-query
+// tile) pairs that see the key tile (query tiles kt.. of every head of the
+// group) are dealt round-robin to the 8 waves, two per SIMD, so one wave's
+// loads and softmax overlap the other's MFMAs.  A wave copies its pair's Q
+// and dO tiles and their lse / delta straight from memory into its own
+// swizzled LDS slice (no register staging), then, with the key tile's K
+// and V rows held in registers as B operands:
+//   S  = Q . K^T,  dP = dO . V^T      (A operands: tile rows)
 //   P  = exp2(S c2 - lse2), dS = P * (dP - delta)
-//   dV^T += dO^T . P,  dK^T += Q^T . dS   (dO^T, Q^T staged transposed into
-//                                          the wave's own LDS slice)
+//   dV^T += dO^T . P,  dK^T += Q^T . dS   (A operands: transposed reads of
+//                                          the same tiles)
+// The 8 partial dK^T, dV^T are folded pairwise through LDS at the end.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void dkdv_bf16_kernel(
+__global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, const float* __restrict__ lse,
     const __bf16* __restrict__ dO, const float* __restrict__ delta,
@@ -262,12 +302,13 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
   constexpr int TQ = 32;                 // queries per tile
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int T_ELEMS = D * TQ;        // one transposed tile
-  constexpr int RSTR = D + 4;            // fp32 fold row stride
-  constexpr int LDS_STAGE = 4 * 2 * T_ELEMS * 2;        // bytes: 4 waves x (Qt, dOt)
-  constexpr int LDS_FOLD = 4 * 32 * RSTR * 4;           // bytes: 4 waves x 32 keys x D fp32
-  constexpr int LDS_BYTES = LDS_STAGE > LDS_FOLD ? LDS_STAGE : LDS_FOLD;
-  __shared__ __attribute__((aligned(16))) unsigned char s_raw[LDS_BYTES];
+  constexpr int TILE_B = TQ * 2 * D;     // bytes of one row-major tile
+  constexpr int SLICE_B = 2 * TILE_B + 256;  // Q tile, dO tile, lse + delta
+  constexpr int NW = 8;
+  constexpr int PART_F = 2 * NDB * 16 * 64;  // floats of one wave's (dK^T, dV^T)
+  constexpr int STAGE_B = 2 * TILE_B + NW * SLICE_B;  // K, V tiles + wave slices
+  constexpr int LDS_BYTES = STAGE_B > 4 * PART_F * 4 ? STAGE_B : 4 * PART_F * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char s_raw[LDS_BYTES];
 
   const int nkt = (a.L + 31) / 32;
   const int w = xcd_remap(blockIdx.x, gridDim.x);
@@ -278,26 +319,24 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
   const int tend = t0 + a.L;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lq = lane & 31, hi = lane >> 5;
-  __bf16* s_qt = reinterpret_cast<__bf16*>(s_raw) + wave * 2 * T_ELEMS;
-  __bf16* s_dot = s_qt + T_ELEMS;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
+  unsigned char* s_k = s_raw;
+  unsigned char* s_v = s_raw + TILE_B;
+  unsigned char* s_q = s_raw + 2 * TILE_B + wave * SLICE_B;
+  unsigned char* s_do = s_q + TILE_B;
+  float* s_ld = reinterpret_cast<float*>(s_do + TILE_B);  // [0,32) lse, [32,64) delta
 
-  // K and V rows of this key tile as B operands: lane (key lq, hi) holds
-  // K[key][16kk + 8hi .. +7]
-  const int tk = t0 + kt * 32 + lq;
+  // K and V rows of this key tile, shared by the 8 waves as B operands
+  // (lane (key lq, hi) reads K[key][16kk + 8hi .. +7])
+  const int kfirst = t0 + kt * 32;
+  const int tk = kfirst + lq;
   const bool key_ok = tk < tend;
   const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
-  bf16x8 kreg[NKK], vreg[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    if (key_ok) {
-      kreg[kk] = *reinterpret_cast<const bf16x8*>(k + kv_base + (size_t)tk * D + 16 * kk + 8 * hi);
-      vreg[kk] = *reinterpret_cast<const bf16x8*>(v + kv_base + (size_t)tk * D + 16 * kk + 8 * hi);
-    } else {
-      kreg[kk] = bf16x8{};
-      vreg[kk] = bf16x8{};
-    }
-  }
+  if (wave == 0) dma_rows<D>(k + kv_base + (size_t)kfirst * D, 32, tend - kfirst, s_k, lane);
+  if (wave == 1) dma_rows<D>(v + kv_base + (size_t)kfirst * D, 32, tend - kfirst, s_v, lane);
+  drain_vmem_loads();
+  __syncthreads();
 
   floatx16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
@@ -305,77 +344,50 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
 
   const int nqt = (a.L + TQ - 1) / TQ;
   const int npairs = (nqt - kt) * a.G;
-  for (int pi = wave; pi < npairs; pi += 4) {
+  for (int pi = wave; pi < npairs; pi += NW) {
     const int qt = kt + pi / a.G;
-    const int hh = pi % a.G;
-    const int h = g * a.G + hh;
+    const int h = g * a.G + pi % a.G;
     const int tq0 = t0 + qt * TQ;
     const size_t hrow = (size_t)(b * a.Hq + h) * a.S;
-
-    // Q and dO rows as A operands: lane (row lq, hi)
-    const bool qrow_ok = tq0 + lq < tend;
-    bf16x8 qa[NKK], da[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      if (qrow_ok) {
-        qa[kk] = *reinterpret_cast<const bf16x8*>(q + (hrow + tq0 + lq) * D + 16 * kk + 8 * hi);
-        da[kk] = *reinterpret_cast<const bf16x8*>(dO + (hrow + tq0 + lq) * D + 16 * kk + 8 * hi);
-      } else {
-        qa[kk] = bf16x8{};
-        da[kk] = bf16x8{};
-      }
+    const int nvalid = min(TQ, tend - tq0);
+    // stage the pair: tiles by direct loads, lse / delta one dword per lane
+    dma_rows<D>(q + (hrow + tq0) * D, TQ, nvalid, s_q, lane);
+    dma_rows<D>(dO + (hrow + tq0) * D, TQ, nvalid, s_do, lane);
+    {
+      const int tl = tq0 + min(lq, nvalid - 1);
+      const float* src_ = hi == 0 ? lse + hrow + tl
+                                  : delta + (size_t)(b * a.Hq + h) * a.L + (tl - t0);
+      __builtin_amdgcn_global_load_lds((const void*)src_, to_lds(s_ld), 4, 0, 0);
     }
-    // lse2 and delta of the 16 query rows this lane holds in C layout
-    float lse2[16], dl[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tqr = tq0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const bool ok = tqr < tend;
-      lse2[r] = ok ? lse[hrow + tqr] * kLog2e : 0.f;
-      dl[r] = ok ? delta[(size_t)(b * a.Hq + h) * a.L + (tqr - t0)] : 0.f;
-    }
-    // stage Q^T and dO^T into this wave's LDS slice: jobs of 4 rows x 8 dims
-#pragma unroll
-    for (int jb = lane; jb < (TQ / 4) * (D / 8); jb += 64) {
-      const int rq = jb / (D / 8), cc = jb % (D / 8);
-      uint4 x[4], y[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = tq0 + 4 * rq + i;
-        if (t < tend) {
-          x[i] = *reinterpret_cast<const uint4*>(q + (hrow + t) * D + 8 * cc);
-          y[i] = *reinterpret_cast<const uint4*>(dO + (hrow + t) * D + 8 * cc);
-        } else {
-          x[i] = make_uint4(0, 0, 0, 0);
-          y[i] = x[i];
-        }
-      }
-      const int pos = tpos(4 * rq);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        *reinterpret_cast<uint2*>(&s_qt[toff<TQ>(8 * cc + e, pos)]) =
-            quad_column(x[0], x[1], x[2], x[3], e);
-        *reinterpret_cast<uint2*>(&s_dot[toff<TQ>(8 * cc + e, pos)]) =
-            quad_column(y[0], y[1], y[2], y[3], e);
-      }
-    }
+    drain_vmem_loads();
     wave_lds_sync();
 
     floatx16 sacc = floatx16{}, pacc = floatx16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      sacc = mfma32(qa[kk], kreg[kk], sacc);
-      pacc = mfma32(da[kk], vreg[kk], pacc);
+      sacc = mfma32(row_fragment<D>(s_q, lq, kk, hi), row_fragment<D>(s_k, lq, kk, hi), sacc);
+      pacc = mfma32(row_fragment<D>(s_do, lq, kk, hi), row_fragment<D>(s_v, lq, kk, hi), pacc);
     }
     // C layout: lane = key lq, item r = query row 8(r/4)+4hi+(r%4) of the tile
+    const bool need_mask = (tq0 < kfirst + 31) || (nvalid < TQ) || (kfirst + 32 > tend);
     float pv[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tqr = tq0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const bool ok = key_ok && tk <= tqr && tqr < tend;
-      const float p = ok ? exp2f(sacc[r] * a.c2 - lse2[r]) : 0.f;
-      pv[r] = p;
-      sacc[r] = p * (pacc[r] - dl[r]);  // dS
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&s_ld[8 * r4 + 4 * hi]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&s_ld[32 + 8 * r4 + 4 * hi]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dv_[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * r4 + e;
+        float p = exp2f(sacc[r] * a.c2 - lv[e] * kLog2e);
+        if (need_mask) {
+          const int tqr = tq0 + 8 * r4 + 4 * hi + e;
+          p = (key_ok && tk <= tqr && tqr < tend) ? p : 0.f;
+        }
+        pv[r] = p;
+        sacc[r] = p * (pacc[r] - dv_[e]);  // dS
+      }
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -384,52 +396,59 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
                                   pv[r0 + 5], pv[r0 + 6], pv[r0 + 7]);
       const bf16x8 sb = to_bf16x8(sacc[r0], sacc[r0 + 1], sacc[r0 + 2], sacc[r0 + 3],
                                   sacc[r0 + 4], sacc[r0 + 5], sacc[r0 + 6], sacc[r0 + 7]);
-      const int pos = 16 * ks + 8 * hi;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        dvacc[db] = mfma32(lds_b128(s_dot + toff<TQ>(32 * db + lq, pos)), pb, dvacc[db]);
-        dkacc[db] = mfma32(lds_b128(s_qt + toff<TQ>(32 * db + lq, pos)), sb, dkacc[db]);
+        dvacc[db] = mfma32(tr_fragment<D>(s_do, 16 * ks, db, lane), pb, dvacc[db]);
+        dkacc[db] = mfma32(tr_fragment<D>(s_q, 16 * ks, db, lane), sb, dkacc[db]);
       }
     }
-    wave_lds_sync();
+    wave_lds_sync();  // this slice's reads are done before the next pair's loads land
   }
 
-  // fold the 4 waves' partial sums through LDS, then scale / round / store
-  __syncthreads();
+  // fold the 8 partial sums pairwise through LDS: 8 -> 4 -> 2 -> 1 (the
+  // first barrier also retires every wave's reads of the K/V tiles)
   float* fold = reinterpret_cast<float*>(s_raw);
-  for (int pass = 0; pass < 2; ++pass) {
-    const floatx16* acc = pass == 0 ? dkacc : dvacc;
+  for (int span = NW / 2; span >= 1; span >>= 1) {
+    __syncthreads();
+    if (wave >= span && wave < 2 * span) {
+      float* dst = fold + (wave - span) * PART_F;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          dst[((0 * NDB + db) * 16 + r) * 64 + lane] = dkacc[db][r];
+          dst[((1 * NDB + db) * 16 + r) * 64 + lane] = dvacc[db][r];
+        }
+    }
+    __syncthreads();
+    if (wave < span) {
+      const float* src_ = fold + wave * PART_F;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          dkacc[db][r] += src_[((0 * NDB + db) * 16 + r) * 64 + lane];
+          dvacc[db][r] += src_[((1 * NDB + db) * 16 + r) * 64 + lane];
+        }
+    }
+  }
+  if (wave == 0 && key_ok) {
+    __bf16* kp = dk + kv_base + (size_t)tk * D;
+    __bf16* vp = dv + kv_base + (size_t)tk * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        float4 val = make_float4(acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2],
-                                 acc[db][4 * r4 + 3]);
-        *reinterpret_cast<float4*>(&fold[(wave * 32 + lq) * RSTR + 32 * db + 8 * r4 + 4 * hi]) = val;
-      }
-    }
-    __syncthreads();
-    const float mul = pass == 0 ? a.scale : 1.f;
-    __bf16* outp = pass == 0 ? dk : dv;
-    constexpr int PER = D / 8;  // 8 threads per key row
-    const int key = tid / 8, d0 = (tid % 8) * PER;
-    const int tko = t0 + kt * 32 + key;
-    if (tko < tend) {
+        bf16x4 pk, pw;
 #pragma unroll
-      for (int e = 0; e < PER; e += 4) {
-        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-          const float4 x = *reinterpret_cast<const float4*>(&fold[(ww * 32 + key) * RSTR + d0 + e]);
-          s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
+        for (int e = 0; e < 4; ++e) {
+          pk[e] = (__bf16)(dkacc[db][4 * r4 + e] * a.scale);
+          pw[e] = (__bf16)(dvacc[db][4 * r4 + e]);
         }
-        bf16x4 pk;
-        pk[0] = (__bf16)(s.x * mul); pk[1] = (__bf16)(s.y * mul);
-        pk[2] = (__bf16)(s.z * mul); pk[3] = (__bf16)(s.w * mul);
-        *reinterpret_cast<bf16x4*>(outp + kv_base + (size_t)tko * D + d0 + e) = pk;
+        *reinterpret_cast<bf16x4*>(kp + 32 * db + 8 * r4 + 4 * hi) = pk;
+        *reinterpret_cast<bf16x4*>(vp + 32 * db + 8 * r4 + 4 * hi) = pw;
       }
     }
-    __syncthreads();
   }
 }
 
@@ -614,7 +633,7 @@ hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
   {
     const int nblocks = p.B * p.Hkv * p.nqb * a.wpu;
     ProfScope ps(HGA_K_BWD_DQ, st);
-    hipLaunchKernelGGL((dq_bf16_kernel<D>), dim3(nblocks), dim3(256), 0, st, (const __bf16*)q,
+    hipLaunchKernelGGL((dq_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dO, delta, sel,
                        (__bf16*)dq, a);
     e = hipGetLastError();
@@ -623,7 +642,7 @@ hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
   {
     const int nblocks = p.B * p.Hkv * ((p.L + 31) / 32);
     ProfScope ps(HGA_K_BWD_DKDV, st);
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D>), dim3(nblocks), dim3(256), 0, st,
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, lse,
                        (const __bf16*)dO, delta, (__bf16*)dk, (__bf16*)dv, a);
     e = hipGetLastError();

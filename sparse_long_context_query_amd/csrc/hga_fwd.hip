@@ -28,17 +28,26 @@ struct FwdArgs {
 };
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel.  256 threads = 4 waves; each wave owns 32 query rows of
-// one head (a "wave row": query sub-block qs of 32 tokens, head hh of the
-// group); the waves of a block of threads share one (b, g, j) unit and so
-// one key set, which is staged through LDS in 64-key tiles (K row-major,
-// V transposed), double buffered with the next tile's global loads in
-// registers.  Per wave and tile: S^T = K.Q^T (keys x queries, Q^T held in
-// registers as the B operand), online softmax per query (one query per
-// lane pair), O^T += V^T.P^T with P^T fed straight from the accumulator.
+// bf16 MFMA kernel.  512 threads = 8 waves.  A block of threads owns up to 4
+// "wave rows" of one (b, g, j) unit (a wave row = 32 query tokens of one
+// head: query sub-block qs, head hh of the group), so all its waves share
+// one key set.  The key tiles (64 keys; history tiles first, then local
+// tiles) are split in two halves: waves 0-3 walk the first half and waves
+// 4-7 the second, each half with its own double-buffered LDS stream (K
+// row-major, V transposed; the next tile's global loads held in registers
+// while the current one is computed).  Two waves per SIMD let one wave's
+// softmax overlap the other's MFMAs.  The halves' partial (O, m, l) are
+// merged through LDS at the end (log-sum-exp rule).
+// Per wave and tile: S^T = K.Q^T (Q^T in registers as B operand), online
+// softmax per query, O^T += V^T.P^T with P^T taken from the accumulator.
+// The running max is only raised when a tile max exceeds it by more than
+// kRescale (log2 units), so O is rarely rescaled; exp2 arguments stay below
+// kRescale and the final normalisation is exact either way.
 // ---------------------------------------------------------------------------
+constexpr float kRescale = 8.f;
+
 template <int D>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(
+__global__ __launch_bounds__(512) void fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, const int32_t* __restrict__ sel,
     __bf16* __restrict__ o, float* __restrict__ lse, FwdArgs a) {
@@ -48,9 +57,10 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   constexpr int NKK = D / 16;  // MFMA k-steps over the head dim
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
   constexpr int JOB_C = D / 8;
+  constexpr int STAGE = G_::ROW_ELEMS + G_::T_ELEMS;  // one tile (K rows + V^T)
+  static_assert(4 * STAGE * 2 >= 4 * (NDB * 16 * 64 + 2 * 64) * 4, "merge buffer fits");
 
-  __shared__ __bf16 s_k[2][G_::ROW_ELEMS];
-  __shared__ __bf16 s_vt[2][G_::T_ELEMS];
+  __shared__ __attribute__((aligned(16))) __bf16 s_tiles[2][2][STAGE];  // [half][buf]
   __shared__ int s_hlist[kMaxTopK];
   __shared__ int s_hcount;
 
@@ -63,11 +73,13 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   const int nb = t0 / a.Bh;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lq = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
+  const int half = wave >> 2, wr = wave & 3;
+  const int htid = tid & 255;  // thread index within the half
 
-  // wave row of this wave and the block's last query token
   const int nwr = a.G * a.nq32;
-  const int idx = c * 4 + wave;
+  const int idx = c * 4 + wr;
   const bool active = idx < nwr;
   const int qs = idx / a.G, hh = idx % a.G;
   const int h = g * a.G + hh;
@@ -83,59 +95,66 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     }
   }
 
-  // selected history blocks of this unit
   const int32_t* srow = sel + ((size_t)(b * a.Hkv + g) * a.nqb_all + (size_t)a.seg * a.nqb + j) * a.K;
   const int nsel = compact_selection(srow, a.K, nb, s_hlist, &s_hcount);
   KeySource<TK> src;
   src.init(s_hlist, nsel, a.Bh, t0, t0 + a.L);
-  const int n_local_tiles = (blk_qmax - t0) / TK + 1;
-  const int ntiles = src.n_hist_tiles + n_local_tiles;
+  const int ntiles = src.n_hist_tiles + (blk_qmax - t0) / TK + 1;
+  const int n0 = (ntiles + 1) / 2;              // tiles of half 0
+  const int my_first = half ? n0 : 0;
+  const int my_count = half ? ntiles - n0 : n0;
 
   const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
   const __bf16* kg = k + kv_base;
   const __bf16* vg = v + kv_base;
 
-  // Q^T as the B operand: lane (query lq, hi) holds Q[t][16kk+8hi .. +7]
   const int tq = qfirst + lq;
   const bool row_ok = lq < nvalid;
   bf16x8 qreg[NKK];
   {
     const __bf16* qp = q + ((size_t)(b * a.Hq + h) * a.S + tq) * D + 8 * hi;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      if (row_ok) qreg[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
-      else qreg[kk] = bf16x8{};
-    }
+    for (int kk = 0; kk < NKK; ++kk)
+      qreg[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * kk) : bf16x8{};
   }
 
-  // staging: job = (4-row group rq, 8-dim chunk cc)
-  const bool has_job = tid < G_::NJOB;
-  const int rq = tid / JOB_C, cc = tid % JOB_C;
-  uint4 kr[4], vr[4];
-  auto load_tile = [&](int it) {
+  // staging job of this thread within its half: rows 4rq..4rq+3, dims 8cc..8cc+7
+  const bool has_job = htid < G_::NJOB;
+  const int rq = htid / JOB_C, cc = htid % JOB_C;
+  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+
+#define HGA_FWD_LOAD(IT)                                                         \
+  do {                                                                           \
+    const int tok_ = has_job ? src.token4((IT), 4 * rq) : -1;                    \
+    if (tok_ >= 0) {                                                             \
+      const __bf16* kp_ = kg + (size_t)tok_ * D + 8 * cc;                         \
+      const __bf16* vp_ = vg + (size_t)tok_ * D + 8 * cc;                         \
+      k0 = *reinterpret_cast<const uint4*>(kp_);                                 \
+      k1 = *reinterpret_cast<const uint4*>(kp_ + D);                             \
+      k2 = *reinterpret_cast<const uint4*>(kp_ + 2 * D);                         \
+      k3 = *reinterpret_cast<const uint4*>(kp_ + 3 * D);                         \
+      v0 = *reinterpret_cast<const uint4*>(vp_);                                 \
+      v1 = *reinterpret_cast<const uint4*>(vp_ + D);                             \
+      v2 = *reinterpret_cast<const uint4*>(vp_ + 2 * D);                         \
+      v3 = *reinterpret_cast<const uint4*>(vp_ + 3 * D);                         \
+    } else {                                                                     \
+      k0 = k1 = k2 = k3 = v0 = v1 = v2 = v3 = z4;                                \
+    }                                                                            \
+  } while (0)
+
+  auto store_stage = [&](__bf16* st) {
     if (!has_job) return;
-    const int tok = src.token4(it, 4 * rq);
-    if (tok < 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { kr[i] = make_uint4(0, 0, 0, 0); vr[i] = kr[i]; }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kr[i] = *reinterpret_cast<const uint4*>(kg + (size_t)(tok + i) * D + 8 * cc);
-      vr[i] = *reinterpret_cast<const uint4*>(vg + (size_t)(tok + i) * D + 8 * cc);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    if (!has_job) return;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(&s_k[buf][(4 * rq + i) * KSTR + 8 * cc]) = kr[i];
+    __bf16* ks = st;
+    __bf16* vt = st + G_::ROW_ELEMS;
+    *reinterpret_cast<uint4*>(&ks[(4 * rq + 0) * KSTR + 8 * cc]) = k0;
+    *reinterpret_cast<uint4*>(&ks[(4 * rq + 1) * KSTR + 8 * cc]) = k1;
+    *reinterpret_cast<uint4*>(&ks[(4 * rq + 2) * KSTR + 8 * cc]) = k2;
+    *reinterpret_cast<uint4*>(&ks[(4 * rq + 3) * KSTR + 8 * cc]) = k3;
     const int pos = tpos(4 * rq);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<uint2*>(&s_vt[buf][toff<TK>(8 * cc + e, pos)]) =
-          quad_column(vr[0], vr[1], vr[2], vr[3], e);
+      *reinterpret_cast<uint2*>(&vt[toff<TK>(8 * cc + e, pos)]) = quad_column(v0, v1, v2, v3, e);
   };
 
   floatx16 oacc[NDB];
@@ -143,20 +162,22 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  load_tile(0);
-  store_tile(0);
+  if (my_count > 0) HGA_FWD_LOAD(my_first);
+  if (my_count > 0) store_stage(s_tiles[half][0]);
+  drain_vmem_loads();
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < ntiles) load_tile(it + 1);
+  for (int i = 0; i < n0; ++i) {
+    const int it = my_first + i;
+    const bool mine = i < my_count;
+    if (i + 1 < my_count) HGA_FWD_LOAD(it + 1);
 
     const bool is_local = it >= src.n_hist_tiles;
     const int local_first = t0 + (it - src.n_hist_tiles) * TK;
-    const bool work = active && (!is_local || local_first <= wave_qmax);
+    const bool work = mine && active && (!is_local || local_first <= wave_qmax);
     if (work) {
-      const __bf16* kt = s_k[buf];
-      const __bf16* vt = s_vt[buf];
+      const __bf16* kt = s_tiles[half][i & 1];
+      const __bf16* vt = kt + G_::ROW_ELEMS;
       floatx16 sacc[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -166,24 +187,45 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
           sacc[st] = mfma32(lds_b128(kt + (32 * st + lq) * KSTR + 16 * kk + 8 * hi), qreg[kk],
                             sacc[st]);
       }
-      // scale + mask, tile max per query
-      const int hist_first = it * TK;
+      // scale; mask only on tiles that can hold invisible keys
+      const bool need_mask = is_local ? (local_first + TK - 1 > qfirst)
+                                      : ((it + 1) * TK > src.nh);
       float mt = -INFINITY;
+      if (need_mask) {
+        const int base = is_local ? local_first : it * TK;
+        const int lim = is_local ? tq : src.nh - 1;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+        for (int st = 0; st < 2; ++st) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kr_ = 32 * st + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool ok = is_local ? (local_first + kr_ <= tq) : (hist_first + kr_ < src.nh);
-          const float x = ok ? sacc[st][r] * a.c2 : -INFINITY;
-          sacc[st][r] = x;
-          mt = fmaxf(mt, x);
+          for (int r = 0; r < 16; ++r) {
+            const int kr_ = base + 32 * st + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const float x = (kr_ <= lim) ? sacc[st][r] * a.c2 : -INFINITY;
+            sacc[st][r] = x;
+            mt = fmaxf(mt, x);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float x = sacc[st][r] * a.c2;
+            sacc[st][r] = x;
+            mt = fmaxf(mt, x);
+          }
         }
       }
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
+      const bool raise = mt > m_run + kRescale;
+      if (__ballot(raise)) {
+        const float m_new = raise ? mt : m_run;
+        const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       float rs = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -194,11 +236,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
           rs += p;
         }
       }
-      rs += __shfl_xor(rs, 32, 64);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      l_run += rs;  // this lane's 32 keys; the partner lane's are added at the end
       // O^T += V^T . P^T
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -215,28 +253,51 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
         }
       }
     }
-
-    if (it + 1 < ntiles) store_tile(buf ^ 1);
+    if (i + 1 < my_count) store_stage(s_tiles[half][(i + 1) & 1]);
     __syncthreads();
   }
+#undef HGA_FWD_LOAD
 
-  if (active && row_ok) {
-    const float inv = 1.f / l_run;
+  // both lanes of a query kept partial row sums over their own keys
+  l_run += __shfl_xor(l_run, 32, 64);
+
+  // merge the two halves: half 1 parks (m, l, O^T) in LDS, half 0 combines
+  float* park = reinterpret_cast<float*>(&s_tiles[0][0][0]);
+  float* park_o = park + wr * (NDB * 16 * 64);
+  float* park_ml = park + 4 * (NDB * 16 * 64) + wr * 128;
+  if (half == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) park_o[(db * 16 + r) * 64 + lane] = oacc[db][r];
+    park_ml[lane] = m_run;
+    park_ml[64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (half == 0 && active && row_ok) {
+    const float m1 = park_ml[lane], l1 = park_ml[64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float f0 = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m);
+    const float f1 = (m1 == -INFINITY) ? 0.f : exp2f(m1 - m);
+    const float l = l_run * f0 + l1 * f1;
+    const float inv = 1.f / l;
+    const float g0 = f0 * inv, g1 = f1 * inv;
     __bf16* op = o + ((size_t)(b * a.Hq + h) * a.S + tq) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         bf16x4 pk;
-        pk[0] = (__bf16)(oacc[db][4 * r4 + 0] * inv);
-        pk[1] = (__bf16)(oacc[db][4 * r4 + 1] * inv);
-        pk[2] = (__bf16)(oacc[db][4 * r4 + 2] * inv);
-        pk[3] = (__bf16)(oacc[db][4 * r4 + 3] * inv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          pk[e] = (__bf16)(oacc[db][r] * g0 + park_o[(db * 16 + r) * 64 + lane] * g1);
+        }
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * r4 + 4 * hi) = pk;
       }
     }
     if (lse != nullptr && hi == 0)
-      lse[(size_t)(b * a.Hq + h) * a.S + tq] = (m_run + log2f(l_run)) * kLn2;
+      lse[(size_t)(b * a.Hq + h) * a.S + tq] = (m + log2f(l)) * kLn2;
   }
 }
 
@@ -342,7 +403,7 @@ hipError_t fwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
   FwdArgs a = make_args(p, seg);
   const int nblocks = p.B * p.Hkv * p.nqb * a.wpu;
   ProfScope ps(HGA_K_FWD, st);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(nblocks), dim3(256), 0, st,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, sel, (__bf16*)o,
                      lse, a);
   return hipGetLastError();

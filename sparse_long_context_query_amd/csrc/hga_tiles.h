@@ -118,6 +118,80 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ---- row-major LDS tiles filled by direct global->LDS loads --------------
+// A tile of bf16 rows of D elements is stored row-major without padding; the
+// 16-byte chunk c of row r sits at chunk position c ^ sw8(r), which puts
+// the 8 rows a group of lanes reads at once (and the 4 rows of a transposed
+// read) on distinct LDS banks.
+__device__ __forceinline__ int sw8(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int D>
+__device__ __forceinline__ int swz_byte(int r, int chunk) {
+  return r * (2 * D) + ((chunk ^ sw8(r)) << 4);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ lds_void* to_lds(void* p) {
+  return (lds_void*)(uintptr_t)(p);
+}
+
+// One wave copies `rows` (a multiple of 1024/(2D)) bf16 rows of D elements,
+// starting at global row pointer `g` (row stride D), into the swizzled
+// tile at `lds` (wave-uniform), 1 KB per instruction, lane l writing
+// bytes [16l, 16l+16) of each KB.  Rows at or beyond `valid` read row
+// valid-1 instead (callers mask them), so every global address stays in
+// bounds.  The data lands asynchronously: wait on vmcnt before reading.
+template <int D>
+__device__ __forceinline__ void dma_rows(const __bf16* g, int rows, int valid, unsigned char* lds,
+                                         int lane) {
+  constexpr int CPR = (2 * D) / 16;  // chunks per row
+  constexpr int RPI = 64 / CPR;      // rows per 1 KB instruction
+  for (int i = 0; i < rows / RPI; ++i) {
+    const int row = i * RPI + lane / CPR;
+    const int p = lane % CPR;
+    const int c = p ^ sw8(row);
+    const int rr = row < valid ? row : valid - 1;
+    __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)rr * D + c * 8),
+                                     to_lds(lds + i * 1024), 16, 0, 0);
+  }
+}
+
+// Transposed 32x16 A-operand fragment from a swizzled row-major tile: the
+// MFMA rows are the tile's columns d in [32*db, 32*db+32), the 16 k-values
+// are tile rows rbase + {4hi..4hi+3, 8+4hi..8+4hi+3} (the same 16-row
+// permutation the C-layout B operands use).  Two ds_read_b64_tr_b16: in each
+// group of 16 lanes, lane j receives element j%4 of the 8-byte pieces read
+// by lanes j/4, j/4+4, j/4+8, j/4+12; lane i points at tile row
+// rbase+4hi(+8)+i/4, columns 32db+16*(group&1)+4*(i%4) .. +3.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_fragment(const unsigned char* tile, int rbase, int db,
+                                              int lane) {
+  const int j = lane & 15, grp = lane >> 4, hi = lane >> 5;
+  const int d = 32 * db + 16 * (grp & 1) + 4 * (j & 3);
+  const int chunk = d >> 3, boff = (d & 7) * 2;
+  const int r0 = rbase + 4 * hi + (j >> 2);
+  const int r1 = r0 + 8;
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)to_lds((void*)(tile + swz_byte<D>(r0, chunk) + boff)));
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)to_lds((void*)(tile + swz_byte<D>(r1, chunk) + boff)));
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Row-major A/B-operand fragment: row r, elements 16kk+8hi .. +7.
+template <int D>
+__device__ __forceinline__ bf16x8 row_fragment(const unsigned char* tile, int r, int kk, int hi) {
+  return *reinterpret_cast<const bf16x8*>(tile + swz_byte<D>(r, 2 * kk + hi));
+}
+
+// Waits for every outstanding vector-memory load of this wave (vmcnt(0);
+// expcnt and lgkmcnt left at their maxima).  Used once before a pipelined
+// loop so that operands loaded ahead of it do not make the compiler wait
+// for in-flight prefetches inside the loop.
+__device__ __forceinline__ void drain_vmem_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Compacts the valid entries (0 <= e < nb) of one selection row into LDS.
 // Must be called by every thread of the block; returns the count.
 __device__ __forceinline__ int compact_selection(const int32_t* __restrict__ row, int K, int nb,
