@@ -65,13 +65,15 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o,
 // ---------------------------------------------------------------------------
 // a7, bf16 MFMA: dq.  Same work split as the forward: 512 threads = 8 waves,
 // up to 4 wave rows (32 queries of one head each) of one (b, g, j) unit per
-// block of threads; the key tiles (32 keys) are split in two halves walked
-// by waves 0-3 and 4-7, each half with its own double-buffered LDS stream
-// (K row-major, V row-major, K transposed).  Per wave and tile:
+// block of threads; the key tiles (64 keys) are split in two halves walked
+// by waves 0-3 and 4-7, each half double-buffering swizzled row-major K
+// and V tiles that are copied straight from memory into LDS.  Per wave and
+// 32-key sub-tile:
 //   S^T  = K . Q^T          (Q^T in registers as B operand)
 //   dP^T = V . dO^T         (dO^T in registers as B operand)
 //   dS^T = P^T * (dP^T - delta),  P^T = exp2(S^T c2 - lse2)
-//   dQ^T += K^T . dS^T      (dS^T straight from the accumulator)
+//   dQ^T += K^T . dS^T      (K^T read transposed from the K tile, dS^T
+//                            straight from the accumulator)
 // The two halves' partial dQ^T are added through LDS at the end.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -80,16 +82,14 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
     const __bf16* __restrict__ v, const float* __restrict__ lse,
     const __bf16* __restrict__ dO, const float* __restrict__ delta,
     const int32_t* __restrict__ sel, __bf16* __restrict__ dq, BwdArgs a) {
-  constexpr int TK = 32;
-  using G_ = TileGeom<D, TK>;
-  constexpr int KSTR = G_::KSTR;
+  constexpr int TK = 64;
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int JOB_C = D / 8;
-  constexpr int STAGE = 2 * G_::ROW_ELEMS + G_::T_ELEMS;  // K rows, V rows, K^T
-  static_assert(4 * STAGE * 2 >= 4 * NDB * 16 * 64 * 4, "merge buffer fits");
+  constexpr int TILE_B = TK * 2 * D;
+  constexpr int STAGE_B = 2 * TILE_B;  // K tile + V tile
+  static_assert(4 * STAGE_B >= 4 * NDB * 16 * 64 * 4, "merge buffer fits");
 
-  __shared__ __attribute__((aligned(16))) __bf16 s_tiles[2][2][STAGE];  // [half][buf]
+  __shared__ __attribute__((aligned(1024))) unsigned char s_tiles[2][2][STAGE_B];  // [half][buf]
   __shared__ int s_hlist[kMaxTopK];
   __shared__ int s_hcount;
 
@@ -105,7 +105,6 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
   const int half = wave >> 2, wr = wave & 3;
-  const int htid = tid & 255;
 
   const int nwr = a.G * a.nq32;
   const int idx = c * 4 + wr;
@@ -149,107 +148,69 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
   const float lse2 = row_ok ? lse[qrow] * kLog2e : 0.f;
   const float dlt = row_ok ? delta[(size_t)(b * a.Hq + h) * a.L + (tq - t0)] : 0.f;
 
-  const bool has_job = htid < G_::NJOB;
-  const int rq = htid / JOB_C, cc = htid % JOB_C;
-  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
-
-#define HGA_DQ_LOAD(IT)                                                          \
-  do {                                                                           \
-    const int tok_ = has_job ? src.token4((IT), 4 * rq) : -1;                    \
-    if (tok_ >= 0) {                                                             \
-      const __bf16* kp_ = kg + (size_t)tok_ * D + 8 * cc;                         \
-      const __bf16* vp_ = vg + (size_t)tok_ * D + 8 * cc;                         \
-      k0 = *reinterpret_cast<const uint4*>(kp_);                                 \
-      k1 = *reinterpret_cast<const uint4*>(kp_ + D);                             \
-      k2 = *reinterpret_cast<const uint4*>(kp_ + 2 * D);                         \
-      k3 = *reinterpret_cast<const uint4*>(kp_ + 3 * D);                         \
-      v0 = *reinterpret_cast<const uint4*>(vp_);                                 \
-      v1 = *reinterpret_cast<const uint4*>(vp_ + D);                             \
-      v2 = *reinterpret_cast<const uint4*>(vp_ + 2 * D);                         \
-      v3 = *reinterpret_cast<const uint4*>(vp_ + 3 * D);                         \
-    } else {                                                                     \
-      k0 = k1 = k2 = k3 = v0 = v1 = v2 = v3 = z4;                                \
-    }                                                                            \
-  } while (0)
-
-  auto store_stage = [&](__bf16* st) {
-    if (!has_job) return;
-    __bf16* ks = st;
-    __bf16* vs = st + G_::ROW_ELEMS;
-    __bf16* kts = st + 2 * G_::ROW_ELEMS;
-    *reinterpret_cast<uint4*>(&ks[(4 * rq + 0) * KSTR + 8 * cc]) = k0;
-    *reinterpret_cast<uint4*>(&ks[(4 * rq + 1) * KSTR + 8 * cc]) = k1;
-    *reinterpret_cast<uint4*>(&ks[(4 * rq + 2) * KSTR + 8 * cc]) = k2;
-    *reinterpret_cast<uint4*>(&ks[(4 * rq + 3) * KSTR + 8 * cc]) = k3;
-    *reinterpret_cast<uint4*>(&vs[(4 * rq + 0) * KSTR + 8 * cc]) = v0;
-    *reinterpret_cast<uint4*>(&vs[(4 * rq + 1) * KSTR + 8 * cc]) = v1;
-    *reinterpret_cast<uint4*>(&vs[(4 * rq + 2) * KSTR + 8 * cc]) = v2;
-    *reinterpret_cast<uint4*>(&vs[(4 * rq + 3) * KSTR + 8 * cc]) = v3;
-    const int pos = tpos(4 * rq);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<uint2*>(&kts[toff<TK>(8 * cc + e, pos)]) = quad_column(k0, k1, k2, k3, e);
-  };
-
   floatx16 dqacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqacc[db] = floatx16{};
+  FragOffsets<D> fo;
+  fo.init(lane);
 
-  if (my_count > 0) HGA_DQ_LOAD(my_first);
-  if (my_count > 0) store_stage(s_tiles[half][0]);
+  if (my_count > 0)
+    dma_kv_tile<D, TK>(src, my_first, kg, vg, s_tiles[half][0], s_tiles[half][0] + TILE_B, wr,
+                       lane);
   drain_vmem_loads();
   __syncthreads();
 
   for (int i = 0; i < n0; ++i) {
     const int it = my_first + i;
     const bool mine = i < my_count;
-    if (i + 1 < my_count) HGA_DQ_LOAD(it + 1);
+    if (i + 1 < my_count)
+      dma_kv_tile<D, TK>(src, it + 1, kg, vg, s_tiles[half][(i + 1) & 1],
+                         s_tiles[half][(i + 1) & 1] + TILE_B, wr, lane);
     const bool is_local = it >= src.n_hist_tiles;
     const int local_first = t0 + (it - src.n_hist_tiles) * TK;
     const bool work = mine && active && (!is_local || local_first <= wave_qmax);
     if (work) {
-      const __bf16* kt = s_tiles[half][i & 1];
-      const __bf16* vt = kt + G_::ROW_ELEMS;
-      const __bf16* ktt = kt + 2 * G_::ROW_ELEMS;
-      floatx16 sacc = floatx16{}, pacc = floatx16{};
+      const unsigned char* kt = s_tiles[half][i & 1];
+      const unsigned char* vt = kt + TILE_B;
+      const int base = is_local ? local_first : it * TK;
+      const int lim = is_local ? tq : src.nh - 1;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        sacc = mfma32(lds_b128(kt + lq * KSTR + 16 * kk + 8 * hi), qreg[kk], sacc);
-        pacc = mfma32(lds_b128(vt + lq * KSTR + 16 * kk + 8 * hi), doreg[kk], pacc);
-      }
-      const bool need_mask = is_local ? (local_first + TK - 1 > qfirst) : ((it + 1) * TK > src.nh);
-      if (need_mask) {
-        const int base = is_local ? local_first : it * TK;
-        const int lim = is_local ? tq : src.nh - 1;
+      for (int st = 0; st < 2; ++st) {
+        if (is_local && local_first + 32 * st > wave_qmax) break;  // sub-tile fully masked
+        floatx16 sacc = floatx16{}, pacc = floatx16{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          sacc = mfma32(fo.row(kt, st, kk), qreg[kk], sacc);
+          pacc = mfma32(fo.row(vt, st, kk), doreg[kk], pacc);
+        }
+        const bool need_mask = is_local ? (local_first + 32 * st + 31 > qfirst)
+                                        : ((it * TK + 32 * st + 32) > src.nh);
+        if (need_mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kr_ = base + 32 * st + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (kr_ > lim) sacc[r] = -INFINITY;
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kr_ = base + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const float p = (kr_ <= lim) ? exp2f(sacc[r] * a.c2 - lse2) : 0.f;
+          const float p = fast_exp2(fmaf(sacc[r], a.c2, -lse2));
           sacc[r] = p * (pacc[r] - dlt);
         }
-      } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(sacc[r] * a.c2 - lse2);
-          sacc[r] = p * (pacc[r] - dlt);
+        for (int ks = 0; ks < 2; ++ks) {
+          const int r0 = 8 * ks;
+          const bf16x8 sb = to_bf16x8(sacc[r0], sacc[r0 + 1], sacc[r0 + 2], sacc[r0 + 3],
+                                      sacc[r0 + 4], sacc[r0 + 5], sacc[r0 + 6], sacc[r0 + 7]);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            dqacc[db] = mfma32(fo.tr(kt, 32 * st + 16 * ks, db), sb, dqacc[db]);
         }
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int r0 = 8 * ks;
-        const bf16x8 sb = to_bf16x8(sacc[r0], sacc[r0 + 1], sacc[r0 + 2], sacc[r0 + 3],
-                                    sacc[r0 + 4], sacc[r0 + 5], sacc[r0 + 6], sacc[r0 + 7]);
-        const int pos = 16 * ks + 8 * hi;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          dqacc[db] = mfma32(lds_b128(ktt + toff<TK>(32 * db + lq, pos)), sb, dqacc[db]);
       }
     }
-    if (i + 1 < my_count) store_stage(s_tiles[half][(i + 1) & 1]);
+    drain_vmem_loads();
     __syncthreads();
   }
-#undef HGA_DQ_LOAD
 
   // add the two halves' partial dQ^T through LDS, scale, round, store
   float* park = reinterpret_cast<float*>(&s_tiles[0][0][0]) + wr * (NDB * 16 * 64);
@@ -341,6 +302,8 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   floatx16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) { dkacc[db] = floatx16{}; dvacc[db] = floatx16{}; }
+  FragOffsets<D> fo;
+  fo.init(lane);
 
   const int nqt = (a.L + TQ - 1) / TQ;
   const int npairs = (nqt - kt) * a.G;
@@ -365,8 +328,8 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     floatx16 sacc = floatx16{}, pacc = floatx16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      sacc = mfma32(row_fragment<D>(s_q, lq, kk, hi), row_fragment<D>(s_k, lq, kk, hi), sacc);
-      pacc = mfma32(row_fragment<D>(s_do, lq, kk, hi), row_fragment<D>(s_v, lq, kk, hi), pacc);
+      sacc = mfma32(fo.row(s_q, 0, kk), fo.row(s_k, 0, kk), sacc);
+      pacc = mfma32(fo.row(s_do, 0, kk), fo.row(s_v, 0, kk), pacc);
     }
     // C layout: lane = key lq, item r = query row 8(r/4)+4hi+(r%4) of the tile
     const bool need_mask = (tq0 < kfirst + 31) || (nvalid < TQ) || (kfirst + 32 > tend);
@@ -380,7 +343,7 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * r4 + e;
-        float p = exp2f(sacc[r] * a.c2 - lv[e] * kLog2e);
+        float p = fast_exp2(fmaf(sacc[r], a.c2, -lv[e] * kLog2e));
         if (need_mask) {
           const int tqr = tq0 + 8 * r4 + 4 * hi + e;
           p = (key_ok && tk <= tqr && tqr < tend) ? p : 0.f;
@@ -398,8 +361,8 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
                                   sacc[r0 + 4], sacc[r0 + 5], sacc[r0 + 6], sacc[r0 + 7]);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        dvacc[db] = mfma32(tr_fragment<D>(s_do, 16 * ks, db, lane), pb, dvacc[db]);
-        dkacc[db] = mfma32(tr_fragment<D>(s_q, 16 * ks, db, lane), sb, dkacc[db]);
+        dvacc[db] = mfma32(fo.tr(s_do, 16 * ks, db), pb, dvacc[db]);
+        dkacc[db] = mfma32(fo.tr(s_q, 16 * ks, db), sb, dkacc[db]);
       }
     }
     wave_lds_sync();  // this slice's reads are done before the next pair's loads land

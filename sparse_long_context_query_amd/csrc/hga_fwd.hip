@@ -33,16 +33,17 @@ struct FwdArgs {
 // head: query sub-block qs, head hh of the group), so all its waves share
 // one key set.  The key tiles (64 keys; history tiles first, then local
 // tiles) are split in two halves: waves 0-3 walk the first half and waves
-// 4-7 the second, each half with its own double-buffered LDS stream (K
-// row-major, V transposed; the next tile's global loads held in registers
-// while the current one is computed).  Two waves per SIMD let one wave's
-// softmax overlap the other's MFMAs.  The halves' partial (O, m, l) are
-// merged through LDS at the end (log-sum-exp rule).
-// Per wave and tile: S^T = K.Q^T (Q^T in registers as B operand), online
-// softmax per query, O^T += V^T.P^T with P^T taken from the accumulator.
-// The running max is only raised when a tile max exceeds it by more than
-// kRescale (log2 units), so O is rarely rescaled; exp2 arguments stay below
-// kRescale and the final normalisation is exact either way.
+// 4-7 the second, two waves per SIMD so that one wave's softmax overlaps
+// the other's MFMAs.  Each half double-buffers its tiles in LDS; the next
+// tile's K and V rows are copied straight from memory into swizzled
+// row-major LDS tiles while the current tile is computed.  Per wave and
+// tile: S^T = K.Q^T (Q^T held in registers as B operand), online softmax
+// per query, O^T += V^T.P^T with V^T read transposed from the V tile and P^T
+// taken from the accumulator.  The running max is only raised when a tile
+// max exceeds it by more than kRescale (log2 units), so O is rarely
+// rescaled; exp2 arguments stay below kRescale and the final normalisation
+// is exact either way.  The halves' partial (O, m, l) are merged through
+// LDS at the end (log-sum-exp rule).
 // ---------------------------------------------------------------------------
 constexpr float kRescale = 8.f;
 
@@ -52,15 +53,13 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
     const __bf16* __restrict__ v, const int32_t* __restrict__ sel,
     __bf16* __restrict__ o, float* __restrict__ lse, FwdArgs a) {
   constexpr int TK = 64;
-  using G_ = TileGeom<D, TK>;
-  constexpr int KSTR = G_::KSTR;
   constexpr int NKK = D / 16;  // MFMA k-steps over the head dim
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
-  constexpr int JOB_C = D / 8;
-  constexpr int STAGE = G_::ROW_ELEMS + G_::T_ELEMS;  // one tile (K rows + V^T)
-  static_assert(4 * STAGE * 2 >= 4 * (NDB * 16 * 64 + 2 * 64) * 4, "merge buffer fits");
+  constexpr int TILE_B = TK * 2 * D;
+  constexpr int STAGE_B = 2 * TILE_B;  // K tile + V tile
+  static_assert(4 * STAGE_B >= 4 * (NDB * 16 * 64 + 2 * 64) * 4, "merge buffer fits");
 
-  __shared__ __attribute__((aligned(16))) __bf16 s_tiles[2][2][STAGE];  // [half][buf]
+  __shared__ __attribute__((aligned(1024))) unsigned char s_tiles[2][2][STAGE_B];  // [half][buf]
   __shared__ int s_hlist[kMaxTopK];
   __shared__ int s_hcount;
 
@@ -76,7 +75,6 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
   const int half = wave >> 2, wr = wave & 3;
-  const int htid = tid & 255;  // thread index within the half
 
   const int nwr = a.G * a.nq32;
   const int idx = c * 4 + wr;
@@ -118,108 +116,66 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
       qreg[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * kk) : bf16x8{};
   }
 
-  // staging job of this thread within its half: rows 4rq..4rq+3, dims 8cc..8cc+7
-  const bool has_job = htid < G_::NJOB;
-  const int rq = htid / JOB_C, cc = htid % JOB_C;
-  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
-
-#define HGA_FWD_LOAD(IT)                                                         \
-  do {                                                                           \
-    const int tok_ = has_job ? src.token4((IT), 4 * rq) : -1;                    \
-    if (tok_ >= 0) {                                                             \
-      const __bf16* kp_ = kg + (size_t)tok_ * D + 8 * cc;                         \
-      const __bf16* vp_ = vg + (size_t)tok_ * D + 8 * cc;                         \
-      k0 = *reinterpret_cast<const uint4*>(kp_);                                 \
-      k1 = *reinterpret_cast<const uint4*>(kp_ + D);                             \
-      k2 = *reinterpret_cast<const uint4*>(kp_ + 2 * D);                         \
-      k3 = *reinterpret_cast<const uint4*>(kp_ + 3 * D);                         \
-      v0 = *reinterpret_cast<const uint4*>(vp_);                                 \
-      v1 = *reinterpret_cast<const uint4*>(vp_ + D);                             \
-      v2 = *reinterpret_cast<const uint4*>(vp_ + 2 * D);                         \
-      v3 = *reinterpret_cast<const uint4*>(vp_ + 3 * D);                         \
-    } else {                                                                     \
-      k0 = k1 = k2 = k3 = v0 = v1 = v2 = v3 = z4;                                \
-    }                                                                            \
-  } while (0)
-
-  auto store_stage = [&](__bf16* st) {
-    if (!has_job) return;
-    __bf16* ks = st;
-    __bf16* vt = st + G_::ROW_ELEMS;
-    *reinterpret_cast<uint4*>(&ks[(4 * rq + 0) * KSTR + 8 * cc]) = k0;
-    *reinterpret_cast<uint4*>(&ks[(4 * rq + 1) * KSTR + 8 * cc]) = k1;
-    *reinterpret_cast<uint4*>(&ks[(4 * rq + 2) * KSTR + 8 * cc]) = k2;
-    *reinterpret_cast<uint4*>(&ks[(4 * rq + 3) * KSTR + 8 * cc]) = k3;
-    const int pos = tpos(4 * rq);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<uint2*>(&vt[toff<TK>(8 * cc + e, pos)]) = quad_column(v0, v1, v2, v3, e);
-  };
-
   floatx16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
   float m_run = -INFINITY, l_run = 0.f;
+  FragOffsets<D> fo;
+  fo.init(lane);
 
-  if (my_count > 0) HGA_FWD_LOAD(my_first);
-  if (my_count > 0) store_stage(s_tiles[half][0]);
+  if (my_count > 0)
+    dma_kv_tile<D, TK>(src, my_first, kg, vg, s_tiles[half][0], s_tiles[half][0] + TILE_B, wr,
+                       lane);
   drain_vmem_loads();
   __syncthreads();
 
   for (int i = 0; i < n0; ++i) {
     const int it = my_first + i;
     const bool mine = i < my_count;
-    if (i + 1 < my_count) HGA_FWD_LOAD(it + 1);
+    if (i + 1 < my_count)
+      dma_kv_tile<D, TK>(src, it + 1, kg, vg, s_tiles[half][(i + 1) & 1],
+                         s_tiles[half][(i + 1) & 1] + TILE_B, wr, lane);
 
     const bool is_local = it >= src.n_hist_tiles;
     const int local_first = t0 + (it - src.n_hist_tiles) * TK;
     const bool work = mine && active && (!is_local || local_first <= wave_qmax);
     if (work) {
-      const __bf16* kt = s_tiles[half][i & 1];
-      const __bf16* vt = kt + G_::ROW_ELEMS;
+      const unsigned char* kt = s_tiles[half][i & 1];
+      const unsigned char* vt = kt + TILE_B;
       floatx16 sacc[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        sacc[st] = floatx16{};
+      for (int st = 0; st < 2; ++st) sacc[st] = floatx16{};
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          sacc[st] = mfma32(lds_b128(kt + (32 * st + lq) * KSTR + 16 * kk + 8 * hi), qreg[kk],
-                            sacc[st]);
+      for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+          sacc[st] = mfma32(fo.row(kt, st, kk), qreg[kk], sacc[st]);
       }
-      // scale; mask only on tiles that can hold invisible keys
+      // tile max of the raw scores; mask only on tiles that can hold
+      // invisible keys
       const bool need_mask = is_local ? (local_first + TK - 1 > qfirst)
                                       : ((it + 1) * TK > src.nh);
-      float mt = -INFINITY;
       if (need_mask) {
         const int base = is_local ? local_first : it * TK;
         const int lim = is_local ? tq : src.nh - 1;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kr_ = base + 32 * st + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const float x = (kr_ <= lim) ? sacc[st][r] * a.c2 : -INFINITY;
-            sacc[st][r] = x;
-            mt = fmaxf(mt, x);
+            if (kr_ > lim) sacc[st][r] = -INFINITY;
           }
-        }
-      } else {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float x = sacc[st][r] * a.c2;
-            sacc[st][r] = x;
-            mt = fmaxf(mt, x);
-          }
-        }
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      float mt = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[st][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * a.c2;
       const bool raise = mt > m_run + kRescale;
       if (__ballot(raise)) {
         const float m_new = raise ? mt : m_run;
-        const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
@@ -231,7 +187,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(sacc[st][r] - m_use);
+          const float p = fast_exp2(fmaf(sacc[st][r], a.c2, -m_use));
           sacc[st][r] = p;
           rs += p;
         }
@@ -246,17 +202,15 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
           const bf16x8 pb = to_bf16x8(sacc[st][r0], sacc[st][r0 + 1], sacc[st][r0 + 2],
                                       sacc[st][r0 + 3], sacc[st][r0 + 4], sacc[st][r0 + 5],
                                       sacc[st][r0 + 6], sacc[st][r0 + 7]);
-          const int pos = 32 * st + 16 * ks + 8 * hi;
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
-            oacc[db] = mfma32(lds_b128(vt + toff<TK>(32 * db + lq, pos)), pb, oacc[db]);
+            oacc[db] = mfma32(fo.tr(vt, 32 * st + 16 * ks, db), pb, oacc[db]);
         }
       }
     }
-    if (i + 1 < my_count) store_stage(s_tiles[half][(i + 1) & 1]);
+    drain_vmem_loads();  // the next tile has landed in LDS
     __syncthreads();
   }
-#undef HGA_FWD_LOAD
 
   // both lanes of a query kept partial row sums over their own keys
   l_run += __shfl_xor(l_run, 32, 64);

@@ -97,18 +97,18 @@ struct KeySource {
     n_hist_tiles = (nh + TK - 1) / TK;
   }
 
-  // first token of the 4-row group starting at tile row r4 of tile `it`,
-  // or -1 if those rows hold no key.
-  __device__ __forceinline__ int token4(int it, int r4) const {
+  // token of row r of tile `it`; rows that hold no key map to the segment's
+  // first token (a valid row whose scores the kernels mask).
+  __device__ __forceinline__ int token_row(int it, int r) const {
     if (it < n_hist_tiles) {
-      const int gs = it * TK + r4;
-      if (gs >= nh) return -1;
-      return hlist[gs / Bh] * Bh + gs % Bh;
+      const int gs = it * TK + r;
+      return gs < nh ? hlist[gs / Bh] * Bh + gs % Bh : t0;
     }
-    const int t = t0 + (it - n_hist_tiles) * TK + r4;
-    return t < tend ? t : -1;
+    const int t = t0 + (it - n_hist_tiles) * TK + r;
+    return t < tend ? t : t0;
   }
 };
+
 
 // Orders LDS traffic of one wave: its earlier LDS stores are visible to its
 // later LDS loads from any lane (no other wave involved).
@@ -185,6 +185,68 @@ template <int D>
 __device__ __forceinline__ bf16x8 row_fragment(const unsigned char* tile, int r, int kk, int hi) {
   return *reinterpret_cast<const bf16x8*>(tile + swz_byte<D>(r, 2 * kk + hi));
 }
+
+// The 4 waves of one half of a block of threads copy the K and V rows of
+// key tile `it` straight into swizzled row-major LDS tiles (one 1 KB
+// direct load per wave and instruction, every lane supplying its own row).
+template <int D, int TK>
+__device__ __forceinline__ void dma_kv_tile(const KeySource<TK>& src, int it, const __bf16* kg,
+                                            const __bf16* vg, unsigned char* kdst,
+                                            unsigned char* vdst, int wr, int lane) {
+  constexpr int CPR = (2 * D) / 16;
+  constexpr int RPI = 64 / CPR;
+  constexpr int NI = TK / RPI;
+  static_assert(NI % 4 == 0, "instructions per wave");
+#pragma unroll
+  for (int n = 0; n < NI / 4; ++n) {
+    const int i = wr + 4 * n;
+    const int row = i * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ sw8(row);
+    const size_t off = (size_t)src.token_row(it, row) * D + c * 8;
+    __builtin_amdgcn_global_load_lds((const void*)(kg + off), to_lds(kdst + i * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(vg + off), to_lds(vdst + i * 1024), 16, 0, 0);
+  }
+}
+
+// Lane-constant byte offsets of the MFMA fragments inside a swizzled
+// row-major tile of D-element bf16 rows, hoisted out of the tile loops.
+// Moving by a multiple of 8 rows keeps sw8() and only adds rows*2D bytes;
+// chunks c and c+8 of a row differ by 128 bytes after the swizzle.  So:
+//   row fragment (row lq + 32*st, chunk 2kk+hi):
+//       rowf[kk & 3] + (kk >> 2) * 128 + st * 32 * 2D
+//   transposed fragment (tile rows rbase + 4hi.. (+8), columns of block db):
+//       first read  trf[db & 1] + (db >> 1) * 128 + rbase * 2D
+//       second read the same + 8 * 2D
+template <int D>
+struct FragOffsets {
+  int rowf[4];
+  int trf[2];
+  __device__ __forceinline__ void init(int lane) {
+    const int lq = lane & 31, hi = lane >> 5, j = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) rowf[kk] = swz_byte<D>(lq, 2 * kk + hi);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int d = 32 * db + 16 * (grp & 1) + 4 * (j & 3);
+      trf[db] = swz_byte<D>(4 * hi + (j >> 2), d >> 3) + (d & 7) * 2;
+    }
+  }
+  __device__ __forceinline__ bf16x8 row(const unsigned char* tile, int st, int kk) const {
+    return *reinterpret_cast<const bf16x8*>(tile + rowf[kk & 3] + (kk >> 2) * 128 +
+                                            st * 32 * 2 * D);
+  }
+  __device__ __forceinline__ bf16x8 tr(const unsigned char* tile, int rbase, int db) const {
+    const unsigned char* p = tile + trf[db & 1] + (db >> 1) * 128 + rbase * 2 * D;
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)to_lds((void*)p));
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)to_lds((void*)(p + 8 * 2 * D)));
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+};
+
+// exp2 straight on v_exp_f32 (no denormal range fix-up: results below the
+// normal range flush to zero, which the softmax never needs)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Waits for every outstanding vector-memory load of this wave (vmcnt(0);
 // expcnt and lgkmcnt left at their maxima).  Used once before a pipelined
