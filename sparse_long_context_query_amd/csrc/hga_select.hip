@@ -86,45 +86,52 @@ __device__ void bitonic_desc(unsigned long long* a, int n) {
   }
 }
 
-// In-LDS bitonic sort of n (power of two) ints, ascending.
-__device__ void bitonic_asc(int* a, int n) {
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n; i += kThreads) {
-        int ixj = i ^ j;
-        if (ixj > i) {
-          int x = a[i], y = a[ixj];
-          bool asc = (i & k) == 0;
-          if (asc ? (x > y) : (x < y)) { a[i] = y; a[ixj] = x; }
-        }
-      }
-      __syncthreads();
-    }
+// The k-th largest of the 64*E distinct keys held by one wave (E per lane,
+// unused slots 0): the largest T with #{keys >= T} >= k, found bit by bit
+// from the top.  Every step is one wave-uniform candidate, E compares, E
+// ballots and scalar popcounts; no shuffles, no LDS.
+template <int E>
+__device__ __forceinline__ unsigned long long wave_kth_largest(const unsigned long long (&v)[E],
+                                                               int k) {
+  unsigned long long t = 0;
+  for (int bit = 63; bit >= 0; --bit) {
+    const unsigned long long cand = t | (1ull << bit);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) c += __popcll(__ballot(v[e] >= cand));
+    if (c >= k) t = cand;
   }
+  return t;
 }
 
 // ---------------------------------------------------------------------------
 // a2 + a3: one block of threads per (query block j, KV head g, sequence b).
 //   1. qbar = mean of q over the G heads of the group and the Bq tokens of
-//      the block (float32, LDS fold as in summarize_kernel);
-//   2. scores against the nb resident summaries: 16 lanes per candidate,
-//      each holding D/16 dims, folded with a 16-lane shuffle reduction;
-//   3. bitonic sort of the orderable keys in LDS, keep the first k;
-//   4. bitonic sort of those k indices ascending, pad with -1, store.
+//      the block (float32; every row load of a thread in flight at once,
+//      then an LDS fold);
+//   2. score_i = qbar . summ_i (unscaled), one candidate per thread, qbar
+//      broadcast from LDS; the score and index form one orderable 64-bit key;
+//   3. the k-th largest key T: for up to 1024 candidates one wave finds it
+//      by a bitwise search over the keys held in its registers, beyond that
+//      an LDS bitonic sort over all threads;
+//   4. the candidates with key >= T, i.e. exactly the k best by (score desc,
+//      index asc), are compacted in index order (ballots), so the output is
+//      ascending; padded with -1.
+// E = keys per lane of the register search (0 selects the LDS sort).
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, int E>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const T* __restrict__ q, const float* __restrict__ summ,
     int32_t* __restrict__ sel, int S, int L, int Bq, int Bh, int K, int Hq,
     int Hkv, int G, int nqb_all, int nblk, int seg) {
-  constexpr int E = Vec16<T>::N;
-  constexpr int C = D / E;
+  constexpr int EL = Vec16<T>::N;
+  constexpr int C = D / EL;
   constexpr int R = kThreads / C;
-  constexpr int DL = D / 16;
-  extern __shared__ unsigned long long keys[];
+  extern __shared__ unsigned long long keys[];  // LDS sort only
   __shared__ float part[R][D + 1];
-  __shared__ float qbar[D];
-  __shared__ int top[kMaxTopK];
+  __shared__ __attribute__((aligned(16))) float qbar[D];
+  __shared__ float s_score[kMaxCandidates];
+  __shared__ unsigned long long s_thresh;
 
   const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int t0 = seg * L;
@@ -140,70 +147,103 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   // 1. query-block mean over (head in group, token in block)
   {
     const int c = threadIdx.x % C, r = threadIdx.x / C;
-    float acc[E];
+    float acc[EL];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int e = 0; e < EL; ++e) acc[e] = 0.f;
     const int rows = G * Bq;
-    for (int row = r; row < rows; row += R) {
-      const int hh = row / Bq, tt = row % Bq;
-      const T* p = q + ((size_t)(b * Hq + g * G + hh) * S + t0 + j * Bq + tt) * D + c * E;
-      float f[E];
-      Vec16<T>::load(p, f);
+    constexpr int U = 16;  // row loads in flight per thread
+    for (int row0 = r; row0 < rows; row0 += U * R) {
+      float f[U][EL];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += f[e];
+      for (int u = 0; u < U; ++u) {
+        const int row = row0 + u * R;
+        if (row < rows) {
+          const int hh = row / Bq, tt = row % Bq;
+          Vec16<T>::load(q + ((size_t)(b * Hq + g * G + hh) * S + t0 + j * Bq + tt) * D + c * EL,
+                         f[u]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EL; ++e) f[u][e] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < EL; ++e) acc[e] += f[u][e];
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) part[r][c * E + e] = acc[e];
+    for (int e = 0; e < EL; ++e) part[r][c * EL + e] = acc[e];
     __syncthreads();
     const float inv = 1.0f / (float)rows;
     for (int d = threadIdx.x; d < D; d += kThreads) {
-      float s = 0.f;
+      float sum = 0.f;
 #pragma unroll
-      for (int rr = 0; rr < R; ++rr) s += part[rr][d];
-      qbar[d] = s * inv;
+      for (int rr = 0; rr < R; ++rr) sum += part[rr][d];
+      qbar[d] = sum * inv;
     }
     __syncthreads();
   }
 
-  // 2. scores (unscaled dot products) -> orderable keys
-  int W = 1;
-  while (W < nb) W <<= 1;
-  {
-    const int grp = threadIdx.x / 16, ln = threadIdx.x % 16;
-    float qv[DL];
+  // 2. scores, one candidate per thread
+  const float* sbase = summ + (size_t)(b * Hkv + g) * nblk * D;
+  for (int i = threadIdx.x; i < nb; i += kThreads) {
+    const float4* rowp = reinterpret_cast<const float4*>(sbase + (size_t)i * D);
+    float sc = 0.f;
+    constexpr int NV = D / 4;
+    constexpr int UV = 16;
 #pragma unroll
-    for (int e = 0; e < DL; ++e) qv[e] = qbar[ln * DL + e];
-    const float* srow = summ + (size_t)(b * Hkv + g) * nblk * D + ln * DL;
-    for (int i = grp; i < W; i += kThreads / 16) {
-      float s = 0.f;
-      if (i < nb) {
-        const float* p = srow + (size_t)i * D;
+    for (int v0 = 0; v0 < NV; v0 += UV) {
+      float4 x[UV];
 #pragma unroll
-        for (int e = 0; e < DL; e += 4) {
-          float4 x = *reinterpret_cast<const float4*>(p + e);
-          s += qv[e] * x.x + qv[e + 1] * x.y + qv[e + 2] * x.z + qv[e + 3] * x.w;
-        }
+      for (int u = 0; u < UV; ++u) x[u] = rowp[v0 + u];
+#pragma unroll
+      for (int u = 0; u < UV; ++u) {
+        const float4 qv = *reinterpret_cast<const float4*>(&qbar[4 * (v0 + u)]);
+        sc += qv.x * x[u].x + qv.y * x[u].y + qv.z * x[u].z + qv.w * x[u].w;
       }
-      s += __shfl_xor(s, 8, 16);
-      s += __shfl_xor(s, 4, 16);
-      s += __shfl_xor(s, 2, 16);
-      s += __shfl_xor(s, 1, 16);
-      if (ln == 0) keys[i] = (i < nb) ? rank_key(s, i) : 0ull;
     }
+    s_score[i] = sc;
   }
   __syncthreads();
 
-  // 3. rank all candidates
-  bitonic_desc(keys, W);
-
-  // 4. the k best, ascending by index
-  int KP = 1;
-  while (KP < K) KP <<= 1;
-  for (int t = threadIdx.x; t < KP; t += kThreads)
-    top[t] = (t < K) ? (int)(0xffffffffu - (uint32_t)(keys[t] & 0xffffffffull)) : 0x7fffffff;
+  // 3. the k-th largest key
+  if constexpr (E > 0) {
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      unsigned long long v[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = 64 * e + lane;
+        v[e] = i < nb ? rank_key(s_score[i], i) : 0ull;
+      }
+      const unsigned long long thr = wave_kth_largest<E>(v, K);
+      if (lane == 0) s_thresh = thr;
+    }
+  } else {
+    int W = 1;
+    while (W < nb) W <<= 1;
+    for (int i = threadIdx.x; i < W; i += kThreads)
+      keys[i] = i < nb ? rank_key(s_score[i], i) : 0ull;
+    __syncthreads();
+    bitonic_desc(keys, W);
+    if (threadIdx.x == 0) s_thresh = keys[K - 1];
+  }
   __syncthreads();
-  bitonic_asc(top, KP);
-  for (int t = threadIdx.x; t < K; t += kThreads) out[t] = top[t];
+
+  // 4. the k best in index order
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const unsigned long long thr = s_thresh;
+    int count = 0;
+    for (int base = 0; base < nb; base += 64) {
+      const int i = base + lane;
+      const bool take = i < nb && rank_key(s_score[i], i) >= thr;
+      const unsigned long long m = __ballot(take);
+      const int pos = count + __popcll(m & ((1ull << lane) - 1ull));
+      if (take && pos < K) out[pos] = i;  // keys are unique: exactly K are taken
+      count += __popcll(m);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -254,25 +294,36 @@ hipError_t summarize_t(const Prob& p, const void* k, int b0, int b1, float* summ
   return hipGetLastError();
 }
 
-template <typename T, int D>
-hipError_t select_t(const Prob& p, const void* q, const float* summ, int seg,
-                    int32_t* sel, hipStream_t st) {
-  const int nb = seg * p.L / p.Bh;
-  int W = 1;
-  while (W < nb) W <<= 1;
-  size_t shm = (nb > p.K) ? (size_t)W * sizeof(unsigned long long) : 0;
+template <typename T, int D, int E>
+hipError_t select_launch(const Prob& p, const void* q, const float* summ, int seg, int32_t* sel,
+                         size_t shm, hipStream_t st) {
   if (shm > 32768) {  // large candidate sets need more than the default LDS cap
-    hipError_t e = hipFuncSetAttribute((const void*)select_kernel<T, D>,
+    hipError_t e = hipFuncSetAttribute((const void*)select_kernel<T, D, E>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)(kMaxCandidates * sizeof(unsigned long long)));
     if (e != hipSuccess) return e;
   }
   dim3 grid(p.nqb, p.Hkv, p.B);
   ProfScope ps(HGA_K_SELECT, st);
-  hipLaunchKernelGGL((select_kernel<T, D>), grid, dim3(kThreads), shm, st, (const T*)q,
-                     summ, sel, p.S, p.L, p.Bq, p.Bh, p.K, p.Hq, p.Hkv, p.G, p.nqb_all,
-                     p.nblk, seg);
+  hipLaunchKernelGGL((select_kernel<T, D, E>), grid, dim3(kThreads), shm, st, (const T*)q, summ,
+                     sel, p.S, p.L, p.Bq, p.Bh, p.K, p.Hq, p.Hkv, p.G, p.nqb_all, p.nblk, seg);
   return hipGetLastError();
+}
+
+// Register search for up to 1024 candidates (E = 1..16 keys per lane), LDS
+// sort beyond.
+template <typename T, int D>
+hipError_t select_t(const Prob& p, const void* q, const float* summ, int seg, int32_t* sel,
+                    hipStream_t st) {
+  const int nb = seg * p.L / p.Bh;
+  int W = 64;
+  while (W < nb) W <<= 1;
+  if (nb <= p.K || W <= 64) return select_launch<T, D, 1>(p, q, summ, seg, sel, 0, st);
+  if (W <= 128) return select_launch<T, D, 2>(p, q, summ, seg, sel, 0, st);
+  if (W <= 256) return select_launch<T, D, 4>(p, q, summ, seg, sel, 0, st);
+  if (W <= 512) return select_launch<T, D, 8>(p, q, summ, seg, sel, 0, st);
+  if (W <= 1024) return select_launch<T, D, 16>(p, q, summ, seg, sel, 0, st);
+  return select_launch<T, D, 0>(p, q, summ, seg, sel, (size_t)W * sizeof(unsigned long long), st);
 }
 
 }  // namespace

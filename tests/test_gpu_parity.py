@@ -150,6 +150,34 @@ def test_selection_crafted_ties_and_order():
     assert boundary_ties > 20  # the case really exercises ties at the boundary
 
 
+@pytest.mark.parametrize("shape", [
+    # > 1024 candidates: the LDS sort path
+    shp(seq_len=20480, seg_len=2048, hist_block=16, query_block=64, top_k=8, n_q_heads=2,
+        n_kv_heads=1, head_dim=64),
+    # 64 < candidates <= 1024 with k spanning several lanes' registers
+    shp(seq_len=8192, seg_len=1024, hist_block=16, query_block=128, top_k=100, n_q_heads=4,
+        n_kv_heads=2),
+])
+def test_selection_many_candidates(shape):
+    """Selection only (summaries + top-k) against the oracle, bit-exact."""
+    inp = make_inputs(shape, seed=12, with_do=False)
+    dev = upload(inp, shape)
+    cfg = hga.Config.from_shape(shape)
+    buf = hga.Buffers(cfg, bwd=False)
+    nblk = shape.seq_len // shape.hist_block
+    hga.summarize(cfg, dev["k"], 0, nblk, buf.summ)
+    for s in range(shape.nseg):
+        hga.select(cfg, dev["q"], buf.summ, s, buf.sel)
+    torch.cuda.synchronize()
+    kbar = orc.block_summaries(inp["k"], shape.hist_block)
+    nqb = shape.n_qblocks
+    for s in range(shape.nseg):
+        assert orc.selection_gap(inp["q"], inp["k"], shape, s) >= 1e-3
+        want = orc.select_segment(inp["q"], inp["k"], shape, s, kbar=kbar)
+        np.testing.assert_array_equal(to_np(buf.sel)[:, :, s * nqb:(s + 1) * nqb], want,
+                                      err_msg=f"segment {s}")
+
+
 def test_summarize_matches_closed_form():
     """K[t, d] = t//64 + 0.25*(t%64) - (d%16)/8 (all bf16-exact): the mean of
     block i is i + 7.875 - (d%16)/8 exactly; rows outside the requested
