@@ -133,8 +133,8 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
   const int my_count = half ? ntiles - n0 : n0;
 
   const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
-  const __bf16* kg = k + kv_base;
-  const __bf16* vg = v + kv_base;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.S * (2 * D));
 
   const int tq = qfirst + lq;
   const bool row_ok = lq < nvalid;
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
   fo.init(lane);
 
   if (my_count > 0)
-    dma_kv_tile<D, TK>(src, my_first, kg, vg, s_tiles[half][0], s_tiles[half][0] + TILE_B, wr,
+    dma_kv_tile<D, TK>(src, my_first, kr, vr, s_tiles[half][0], s_tiles[half][0] + TILE_B, wr,
                        lane);
   drain_vmem_loads();
   __syncthreads();
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
     const int it = my_first + i;
     const bool mine = i < my_count;
     if (i + 1 < my_count)
-      dma_kv_tile<D, TK>(src, it + 1, kg, vg, s_tiles[half][(i + 1) & 1],
+      dma_kv_tile<D, TK>(src, it + 1, kr, vr, s_tiles[half][(i + 1) & 1],
                          s_tiles[half][(i + 1) & 1] + TILE_B, wr, lane);
     const bool is_local = it >= src.n_hist_tiles;
     const int local_first = t0 + (it - src.n_hist_tiles) * TK;
@@ -177,12 +177,29 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         if (is_local && local_first + 32 * st > wave_qmax) break;  // sub-tile fully masked
+        // K and V fragments of the sub-tile are requested well ahead of their
+        // MFMAs (the LDS latency is not paid once per k-step)
+        bf16x8 kf[NKK], vf[NKK];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          kf[kk] = fo.row(kt, st, kk);
+          vf[kk] = fo.row(vt, st, kk);
+        }
         floatx16 sacc = floatx16{}, pacc = floatx16{};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          sacc = mfma32(fo.row(kt, st, kk), qreg[kk], sacc);
-          pacc = mfma32(fo.row(vt, st, kk), doreg[kk], pacc);
+          sacc = mfma32(kf[kk], qreg[kk], sacc);
+          pacc = mfma32(vf[kk], doreg[kk], pacc);
         }
+        // software pipeline 8 fragments deep: 8 reads, then 2 MFMAs per 2
+        // further reads, then the last 8 MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int u = 0; u < NKK - 4; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         const bool need_mask = is_local ? (local_first + 32 * st + 31 > qfirst)
                                         : ((it * TK + 32 * st + 32) > src.nh);
         if (need_mask) {

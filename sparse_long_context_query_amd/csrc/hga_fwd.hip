@@ -103,8 +103,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
   const int my_count = half ? ntiles - n0 : n0;
 
   const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
-  const __bf16* kg = k + kv_base;
-  const __bf16* vg = v + kv_base;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.S * (2 * D));
 
   const int tq = qfirst + lq;
   const bool row_ok = lq < nvalid;
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
   fo.init(lane);
 
   if (my_count > 0)
-    dma_kv_tile<D, TK>(src, my_first, kg, vg, s_tiles[half][0], s_tiles[half][0] + TILE_B, wr,
+    dma_kv_tile<D, TK>(src, my_first, kr, vr, s_tiles[half][0], s_tiles[half][0] + TILE_B, wr,
                        lane);
   drain_vmem_loads();
   __syncthreads();
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
     const int it = my_first + i;
     const bool mine = i < my_count;
     if (i + 1 < my_count)
-      dma_kv_tile<D, TK>(src, it + 1, kg, vg, s_tiles[half][(i + 1) & 1],
+      dma_kv_tile<D, TK>(src, it + 1, kr, vr, s_tiles[half][(i + 1) & 1],
                          s_tiles[half][(i + 1) & 1] + TILE_B, wr, lane);
 
     const bool is_local = it >= src.n_hist_tiles;
@@ -142,15 +142,25 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
     if (work) {
       const unsigned char* kt = s_tiles[half][i & 1];
       const unsigned char* vt = kt + TILE_B;
+      // all K fragments of the tile are requested before the first MFMA so
+      // that the LDS latency is paid once per tile, not once per k-step
+      bf16x8 kf[NKK][2];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) kf[kk][st] = fo.row(kt, st, kk);
       floatx16 sacc[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) sacc[st] = floatx16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-          sacc[st] = mfma32(fo.row(kt, st, kk), qreg[kk], sacc[st]);
+        for (int st = 0; st < 2; ++st) sacc[st] = mfma32(kf[kk][st], qreg[kk], sacc[st]);
       }
+      // keep that order through instruction scheduling: 2*NKK LDS reads, then
+      // the 2*NKK MFMAs (each waits only for its own fragment)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NKK, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NKK, 0);
       // tile max of the raw scores; mask only on tiles that can hold
       // invisible keys
       const bool need_mask = is_local ? (local_first + TK - 1 > qfirst)
@@ -171,7 +181,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[st][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * a.c2;
+      mt = pair_max(mt) * a.c2;
       const bool raise = mt > m_run + kRescale;
       if (__ballot(raise)) {
         const float m_new = raise ? mt : m_run;
@@ -213,7 +223,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
   }
 
   // both lanes of a query kept partial row sums over their own keys
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = pair_sum(l_run);
 
   // merge the two halves: half 1 parks (m, l, O^T) in LDS, half 0 combines
   float* park = reinterpret_cast<float*>(&s_tiles[0][0][0]);

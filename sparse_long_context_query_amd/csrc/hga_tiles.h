@@ -120,14 +120,21 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // ---- row-major LDS tiles filled by direct global->LDS loads --------------
 // A tile of bf16 rows of D elements is stored row-major without padding; the
-// 16-byte chunk c of row r sits at chunk position c ^ sw8(r), which puts
-// the 8 rows a group of lanes reads at once (and the 4 rows of a transposed
-// read) on distinct LDS banks.
-__device__ __forceinline__ int sw8(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// 16-byte chunk c of row r sits at chunk position c ^ swz<D>(r).  LDS serves
+// 256 bytes per cycle, so the 16 rows a half-wave reads with ds_read_b128
+// (same logical chunk) and the 4 rows x 4 chunks a half-wave reads with
+// ds_read_b64_tr_b16 must land on 16 distinct 16-byte bank groups:
+//   D = 128 (16 chunks per row): swz = 4*(r & 3) + ((r >> 2) & 3)
+//   D =  64 (8 chunks, 2 rows per 256 bytes): swz = 4*((r >> 1) & 1) + ((r >> 2) & 3)
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(D == 64 || D == 128, "head dim");
+  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
 
 template <int D>
 __device__ __forceinline__ int swz_byte(int r, int chunk) {
-  return r * (2 * D) + ((chunk ^ sw8(r)) << 4);
+  return r * (2 * D) + ((chunk ^ swz<D>(r)) << 4);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -137,24 +144,43 @@ __device__ __forceinline__ lds_void* to_lds(void* p) {
   return (lds_void*)(uintptr_t)(p);
 }
 
+// Raw buffer resource (stride 0) over `bytes` bytes at `base`.  Loads through
+// it at byte offsets >= bytes return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// 16 bytes per lane from buffer byte offset `voff` straight into LDS at
+// lds + 16*lane (buffer_load_dwordx4 ... lds; `lds` wave-uniform).  The
+// buffer form is used rather than the global one: a global (FLAT-encoded)
+// load into LDS still in flight makes the compiler's wait insertion drain
+// every LDS read to lgkmcnt(0), which would serialise the MFMA operand reads
+// of a double-buffered loop.  Tracked by vmcnt like any other vector load.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(lds), 16, (int)voff, 0, 0, 0);
+}
+
 // One wave copies `rows` (a multiple of 1024/(2D)) bf16 rows of D elements,
 // starting at global row pointer `g` (row stride D), into the swizzled
 // tile at `lds` (wave-uniform), 1 KB per instruction, lane l writing
 // bytes [16l, 16l+16) of each KB.  Rows at or beyond `valid` read row
-// valid-1 instead (callers mask them), so every global address stays in
-// bounds.  The data lands asynchronously: wait on vmcnt before reading.
+// valid-1 instead (callers mask them); the buffer resource covers exactly
+// the `valid` rows.  The data lands asynchronously: wait on vmcnt before
+// reading.
 template <int D>
 __device__ __forceinline__ void dma_rows(const __bf16* g, int rows, int valid, unsigned char* lds,
                                          int lane) {
   constexpr int CPR = (2 * D) / 16;  // chunks per row
   constexpr int RPI = 64 / CPR;      // rows per 1 KB instruction
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(g, (uint32_t)valid * (2 * D));
   for (int i = 0; i < rows / RPI; ++i) {
     const int row = i * RPI + lane / CPR;
     const int p = lane % CPR;
-    const int c = p ^ sw8(row);
+    const int c = p ^ swz<D>(row);
     const int rr = row < valid ? row : valid - 1;
-    __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)rr * D + c * 8),
-                                     to_lds(lds + i * 1024), 16, 0, 0);
+    buffer_to_lds16(r, (uint32_t)rr * (2 * D) + c * 16, lds + i * 1024);
   }
 }
 
@@ -189,10 +215,12 @@ __device__ __forceinline__ bf16x8 row_fragment(const unsigned char* tile, int r,
 // The 4 waves of one half of a block of threads copy the K and V rows of
 // key tile `it` straight into swizzled row-major LDS tiles (one 1 KB
 // direct load per wave and instruction, every lane supplying its own row).
+// `kr` / `vr` cover the K and V rows of one (sequence, KV head).
 template <int D, int TK>
-__device__ __forceinline__ void dma_kv_tile(const KeySource<TK>& src, int it, const __bf16* kg,
-                                            const __bf16* vg, unsigned char* kdst,
-                                            unsigned char* vdst, int wr, int lane) {
+__device__ __forceinline__ void dma_kv_tile(const KeySource<TK>& src, int it,
+                                            __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                            unsigned char* kdst, unsigned char* vdst, int wr,
+                                            int lane) {
   constexpr int CPR = (2 * D) / 16;
   constexpr int RPI = 64 / CPR;
   constexpr int NI = TK / RPI;
@@ -201,45 +229,53 @@ __device__ __forceinline__ void dma_kv_tile(const KeySource<TK>& src, int it, co
   for (int n = 0; n < NI / 4; ++n) {
     const int i = wr + 4 * n;
     const int row = i * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ sw8(row);
-    const size_t off = (size_t)src.token_row(it, row) * D + c * 8;
-    __builtin_amdgcn_global_load_lds((const void*)(kg + off), to_lds(kdst + i * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(vg + off), to_lds(vdst + i * 1024), 16, 0, 0);
+    const int c = (lane % CPR) ^ swz<D>(row);
+    const uint32_t off = (uint32_t)src.token_row(it, row) * (2 * D) + c * 16;
+    buffer_to_lds16(kr, off, kdst + i * 1024);
+    buffer_to_lds16(vr, off, vdst + i * 1024);
   }
+}
+
+// ds_read_b64_tr_b16 behind a restrict-qualified pointer.  Once inlined the
+// read carries alias-scope metadata like any ordinary load, so the compiler's
+// wait insertion treats it like the plain LDS reads beside it: it no longer
+// waits for every direct global->LDS copy still in flight (those target the
+// other buffer of a double-buffered pair; the copies a read depends on are
+// waited for explicitly before the barrier that publishes them).
+__device__ __forceinline__ bf16x4 lds_read_tr_b64(lds_bf16x4* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p);
 }
 
 // Lane-constant byte offsets of the MFMA fragments inside a swizzled
 // row-major tile of D-element bf16 rows, hoisted out of the tile loops.
-// Moving by a multiple of 8 rows keeps sw8() and only adds rows*2D bytes;
-// chunks c and c+8 of a row differ by 128 bytes after the swizzle.  So:
-//   row fragment (row lq + 32*st, chunk 2kk+hi):
-//       rowf[kk & 3] + (kk >> 2) * 128 + st * 32 * 2D
-//   transposed fragment (tile rows rbase + 4hi.. (+8), columns of block db):
-//       first read  trf[db & 1] + (db >> 1) * 128 + rbase * 2D
-//       second read the same + 8 * 2D
+// Moving by a multiple of 16 rows keeps swz() and only adds rows*2D bytes.
+//   row fragment (tile row lq + 32*st, chunk 2kk+hi): rowf[kk] + st*32*2D
+//   transposed fragment (tile rows rbase + 4hi + 0..3, then + 8..11, columns
+//   of block db; rbase a multiple of 16): trf[db][0 / 1] + rbase*2D
 template <int D>
 struct FragOffsets {
-  int rowf[4];
-  int trf[2];
+  static constexpr int NKK = D / 16;
+  static constexpr int NDB = D / 32;
+  int rowf[NKK];
+  int trf[NDB][2];
   __device__ __forceinline__ void init(int lane) {
     const int lq = lane & 31, hi = lane >> 5, j = lane & 15, grp = lane >> 4;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) rowf[kk] = swz_byte<D>(lq, 2 * kk + hi);
+    for (int kk = 0; kk < NKK; ++kk) rowf[kk] = swz_byte<D>(lq, 2 * kk + hi);
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
+    for (int db = 0; db < NDB; ++db) {
       const int d = 32 * db + 16 * (grp & 1) + 4 * (j & 3);
-      trf[db] = swz_byte<D>(4 * hi + (j >> 2), d >> 3) + (d & 7) * 2;
+      const int r0 = 4 * hi + (j >> 2);
+      trf[db][0] = swz_byte<D>(r0, d >> 3) + (d & 7) * 2;
+      trf[db][1] = swz_byte<D>(r0 + 8, d >> 3) + (d & 7) * 2;
     }
   }
   __device__ __forceinline__ bf16x8 row(const unsigned char* tile, int st, int kk) const {
-    return *reinterpret_cast<const bf16x8*>(tile + rowf[kk & 3] + (kk >> 2) * 128 +
-                                            st * 32 * 2 * D);
+    return *reinterpret_cast<const bf16x8*>(tile + rowf[kk] + st * 32 * 2 * D);
   }
   __device__ __forceinline__ bf16x8 tr(const unsigned char* tile, int rbase, int db) const {
-    const unsigned char* p = tile + trf[db & 1] + (db >> 1) * 128 + rbase * 2 * D;
-    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)to_lds((void*)p));
-    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4*)to_lds((void*)(p + 8 * 2 * D)));
+    const bf16x4 a = lds_read_tr_b64((lds_bf16x4*)to_lds((void*)(tile + trf[db][0] + rbase * 2 * D)));
+    const bf16x4 b = lds_read_tr_b64((lds_bf16x4*)to_lds((void*)(tile + trf[db][1] + rbase * 2 * D)));
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   }
 };
@@ -247,6 +283,19 @@ struct FragOffsets {
 // exp2 straight on v_exp_f32 (no denormal range fix-up: results below the
 // normal range flush to zero, which the softmax never needs)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Max / sum of a value over the lane pair (l, l^32) that holds one query's
+// two halves of a C-layout column: v_permlane32_swap, a VALU op (no LDS).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Waits for every outstanding vector-memory load of this wave (vmcnt(0);
 // expcnt and lgkmcnt left at their maxima).  Used once before a pipelined
