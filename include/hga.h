@@ -70,7 +70,7 @@ typedef enum { HGA_F32 = 0, HGA_BF16 = 1 } hga_dtype;
  * all sizes >= 1, S % L == 0, L % Bh == 0, L % Bq == 0, Hq % Hkv == 0.
  * Supported (else HGA_ERR_UNSUPPORTED): head_dim 64 or 128; dtype F32 or
  * BF16; S/Bh <= 8192; top_k <= 1024; bf16 kernels need Bh and Bq to be
- * multiples of 16. */
+ * multiples of 16; one head's S x D slice at most 2 GiB. */
 typedef struct hga_config {
   int32_t batch;
   int32_t seq_len;

@@ -31,7 +31,7 @@ The summary and score rule is fixed by the benchmark spec, not the pages:
 summary = mean of the block's keys per KV head, score = dot product with the
 query block's mean query, top-k ties go to the lower block index.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
   * one selection per (sequence, KV head, query block); the query mean
     averages the block's tokens and the query heads that share the KV head;
   * history = whole blocks before the segment start t0; blocks of the active

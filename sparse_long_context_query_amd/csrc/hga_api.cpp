@@ -70,6 +70,10 @@ int make_prob(const hga_config* c, hga::Prob* p) {
                 "bf16 kernels need hist_block and query_block to be multiples of 16");
   if (c->dtype == HGA_F32 && c->hist_block % 4)
     return fail(HGA_ERR_UNSUPPORTED, "f32 kernels need hist_block to be a multiple of 4");
+  // the bf16 kernels address one (sequence, head) slice of a tensor through a
+  // buffer resource with a 32-bit byte count
+  if ((double)c->seq_len * c->head_dim * (c->dtype == HGA_F32 ? 4 : 2) > 2147483647.0)
+    return fail(HGA_ERR_UNSUPPORTED, "seq_len*head_dim of one head exceeds 2 GiB");
   const double elems = (double)c->batch * c->n_q_heads * c->seq_len * c->head_dim;
   if (elems > 2147483647.0 * 64)
     return fail(HGA_ERR_UNSUPPORTED, "tensor too large");
