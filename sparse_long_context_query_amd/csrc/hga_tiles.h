@@ -86,6 +86,7 @@ struct KeySource {
   int t0;            // segment start token
   int tend;          // one past the last local token of the segment
   int n_hist_tiles;  // ceil(nh / TK)
+  int tpb;           // tiles per history block when Bh % TK == 0, else 0
 
   __device__ __forceinline__ void init(const int* list, int count, int bh, int seg_start,
                                        int seg_end) {
@@ -95,6 +96,7 @@ struct KeySource {
     t0 = seg_start;
     tend = seg_end;
     n_hist_tiles = (nh + TK - 1) / TK;
+    tpb = (bh % TK == 0) ? bh / TK : 0;
   }
 
   // token of row r of tile `it`; rows that hold no key map to the segment's
@@ -107,8 +109,23 @@ struct KeySource {
     const int t = t0 + (it - n_hist_tiles) * TK + r;
     return t < tend ? t : t0;
   }
-};
 
+  // When every history tile lies inside one selected block (tpb > 0), the
+  // rows of tile `it` are consecutive tokens: returns the (wave-uniform)
+  // token of row 0, and row r is that plus r (local rows at or beyond the
+  // segment end still map to t0 through local_row).
+  __device__ __forceinline__ int tile_base(int it) const {
+    if (it < n_hist_tiles) {
+      const int blk = __builtin_amdgcn_readfirstlane(hlist[it / tpb]);
+      return blk * Bh + (it % tpb) * TK;
+    }
+    return t0 + (it - n_hist_tiles) * TK;
+  }
+  __device__ __forceinline__ int contiguous_row(int it, int base, int r) const {
+    const int t = base + r;
+    return (it >= n_hist_tiles && t >= tend) ? t0 : t;
+  }
+};
 
 // Orders LDS traffic of one wave: its earlier LDS stores are visible to its
 // later LDS loads from any lane (no other wave involved).
@@ -212,6 +229,29 @@ __device__ __forceinline__ bf16x8 row_fragment(const unsigned char* tile, int r,
   return *reinterpret_cast<const bf16x8*>(tile + swz_byte<D>(r, 2 * kk + hi));
 }
 
+// The 4 waves of one half of a block of threads copy the rows of key tile
+// `it` of one tensor (K or V, resource `r`) straight into a swizzled
+// row-major LDS tile (one 1 KB direct load per wave and instruction, every
+// lane supplying its own row).
+template <int D, int TK>
+__device__ __forceinline__ void dma_tile(const KeySource<TK>& src, int it,
+                                         __amdgpu_buffer_rsrc_t r, unsigned char* dst, int wr,
+                                         int lane) {
+  constexpr int CPR = (2 * D) / 16;
+  constexpr int RPI = 64 / CPR;
+  constexpr int NI = TK / RPI;
+  static_assert(NI % 4 == 0, "instructions per wave");
+  const int base = src.tpb > 0 ? src.tile_base(it) : 0;
+#pragma unroll
+  for (int n = 0; n < NI / 4; ++n) {
+    const int i = wr + 4 * n;
+    const int row = i * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ swz<D>(row);
+    const int tok = src.tpb > 0 ? src.contiguous_row(it, base, row) : src.token_row(it, row);
+    buffer_to_lds16(r, (uint32_t)tok * (2 * D) + c * 16, dst + i * 1024);
+  }
+}
+
 // The 4 waves of one half of a block of threads copy the K and V rows of
 // key tile `it` straight into swizzled row-major LDS tiles (one 1 KB
 // direct load per wave and instruction, every lane supplying its own row).
@@ -225,6 +265,19 @@ __device__ __forceinline__ void dma_kv_tile(const KeySource<TK>& src, int it,
   constexpr int RPI = 64 / CPR;
   constexpr int NI = TK / RPI;
   static_assert(NI % 4 == 0, "instructions per wave");
+  if (src.tpb > 0) {
+    const int base = src.tile_base(it);
+#pragma unroll
+    for (int n = 0; n < NI / 4; ++n) {
+      const int i = wr + 4 * n;
+      const int row = i * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz<D>(row);
+      const uint32_t off = (uint32_t)src.contiguous_row(it, base, row) * (2 * D) + c * 16;
+      buffer_to_lds16(kr, off, kdst + i * 1024);
+      buffer_to_lds16(vr, off, vdst + i * 1024);
+    }
+    return;
+  }
 #pragma unroll
   for (int n = 0; n < NI / 4; ++n) {
     const int i = wr + 4 * n;
