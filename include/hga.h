@@ -136,7 +136,10 @@ int hga_attn_fwd(const hga_config* cfg, const void* q, const void* k,
  *   dk[t'] = scale * sum dS q, dv[t'] = sum p dO, for local keys t' only,
  *   summed over the queries t >= t' of the segment and the G heads.
  * History rows of dk/dv are not written.  ws: hga_workspace_size(cfg,
- * HGA_OP_BWD) bytes. */
+ * HGA_OP_BWD) bytes, caller-owned scratch that the call overwrites: delta
+ * [B, Hq, L] fp32, then fp32 partial sums of dk/dv for key tiles whose work
+ * is split between two blocks (added in a fixed order, so results stay
+ * bitwise deterministic).  Calls that share one workspace must not overlap. */
 int hga_attn_bwd(const hga_config* cfg, const void* q, const void* k,
                  const void* v, const void* o, const float* lse,
                  const void* dO, const int32_t* sel, int32_t seg, void* dq,

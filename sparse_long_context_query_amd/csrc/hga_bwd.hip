@@ -27,7 +27,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdArgs {
-  int S, L, Bh, Bq, K, Hq, Hkv, G, nqb, nqb_all, seg;
+  int B, S, L, Bh, Bq, K, Hq, Hkv, G, nqb, nqb_all, seg;
   int wpu;      // dq: blocks of threads per (b, g, j) unit
   int nq32;     // 32-row query sub-blocks per query block
   float c2;     // scale * log2(e)
@@ -62,6 +62,43 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o,
   if (row < nrows && c == 0) delta[row] = s;
 }
 
+// Last step of a8 for the key tiles whose dk/dv work two dkdv blocks shared:
+// adds the two fp32 partial sums in a fixed order (part 0 + part 1), scales
+// dK and rounds to bf16.  Runs in the kernel launched right after the dkdv
+// kernel (the launch boundary makes the partial sums visible); the work is
+// strided over all of its threads, one item = 4 consecutive elements of one
+// key row of one slot.
+template <int D>
+__device__ __forceinline__ void dkdv_finish(const float* __restrict__ part_ws,
+                                            __bf16* __restrict__ dk, __bf16* __restrict__ dv,
+                                            const BwdArgs& a, int nph) {
+  constexpr int C4 = D / 4;
+  const int total = a.B * a.Hkv * nph * 32 * C4;
+  const int t0 = a.seg * a.L;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const int c4 = i % C4;
+    const int key = (i / C4) % 32;
+    const int rest = i / (C4 * 32);
+    const int slot = rest % nph;
+    const int bg = rest / nph;
+    const int tk = t0 + slot * 32 + key;
+    if (tk >= t0 + a.L) continue;
+    const float* p0 = part_ws + ((size_t)(bg * nph + slot) * 2) * 64 * D;
+    const float* p1 = p0 + 64 * D;
+    const float4 ka = reinterpret_cast<const float4*>(p0 + (size_t)key * D)[c4];
+    const float4 kb = reinterpret_cast<const float4*>(p1 + (size_t)key * D)[c4];
+    const float4 va = reinterpret_cast<const float4*>(p0 + (size_t)(32 + key) * D)[c4];
+    const float4 vb = reinterpret_cast<const float4*>(p1 + (size_t)(32 + key) * D)[c4];
+    const bf16x4 ko = {(__bf16)((ka.x + kb.x) * a.scale), (__bf16)((ka.y + kb.y) * a.scale),
+                       (__bf16)((ka.z + kb.z) * a.scale), (__bf16)((ka.w + kb.w) * a.scale)};
+    const bf16x4 vo = {(__bf16)(va.x + vb.x), (__bf16)(va.y + vb.y), (__bf16)(va.z + vb.z),
+                       (__bf16)(va.w + vb.w)};
+    const size_t off = ((size_t)bg * a.S + tk) * D + 4 * c4;
+    *reinterpret_cast<bf16x4*>(dk + off) = ko;
+    *reinterpret_cast<bf16x4*>(dv + off) = vo;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // a7, bf16 MFMA: dq.  Same work split as the forward: 512 threads = 8 waves,
 // up to 4 wave rows (32 queries of one head each) of one (b, g, j) unit per
@@ -81,7 +118,8 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, const float* __restrict__ lse,
     const __bf16* __restrict__ dO, const float* __restrict__ delta,
-    const int32_t* __restrict__ sel, __bf16* __restrict__ dq, BwdArgs a) {
+    const int32_t* __restrict__ sel, __bf16* __restrict__ dq, const float* __restrict__ part_ws,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, int nph, BwdArgs a) {
   constexpr int TK = 64;
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
@@ -92,6 +130,8 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char s_tiles[2][2][STAGE_B];  // [half][buf]
   __shared__ int s_hlist[kMaxTopK];
   __shared__ int s_hcount;
+
+  dkdv_finish<D>(part_ws, dk, dv, a, nph);
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int c = w % a.wpu;
@@ -257,26 +297,67 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// a8, bf16 MFMA: dk/dv of the local keys.  One block of threads (8 waves)
-// per (b, g, 32-key tile kt of the segment).  The (query head, 32-query
-// tile) pairs that see the key tile (query tiles kt.. of every head of the
-// group) are dealt round-robin to the 8 waves, two per SIMD, so one wave's
-// loads and softmax overlap the other's MFMAs.  A wave copies its pair's Q
-// and dO tiles and their lse / delta straight from memory into its own
-// swizzled LDS slice (no register staging), then, with the key tile's K
-// and V rows held in registers as B operands:
+// a8, bf16 MFMA: dk/dv of the local keys.  The work of a 32-key tile kt is
+// its (query head, 32-query tile) pairs: query tiles kt.. of every head of
+// the group, G*(nqt-kt) of them, so causality makes early key tiles up to
+// nqt times heavier than late ones.  Blocks are balanced by pairing key tile
+// p with its mirror nqt-1-p: their combined pairs are split evenly between
+// block 2p (first part of tile p) and block 2p+1 (rest of tile p, then the
+// whole mirror tile).  Both blocks publish their fp32 partial sums of tile p
+// in the workspace, and the dq kernel, launched next in the same backward
+// call, adds them in a fixed order and writes the rows (dkdv_finish).  The
+// mirror tile is written directly.
+//
+// Per item (one key tile and a range of its pairs) the pairs are dealt
+// round-robin to the 8 waves, two per SIMD, so one wave's loads and softmax
+// overlap the other's MFMAs.  A wave copies its pair's Q and dO tiles and
+// their lse / delta straight from memory into its own swizzled LDS slice (no
+// register staging), then, with the key tile's K and V rows in LDS:
 //   S  = Q . K^T,  dP = dO . V^T      (A operands: tile rows)
 //   P  = exp2(S c2 - lse2), dS = P * (dP - delta)
 //   dV^T += dO^T . P,  dK^T += Q^T . dS   (A operands: transposed reads of
 //                                          the same tiles)
-// The 8 partial dK^T, dV^T are folded pairwise through LDS at the end.
+// The 8 partial dK^T, dV^T are folded pairwise through LDS at the end of the
+// item.
 // ---------------------------------------------------------------------------
+
+// Key-tile schedule of dkdv block n of one (sequence, KV head): item 0 is
+// part `part` of key tile p (a partial sum), item 1 (block 2p+1 only, when p
+// has a distinct mirror) is the whole mirror tile.  Scalars only, so that
+// nothing is indexed at run time.
+struct DkdvItems {
+  int count;
+  int p, part;  // mirror pair index (= key tile of item 0, partial slot), part
+  int a0, a1;   // pair range of item 0
+  int mirror;   // key tile of item 1
+  int wl;       // pairs of item 1
+};
+
+__device__ __forceinline__ DkdvItems dkdv_items(int n, int nkt, int G) {
+  DkdvItems it;
+  it.p = n >> 1;
+  it.part = n & 1;
+  const int nh = nkt >> 1;  // tiles that have a distinct mirror
+  const int wh = G * (nkt - it.p);
+  it.wl = it.p < nh ? G * (it.p + 1) : 0;
+  const int split = (wh + it.wl + 1) >> 1;  // never above wh
+  it.a0 = it.part ? split : 0;
+  it.a1 = it.part ? wh : split;
+  it.mirror = nkt - 1 - it.p;
+  it.count = (it.part == 1 && it.wl > 0) ? 2 : 1;
+  return it;
+}
+
+// One dkdv item: key tile kt, pairs [pbeg, pend) dealt to the 8 waves, fold,
+// then either the final bf16 rows or (partial) the raw fp32 sums in slot pp.
 template <int D>
-__global__ __launch_bounds__(512) void dkdv_bf16_kernel(
+__device__ __forceinline__ void dkdv_item(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, const float* __restrict__ lse,
     const __bf16* __restrict__ dO, const float* __restrict__ delta,
-    __bf16* __restrict__ dk, __bf16* __restrict__ dv, BwdArgs a) {
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, float* __restrict__ pp,
+    const BwdArgs& a, unsigned char* s_raw, int b, int g, int kt, int pbeg, int pend,
+    bool partial) {
   constexpr int TQ = 32;                 // queries per tile
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
@@ -284,18 +365,8 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   constexpr int SLICE_B = 2 * TILE_B + 256;  // Q tile, dO tile, lse + delta
   constexpr int NW = 8;
   constexpr int PART_F = 2 * NDB * 16 * 64;  // floats of one wave's (dK^T, dV^T)
-  constexpr int STAGE_B = 2 * TILE_B + NW * SLICE_B;  // K, V tiles + wave slices
-  constexpr int LDS_BYTES = STAGE_B > 4 * PART_F * 4 ? STAGE_B : 4 * PART_F * 4;
-  __shared__ __attribute__((aligned(1024))) unsigned char s_raw[LDS_BYTES];
-
-  const int nkt = (a.L + 31) / 32;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = w % nkt;
-  const int g = (w / nkt) % a.Hkv;
-  const int b = w / (nkt * a.Hkv);
   const int t0 = a.seg * a.L;
   const int tend = t0 + a.L;
-
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
@@ -304,13 +375,14 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   unsigned char* s_q = s_raw + 2 * TILE_B + wave * SLICE_B;
   unsigned char* s_do = s_q + TILE_B;
   float* s_ld = reinterpret_cast<float*>(s_do + TILE_B);  // [0,32) lse, [32,64) delta
-
-  // K and V rows of this key tile, shared by the 8 waves as B operands
-  // (lane (key lq, hi) reads K[key][16kk + 8hi .. +7])
+  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
+  // K and V rows of this key tile, shared by the 8 waves (lane (key lq, hi)
+  // reads K[key][16kk + 8hi .. +7]); the barrier also retires the previous
+  // item's reads of the fold buffer that overlaps these tiles
   const int kfirst = t0 + kt * 32;
   const int tk = kfirst + lq;
   const bool key_ok = tk < tend;
-  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
+  __syncthreads();
   if (wave == 0) dma_rows<D>(k + kv_base + (size_t)kfirst * D, 32, tend - kfirst, s_k, lane);
   if (wave == 1) dma_rows<D>(v + kv_base + (size_t)kfirst * D, 32, tend - kfirst, s_v, lane);
   drain_vmem_loads();
@@ -322,9 +394,7 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   FragOffsets<D> fo;
   fo.init(lane);
 
-  const int nqt = (a.L + TQ - 1) / TQ;
-  const int npairs = (nqt - kt) * a.G;
-  for (int pi = wave; pi < npairs; pi += NW) {
+  for (int pi = pbeg + wave; pi < pend; pi += NW) {
     const int qt = kt + pi / a.G;
     const int h = g * a.G + pi % a.G;
     const int tq0 = t0 + qt * TQ;
@@ -385,34 +455,65 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     wave_lds_sync();  // this slice's reads are done before the next pair's loads land
   }
 
-  // fold the 8 partial sums pairwise through LDS: 8 -> 4 -> 2 -> 1 (the
-  // first barrier also retires every wave's reads of the K/V tiles)
-  float* fold = reinterpret_cast<float*>(s_raw);
+  // fold the 8 partial sums pairwise through LDS: 8 -> 4 -> 2 -> 1, 16 bytes
+  // per lane and access (the first barrier also retires every wave's reads
+  // of the K/V tiles)
+  float4* fold = reinterpret_cast<float4*>(s_raw);
+  constexpr int PART_F4 = PART_F / 4;
   for (int span = NW / 2; span >= 1; span >>= 1) {
     __syncthreads();
     if (wave >= span && wave < 2 * span) {
-      float* dst = fold + (wave - span) * PART_F;
+      float4* dst = fold + (wave - span) * PART_F4;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          dst[((0 * NDB + db) * 16 + r) * 64 + lane] = dkacc[db][r];
-          dst[((1 * NDB + db) * 16 + r) * 64 + lane] = dvacc[db][r];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const floatx16& x = dkacc[db];
+          const floatx16& y = dvacc[db];
+          dst[((0 * NDB + db) * 4 + r4) * 64 + lane] =
+              make_float4(x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]);
+          dst[((1 * NDB + db) * 4 + r4) * 64 + lane] =
+              make_float4(y[4 * r4], y[4 * r4 + 1], y[4 * r4 + 2], y[4 * r4 + 3]);
         }
     }
     __syncthreads();
     if (wave < span) {
-      const float* src_ = fold + wave * PART_F;
+      const float4* src_ = fold + wave * PART_F4;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          dkacc[db][r] += src_[((0 * NDB + db) * 16 + r) * 64 + lane];
-          dvacc[db][r] += src_[((1 * NDB + db) * 16 + r) * 64 + lane];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 x = src_[((0 * NDB + db) * 4 + r4) * 64 + lane];
+          const float4 y = src_[((1 * NDB + db) * 4 + r4) * 64 + lane];
+          dkacc[db][4 * r4] += x.x; dkacc[db][4 * r4 + 1] += x.y;
+          dkacc[db][4 * r4 + 2] += x.z; dkacc[db][4 * r4 + 3] += x.w;
+          dvacc[db][4 * r4] += y.x; dvacc[db][4 * r4 + 1] += y.y;
+          dvacc[db][4 * r4 + 2] += y.z; dvacc[db][4 * r4 + 3] += y.w;
         }
     }
   }
-  if (wave == 0 && key_ok) {
+  if (wave != 0) return;
+
+  if (partial) {
+    // one of the two partial sums of this key tile: raw fp32 rows
+    // [dK^T keys 0..31 | dV^T keys 0..31] x D, added by the dq kernel that
+    // follows in the same backward call
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * db + 8 * r4 + 4 * hi;
+        *reinterpret_cast<float4*>(pp + (size_t)lq * D + d) =
+            make_float4(dkacc[db][4 * r4], dkacc[db][4 * r4 + 1], dkacc[db][4 * r4 + 2],
+                        dkacc[db][4 * r4 + 3]);
+        *reinterpret_cast<float4*>(pp + (size_t)(32 + lq) * D + d) =
+            make_float4(dvacc[db][4 * r4], dvacc[db][4 * r4 + 1], dvacc[db][4 * r4 + 2],
+                        dvacc[db][4 * r4 + 3]);
+      }
+    }
+    return;
+  }
+  if (key_ok) {
     __bf16* kp = dk + kv_base + (size_t)tk * D;
     __bf16* vp = dv + kv_base + (size_t)tk * D;
 #pragma unroll
@@ -431,6 +532,38 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     }
   }
 }
+
+template <int D>
+__global__ __launch_bounds__(512) void dkdv_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, const float* __restrict__ lse,
+    const __bf16* __restrict__ dO, const float* __restrict__ delta,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, float* __restrict__ part_ws, BwdArgs a) {
+  constexpr int TQ = 32;
+  constexpr int NDB = D / 32;
+  constexpr int TILE_B = TQ * 2 * D;
+  constexpr int SLICE_B = 2 * TILE_B + 256;
+  constexpr int NW = 8;
+  constexpr int PART_F = 2 * NDB * 16 * 64;
+  constexpr int STAGE_B = 2 * TILE_B + NW * SLICE_B;  // K, V tiles + wave slices
+  constexpr int LDS_BYTES = STAGE_B > 4 * PART_F * 4 ? STAGE_B : 4 * PART_F * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char s_raw[LDS_BYTES];
+
+  const int nkt = (a.L + 31) / 32;
+  const int nbk = nkt + (nkt & 1);  // blocks per (b, g)
+  const int nph = (nkt + 1) / 2;    // mirror pairs (partial-sum slots)
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int n = w % nbk;
+  const int g = (w / nbk) % a.Hkv;
+  const int b = w / (nbk * a.Hkv);
+  const DkdvItems it = dkdv_items(n, nkt, a.G);
+  float* pp = part_ws + ((size_t)((b * a.Hkv + g) * nph + it.p) * 2 + it.part) * 64 * D;
+  dkdv_item<D>(q, k, v, lse, dO, delta, dk, dv, pp, a, s_raw, b, g, it.p, it.a0, it.a1, true);
+  if (it.count == 2)
+    dkdv_item<D>(q, k, v, lse, dO, delta, dk, dv, pp, a, s_raw, b, g, it.mirror, 0, it.wl, false);
+}
+
+
 
 // ---------------------------------------------------------------------------
 // float32 kernels (reference-precision path, plain VALU).
@@ -582,6 +715,7 @@ __global__ __launch_bounds__(64) void dkdv_f32_kernel(
 
 BwdArgs make_args(const Prob& p, int seg) {
   BwdArgs a;
+  a.B = p.B;
   a.S = p.S; a.L = p.L; a.Bh = p.Bh; a.Bq = p.Bq; a.K = p.K; a.Hq = p.Hq; a.Hkv = p.Hkv;
   a.G = p.G; a.nqb = p.nqb; a.nqb_all = p.nqb_all; a.seg = seg;
   a.nq32 = (p.Bq + 31) / 32;
@@ -589,6 +723,21 @@ BwdArgs make_args(const Prob& p, int seg) {
   a.c2 = p.scale * kLog2e;
   a.scale = p.scale;
   return a;
+}
+
+// Backward workspace: delta [B, Hq, L] fp32, then the dK/dV partial sums of
+// the mirror-paired key tiles, [B, Hkv, nph, 2, 64, D] fp32.
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t dkdv_slots(const Prob& p) {
+  const size_t nph = ((size_t)(p.L + 31) / 32 + 1) / 2;
+  return (size_t)p.B * p.Hkv * nph;
+}
+size_t delta_bytes(const Prob& p) { return round256((size_t)p.B * p.Hq * p.L * sizeof(float)); }
+size_t partial_bytes(const Prob& p) {
+  return round256(dkdv_slots(p) * 2 * 64 * p.D * sizeof(float));
+}
+float* dkdv_partials(const Prob& p, float* delta) {
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(delta) + delta_bytes(p));
 }
 
 template <typename T, int D>
@@ -610,21 +759,25 @@ hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
   hipError_t e = delta_t<__bf16, D>(p, o, dO, seg, delta, st);
   if (e != hipSuccess) return e;
   BwdArgs a = make_args(p, seg);
+  const int nkt = (p.L + 31) / 32;
+  const int nph = (nkt + 1) / 2;
+  float* part_ws = dkdv_partials(p, delta);
+  {
+    // dk/dv first: the dq kernel finishes the key tiles it left as partial sums
+    const int nblocks = p.B * p.Hkv * (nkt + (nkt & 1));
+    ProfScope ps(HGA_K_BWD_DKDV, st);
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, lse,
+                       (const __bf16*)dO, delta, (__bf16*)dk, (__bf16*)dv, part_ws, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   {
     const int nblocks = p.B * p.Hkv * p.nqb * a.wpu;
     ProfScope ps(HGA_K_BWD_DQ, st);
     hipLaunchKernelGGL((dq_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dO, delta, sel,
-                       (__bf16*)dq, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    const int nblocks = p.B * p.Hkv * ((p.L + 31) / 32);
-    ProfScope ps(HGA_K_BWD_DKDV, st);
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, lse,
-                       (const __bf16*)dO, delta, (__bf16*)dk, (__bf16*)dv, a);
+                       (__bf16*)dq, part_ws, (__bf16*)dk, (__bf16*)dv, nph, a);
     e = hipGetLastError();
   }
   return e;
@@ -660,8 +813,7 @@ hipError_t bwd_f32(const Prob& p, const void* q, const void* k, const void* v,
 }  // namespace
 
 size_t bwd_workspace_bytes(const Prob& p) {
-  const size_t delta = (size_t)p.B * p.Hq * p.L * sizeof(float);
-  return (delta + 255) & ~(size_t)255;
+  return delta_bytes(p) + partial_bytes(p);
 }
 
 hipError_t launch_bwd(const Prob& p, const void* q, const void* k, const void* v,

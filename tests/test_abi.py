@@ -113,7 +113,9 @@ def test_bad_summary_range(L):
 def test_workspace_too_small(L):
     cfg = good_cfg()
     need = L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_BWD)
-    assert need == 1 * 32 * 1024 * 4  # one fp32 row-sum per query row of a segment
+    # one fp32 row-sum per query row of a segment, then per mirror pair of
+    # 32-key tiles (16 per KV head) two fp32 partial dK/dV tiles
+    assert need == 1 * 32 * 1024 * 4 + 8 * 16 * 2 * 64 * 128 * 4
     rc = L.hga_attn_bwd(ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE,
                         FAKE, FAKE, FAKE, need - 1, None)
     assert rc == hga.HGA_ERR_WORKSPACE
