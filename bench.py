@@ -47,7 +47,97 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size "
                          "reference for HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn the counter CSVs of two rocprofv3 --pmc runs of "
+                         "'bench.py --copy-calibration' (FETCH_SIZE, then WRITE_SIZE) into "
+                         "per-launch HBM bytes, write profiles/traffic.json, print a table")
     return ap.parse_args()
+
+
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_CLASS_OF = {"fwd_bf16_kernel": "fwd", "dq_bf16_kernel": "bwd_dq",
+                   "dkdv_bf16_kernel": "bwd_dkdv", "delta_kernel": "bwd_pre",
+                   "select_kernel": "select", "summarize_kernel": "summarize"}
+
+
+def sources_sha256() -> str:
+    """Hash of the kernel sources and the public header (the counters in
+    profiles/traffic.json are used only for the sources they were taken on)."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (os.path.join(ROOT, "sparse_long_context_query_amd", "csrc"), os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".hip", ".h", ".cpp")):
+                h.update(name.encode())
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()
+
+
+def pmc_summary(fetch_csv, write_csv, workload):
+    """Per-dispatch HBM bytes of each library kernel class from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch, summed over the 8 XCDs), each scaled by what
+    the same counter reads for the run's plain 256 MiB device copy."""
+    import csv
+    import re
+
+    def load(path, counter):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    copy_kib = 256 * 1024
+    cf = [v for k, vs in fetch.items() if "copyBuffer" in k for v in vs]
+    cw = [v for k, vs in write.items() if "copyBuffer" in k for v in vs]
+    if not cf or not cw:
+        raise SystemExit("no 256 MiB calibration copy in the counter files (run with --copy-calibration)")
+    f_scale, w_scale = copy_kib / cf[0], copy_kib / cw[0]
+    classes = {}
+    for name in fetch:
+        m = re.search(r"(fwd_bf16_kernel|dq_bf16_kernel|dkdv_bf16_kernel|delta_kernel|"
+                      r"select_kernel|summarize_kernel)", name)
+        if not m:
+            continue
+        c = classes.setdefault(KERNEL_CLASS_OF[m.group(1)], {"fetch": [], "write": []})
+        c["fetch"] += fetch[name]
+        c["write"] += write.get(name, [])
+    out = {"workload": workload, "sources_sha256": sources_sha256(),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "calibration": {"copy_kib": copy_kib, "fetch_kib": cf[0], "write_kib": cw[0]},
+           "kernels": {}}
+    for c, v in sorted(classes.items()):
+        fk = sum(v["fetch"]) / len(v["fetch"])
+        wk = sum(v["write"]) / len(v["write"]) if v["write"] else 0.0
+        out["kernels"][c] = {"dispatches": len(v["fetch"]), "fetch_kib_raw": round(fk, 1),
+                             "write_kib_raw": round(wk, 1),
+                             "hbm_bytes_per_launch": int(round((fk * f_scale + wk * w_scale) * 1024))}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"calibration: 256 MiB copy reads FETCH_SIZE {cf[0]:.1f} KiB (scale {f_scale:.3f}), "
+          f"WRITE_SIZE {cw[0]:.1f} KiB (scale {w_scale:.3f})")
+    print("| kernel class | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MiB per launch |")
+    print("|---|---:|---:|---:|---:|")
+    for c, v in out["kernels"].items():
+        print(f"| {c} | {v['dispatches']} | {v['fetch_kib_raw']:.1f} | {v['write_kib_raw']:.1f} | "
+              f"{v['hbm_bytes_per_launch'] / 2**20:.2f} |")
+
+
+def measured_traffic(kernel_class, workload):
+    """HBM bytes per launch of a kernel class from profiles/traffic.json, or
+    None when absent or taken on other sources or another workload."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("sources_sha256") != sources_sha256():
+        return None
+    k = t.get("kernels", {}).get(kernel_class)
+    return k["hbm_bytes_per_launch"] if k else None
 
 
 def timed_passes(buf, dev, bwd, n, profile_classes=None):
@@ -81,37 +171,50 @@ def cpu_baseline(inp, shape, budget_s):
         threads = os.cpu_count() or 1
     total = work.flops(shape)
     kbar = orc.block_summaries(inp["k"], shape.hist_block)
-    done = []
     t_start = time.perf_counter()
+    # whole segments of one (sequence, KV head) group after another until the
+    # time budget is spent; the selection of a segment covers every group
     order = [1, shape.nseg - 1] + list(range(2, shape.nseg - 1))
-    for s in order:
-        if time.perf_counter() - t_start > budget_s and done:
-            break
-        sel = orc.select_segment(inp["q"], inp["k"], shape, s, kbar=kbar)
-        O, LSE = orc.segment_forward(inp["q"], inp["k"], inp["v"], sel, shape, s, groups=[(0, 0)])
-        if shape.bwd:
-            orc.segment_backward(inp["q"], inp["k"], inp["v"], inp["do"], sel, shape, s, O, LSE,
-                                 groups=[(0, 0)])
-        done.append(s)
+    groups = [(b, g) for b in range(shape.batch) for g in range(shape.n_kv_heads)]
+    sels = {}
+    sample_fl = 0.0
+    done = []
+    for b, g in groups:
+        for s in order:
+            if time.perf_counter() - t_start > budget_s and done:
+                break
+            if s not in sels:
+                sels[s] = orc.select_segment(inp["q"], inp["k"], shape, s, kbar=kbar)
+            O, LSE = orc.segment_forward(inp["q"], inp["k"], inp["v"], sels[s], shape, s,
+                                         groups=[(b, g)])
+            if shape.bwd:
+                orc.segment_backward(inp["q"], inp["k"], inp["v"], inp["do"], sels[s], shape, s,
+                                     O, LSE, groups=[(b, g)])
+            f = work.flops(shape, segments=[s], groups=1)
+            sample_fl += f["fwd"] + (f["bwd"] if shape.bwd else 0)
+            done.append((b, g, s))
     elapsed = time.perf_counter() - t_start
-    sample = work.flops(shape, segments=done, groups=1)
-    key = "fwd"
-    frac = (sample["fwd"] + (sample["bwd"] if shape.bwd else 0)) / (
-        total["fwd"] + (total["bwd"] if shape.bwd else 0))
+    frac = sample_fl / (total["fwd"] + (total["bwd"] if shape.bwd else 0))
     t_full = elapsed / frac
     del np
+    ngroups = len({(b, g) for b, g, _ in done})
     return {
         "value": shape.batch * shape.seq_len / t_full,
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle, {key}+bwd of segments {done} for KV head 0 of sequence 0 "
-                   f"({elapsed:.1f} s), scaled by its {frac:.4f} share of the pass FLOPs"),
+        "sample": (f"fp64 numpy oracle, fwd{'+bwd' if shape.bwd else ''} of {len(done)} "
+                   f"(segment, sequence, KV head) groups over {ngroups} KV heads, segment "
+                   f"selection included ({elapsed:.1f} s), scaled by their {frac:.4f} share "
+                   f"of the pass FLOPs"),
     }
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the HGA hot "
               "path here has no multi-GPU mode.", file=sys.stderr)
@@ -224,7 +327,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
-            "traffic": None,
+            "traffic": measured_traffic(dominant, shape.name),
             "avg_launch_us": round(avg_launch_ms * 1e3, 2),
             "launches": dom_n,
             "algorithmic_flop_per_launch": per_launch_flop,
