@@ -13,46 +13,18 @@
 //   A (32 x 16): lane holds A[l%32][8*hi .. 8*hi+7]
 //   B (16 x 32): lane holds B[8*hi .. 8*hi+7][l%32]
 //   C (32 x 32): lane holds C[8*(r/4) + 4*hi + r%4][l%32], r = 0..15
-// A product C = A.B contracting over an index that the other operand reads
-// "down a column" needs that operand stored transposed.  Such tiles are
-// staged into LDS transposed, with the 16-key groups permuted by swapping
-// bits 2 and 3 of the key position: then the 8 k-values a lane feeds from
-// an accumulator in C layout (rows 4*hi..4*hi+3 and 8+4*hi..8+4*hi+3 of a
-// 16-row chunk) sit contiguously at positions 8*hi..8*hi+7.  Transposed
-// rows are TK elements long with their 16-byte units XOR-swizzled by the
-// row index to spread LDS banks.
+// Tiles are kept row-major in LDS (one key / query per row, 16-byte chunks
+// XOR-swizzled per row).  An operand read along a row is one ds_read_b128;
+// an operand read down a column (V^T, K^T, Q^T, dO^T) comes from two
+// ds_read_b64_tr_b16.  A C-layout accumulator used as the next product's B
+// operand supplies its 16 k-values in the order rows 4*hi..4*hi+3, then
+// 8+4*hi..8+4*hi+3 of each 16-row group; the transposed reads fetch the
+// other operand's rows in that same order.
 #pragma once
 
 #include "hga_internal.h"
 
 namespace hga {
-
-// position of key slot r inside a transposed row (swap bits 2 and 3)
-__device__ __forceinline__ int tpos(int r) {
-  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-// Element offset of (row d, position pos) in a transposed TK-wide tile.
-// 16-byte units of a row are XOR-swizzled so that the 8 consecutive rows a
-// group of lanes reads in one go, and the rows one staging store touches,
-// fall on different LDS banks.
-template <int TK>
-__device__ __forceinline__ int toff(int d, int pos) {
-  static_assert(TK == 32 || TK == 64, "tile width");
-  const int swz = (TK == 64) ? ((d + (d >> 3)) & 7) : (((d >> 1) + (d >> 3)) & 3);
-  return d * TK + ((((pos >> 3) ^ swz) << 3) | (pos & 7));
-}
-
-template <int D, int TK>
-struct TileGeom {
-  static constexpr int KSTR = D + 8;           // row-major tile row stride (elements)
-  static constexpr int ROW_ELEMS = TK * KSTR;   // one row-major tile
-  static constexpr int T_ELEMS = D * TK;        // one transposed tile
-  static constexpr int NJOB = (TK / 4) * (D / 8);  // jobs of 4 rows x 8 dims
-};
-
-__device__ __forceinline__ bf16x8 lds_b128(const __bf16* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
 
 __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -64,16 +36,6 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float 
   r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
   r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
   return r;
-}
-
-// Packs element e of four 8-wide rows into one 8-byte transposed quad.
-__device__ __forceinline__ uint2 quad_column(const uint4& r0, const uint4& r1, const uint4& r2,
-                                             const uint4& r3, int e) {
-  auto pick = [e](const uint4& u) -> uint32_t {
-    const uint32_t w = (e < 2) ? u.x : (e < 4) ? u.y : (e < 6) ? u.z : u.w;
-    return (e & 1) ? (w >> 16) : (w & 0xffffu);
-  };
-  return make_uint2(pick(r0) | (pick(r1) << 16), pick(r2) | (pick(r3) << 16));
 }
 
 // Where the keys of one query block come from: compacted list of selected
@@ -116,8 +78,9 @@ struct KeySource {
   // segment end still map to t0 through local_row).
   __device__ __forceinline__ int tile_base(int it) const {
     if (it < n_hist_tiles) {
-      const int blk = __builtin_amdgcn_readfirstlane(hlist[it / tpb]);
-      return blk * Bh + (it % tpb) * TK;
+      const int bi = tpb == 1 ? it : it / tpb;
+      const int blk = __builtin_amdgcn_readfirstlane(hlist[bi]);
+      return blk * Bh + (it - bi * tpb) * TK;
     }
     return t0 + (it - n_hist_tiles) * TK;
   }
@@ -227,29 +190,6 @@ __device__ __forceinline__ bf16x8 tr_fragment(const unsigned char* tile, int rba
 template <int D>
 __device__ __forceinline__ bf16x8 row_fragment(const unsigned char* tile, int r, int kk, int hi) {
   return *reinterpret_cast<const bf16x8*>(tile + swz_byte<D>(r, 2 * kk + hi));
-}
-
-// The 4 waves of one half of a block of threads copy the rows of key tile
-// `it` of one tensor (K or V, resource `r`) straight into a swizzled
-// row-major LDS tile (one 1 KB direct load per wave and instruction, every
-// lane supplying its own row).
-template <int D, int TK>
-__device__ __forceinline__ void dma_tile(const KeySource<TK>& src, int it,
-                                         __amdgpu_buffer_rsrc_t r, unsigned char* dst, int wr,
-                                         int lane) {
-  constexpr int CPR = (2 * D) / 16;
-  constexpr int RPI = 64 / CPR;
-  constexpr int NI = TK / RPI;
-  static_assert(NI % 4 == 0, "instructions per wave");
-  const int base = src.tpb > 0 ? src.tile_base(it) : 0;
-#pragma unroll
-  for (int n = 0; n < NI / 4; ++n) {
-    const int i = wr + 4 * n;
-    const int row = i * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ swz<D>(row);
-    const int tok = src.tpb > 0 ? src.contiguous_row(it, base, row) : src.token_row(it, row);
-    buffer_to_lds16(r, (uint32_t)tok * (2 * D) + c * 16, dst + i * 1024);
-  }
 }
 
 // The 4 waves of one half of a block of threads copy the K and V rows of

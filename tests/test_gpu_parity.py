@@ -67,6 +67,9 @@ def test_workload_pass_full_parity(name):
     shp(batch=2, seq_len=256, top_k=2),                        # batch 2
     shp(seq_len=128, seg_len=128),                             # one segment, no history
     shp(top_k=40),                                             # k covers all history
+    shp(seq_len=128, seg_len=32, hist_block=16, query_block=16, top_k=2),  # one 32-key tile
+    shp(seq_len=192, seg_len=48, hist_block=16, query_block=16, top_k=3),  # ragged key tile
+    shp(seq_len=480, seg_len=160, top_k=4),                    # odd number of key tiles
     shp(seq_len=1024, seg_len=256, hist_block=16, query_block=64, top_k=24),  # many candidates
     shp(dtype="f32", head_dim=64, n_q_heads=4, n_kv_heads=2),
     shp(dtype="f32", head_dim=128, query_block=16, hist_block=8, top_k=5, seq_len=256),
