@@ -301,10 +301,14 @@ int hga_segment_step(const hga_config* cfg, int32_t seg, int32_t flags, const vo
   }
   e = hga::launch_select(p, q, summ, seg, sel, st);
   if (e != hipSuccess) return hip_fail(e, "select launch");
-  e = hga::launch_fwd(p, q, k, v, sel, seg, o, lse, st);
+  // with the backward to follow, the forward also writes its row sums
+  // delta = rowsum(dO * o) into the workspace (bf16), saving the backward a pass
+  const bool fuse = bwd && hga::fused_delta(p);
+  e = hga::launch_fwd(p, q, k, v, sel, seg, o, lse, st, fuse ? dO : nullptr,
+                      fuse ? (float*)ws : nullptr);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   if (bwd) {
-    e = hga::launch_bwd(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, (float*)ws, st);
+    e = hga::launch_bwd(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, (float*)ws, st, fuse);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
   }
   return ok();

@@ -755,8 +755,9 @@ hipError_t delta_t(const Prob& p, const void* o, const void* dO, int seg, float*
 template <int D>
 hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
                     const void* o, const float* lse, const void* dO, const int32_t* sel,
-                    int seg, void* dq, void* dk, void* dv, float* delta, hipStream_t st) {
-  hipError_t e = delta_t<__bf16, D>(p, o, dO, seg, delta, st);
+                    int seg, void* dq, void* dk, void* dv, float* delta, hipStream_t st,
+                    bool delta_ready) {
+  hipError_t e = delta_ready ? hipSuccess : delta_t<__bf16, D>(p, o, dO, seg, delta, st);
   if (e != hipSuccess) return e;
   BwdArgs a = make_args(p, seg);
   const int nkt = (p.L + 31) / 32;
@@ -818,10 +819,13 @@ size_t bwd_workspace_bytes(const Prob& p) {
 
 hipError_t launch_bwd(const Prob& p, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, const int32_t* sel,
-                      int seg, void* dq, void* dk, void* dv, float* delta_ws, hipStream_t st) {
+                      int seg, void* dq, void* dk, void* dv, float* delta_ws, hipStream_t st,
+                      bool delta_ready) {
   if (p.dtype == HGA_BF16)
-    return p.D == 64 ? bwd_bf16<64>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st)
-                     : bwd_bf16<128>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st);
+    return p.D == 64 ? bwd_bf16<64>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st,
+                                    delta_ready)
+                     : bwd_bf16<128>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st,
+                                     delta_ready);
   return p.D == 64 ? bwd_f32<64>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st)
                    : bwd_f32<128>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st);
 }

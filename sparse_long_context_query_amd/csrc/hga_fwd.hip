@@ -51,7 +51,8 @@ template <int D>
 __global__ __launch_bounds__(512) void fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, const int32_t* __restrict__ sel,
-    __bf16* __restrict__ o, float* __restrict__ lse, FwdArgs a) {
+    __bf16* __restrict__ o, float* __restrict__ lse, const __bf16* __restrict__ dO,
+    float* __restrict__ delta, FwdArgs a) {
   constexpr int TK = 64;
   constexpr int NKK = D / 16;  // MFMA k-steps over the head dim
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
@@ -225,6 +226,19 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
   // both lanes of a query kept partial row sums over their own keys
   l_run = pair_sum(l_run);
 
+  // fused delta: the dO elements this lane multiplies are requested now, so
+  // that their latency overlaps the merge below
+  const size_t orow = ((size_t)(b * a.Hq + h) * a.S + tq) * D;
+  const bool want_delta = delta != nullptr && half == 0 && active && row_ok;
+  bf16x4 dog[NDB][4];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      dog[db][r4] = want_delta
+                        ? *reinterpret_cast<const bf16x4*>(dO + orow + 32 * db + 8 * r4 + 4 * hi)
+                        : bf16x4{};
+
   // merge the two halves: half 1 parks (m, l, O^T) in LDS, half 0 combines
   float* park = reinterpret_cast<float*>(&s_tiles[0][0][0]);
   float* park_o = park + wr * (NDB * 16 * 64);
@@ -246,7 +260,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
     const float l = l_run * f0 + l1 * f1;
     const float inv = 1.f / l;
     const float g0 = f0 * inv, g1 = f1 * inv;
-    __bf16* op = o + ((size_t)(b * a.Hq + h) * a.S + tq) * D;
+    __bf16* op = o + orow;
+    float dsum = 0.f;  // this lane's half of rowsum(dO * o) (fused delta)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -258,10 +273,17 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
           pk[e] = (__bf16)(oacc[db][r] * g0 + park_o[(db * 16 + r) * 64 + lane] * g1);
         }
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * r4 + 4 * hi) = pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dsum += (float)pk[e] * (float)dog[db][r4][e];
       }
     }
     if (lse != nullptr && hi == 0)
       lse[(size_t)(b * a.Hq + h) * a.S + tq] = (m + log2f(l)) * kLn2;
+    if (delta != nullptr) {
+      // delta of the stored (rounded) o, as the separate delta pass computes it
+      dsum = pair_sum(dsum);
+      if (hi == 0) delta[(size_t)(b * a.Hq + h) * a.L + (tq - t0)] = dsum;
+    }
   }
 }
 
@@ -363,13 +385,14 @@ FwdArgs make_args(const Prob& p, int seg) {
 
 template <int D>
 hipError_t fwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
-                    const int32_t* sel, int seg, void* o, float* lse, hipStream_t st) {
+                    const int32_t* sel, int seg, void* o, float* lse, hipStream_t st,
+                    const void* dO, float* delta) {
   FwdArgs a = make_args(p, seg);
   const int nblocks = p.B * p.Hkv * p.nqb * a.wpu;
   ProfScope ps(HGA_K_FWD, st);
   hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, sel, (__bf16*)o,
-                     lse, a);
+                     lse, (const __bf16*)dO, delta, a);
   return hipGetLastError();
 }
 
@@ -386,11 +409,15 @@ hipError_t fwd_f32(const Prob& p, const void* q, const void* k, const void* v,
 
 }  // namespace
 
+bool fused_delta(const Prob& p) { return p.dtype == HGA_BF16; }
+
 hipError_t launch_fwd(const Prob& p, const void* q, const void* k, const void* v,
-                      const int32_t* sel, int seg, void* o, float* lse, hipStream_t st) {
+                      const int32_t* sel, int seg, void* o, float* lse, hipStream_t st,
+                      const void* dO, float* delta) {
+  if (dO == nullptr || !fused_delta(p)) delta = nullptr;
   if (p.dtype == HGA_BF16)
-    return p.D == 64 ? fwd_bf16<64>(p, q, k, v, sel, seg, o, lse, st)
-                     : fwd_bf16<128>(p, q, k, v, sel, seg, o, lse, st);
+    return p.D == 64 ? fwd_bf16<64>(p, q, k, v, sel, seg, o, lse, st, dO, delta)
+                     : fwd_bf16<128>(p, q, k, v, sel, seg, o, lse, st, dO, delta);
   return p.D == 64 ? fwd_f32<64>(p, q, k, v, sel, seg, o, lse, st)
                    : fwd_f32<128>(p, q, k, v, sel, seg, o, lse, st);
 }

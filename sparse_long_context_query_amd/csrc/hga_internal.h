@@ -36,13 +36,19 @@ hipError_t launch_select(const Prob& p, const void* q, const float* summ,
 hipError_t launch_gather(const Prob& p, const void* k, const void* v,
                          const int32_t* sel, int seg, void* ko, void* vo,
                          hipStream_t st);
+// With dO and delta given (bf16 only), the forward also writes the backward's
+// row sums delta = rowsum(dO * o) into delta [B, Hq, L] (fused_delta returns
+// whether it did); launch_bwd then skips its own delta pass (delta_ready).
+bool fused_delta(const Prob& p);
 hipError_t launch_fwd(const Prob& p, const void* q, const void* k,
                       const void* v, const int32_t* sel, int seg, void* o,
-                      float* lse, hipStream_t st);
+                      float* lse, hipStream_t st, const void* dO = nullptr,
+                      float* delta = nullptr);
 hipError_t launch_bwd(const Prob& p, const void* q, const void* k,
                       const void* v, const void* o, const float* lse,
                       const void* dO, const int32_t* sel, int seg, void* dq,
-                      void* dk, void* dv, float* delta_ws, hipStream_t st);
+                      void* dk, void* dv, float* delta_ws, hipStream_t st,
+                      bool delta_ready = false);
 size_t bwd_workspace_bytes(const Prob& p);
 
 // ---- profiling hooks (no-ops unless hga_profile_begin() was called) -----
