@@ -86,16 +86,22 @@ __device__ void bitonic_desc(unsigned long long* a, int n) {
   }
 }
 
-// The k-th largest of the 64*E distinct keys held by one wave (E per lane,
-// unused slots 0): the largest T with #{keys >= T} >= k, found bit by bit
-// from the top.  Every step is one wave-uniform candidate, E compares, E
-// ballots and scalar popcounts; no shuffles, no LDS.
+// Orderable 32-bit image of a score (larger score -> larger word; -0 and +0
+// tie); 0 lies below every finite score.
+__device__ __forceinline__ uint32_t score_ord(float s) {
+  s = s + 0.0f;
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The k-th largest of the 64*E words held by one wave, counted with
+// multiplicity (E per lane, unused slots 0): the largest T with
+// #{words >= T} >= k, found bit by bit from the top.
 template <int E>
-__device__ __forceinline__ unsigned long long wave_kth_largest(const unsigned long long (&v)[E],
-                                                               int k) {
-  unsigned long long t = 0;
-  for (int bit = 63; bit >= 0; --bit) {
-    const unsigned long long cand = t | (1ull << bit);
+__device__ __forceinline__ uint32_t wave_kth_largest32(const uint32_t (&v)[E], int k) {
+  uint32_t t = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
     int c = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) c += __popcll(__ballot(v[e] >= cand));
@@ -108,15 +114,18 @@ __device__ __forceinline__ unsigned long long wave_kth_largest(const unsigned lo
 // a2 + a3: one block of threads per (query block j, KV head g, sequence b).
 //   1. qbar = mean of q over the G heads of the group and the Bq tokens of
 //      the block (float32; every row load of a thread in flight at once,
-//      then an LDS fold);
+//      then an LDS fold); the summary row of each thread's first candidate
+//      is requested before the q rows so that both round trips overlap;
 //   2. score_i = qbar . summ_i (unscaled), one candidate per thread, qbar
-//      broadcast from LDS; the score and index form one orderable 64-bit key;
-//   3. the k-th largest key T: for up to 1024 candidates one wave finds it
-//      by a bitwise search over the keys held in its registers, beyond that
-//      an LDS bitonic sort over all threads;
-//   4. the candidates with key >= T, i.e. exactly the k best by (score desc,
-//      index asc), are compacted in index order (ballots), so the output is
-//      ascending; padded with -1.
+//      broadcast from LDS;
+//   3. for up to 1024 candidates one wave finds the k-th largest score T
+//      (with multiplicity) by a bitwise search over the 32-bit score order
+//      held in its registers; beyond that the score and index form one
+//      orderable 64-bit key and an LDS bitonic sort over all threads gives
+//      the k-th largest key;
+//   4. the k best by (score desc, index asc) -- every score above T plus the
+//      lowest-index ties at T, or every key >= the k-th key -- are compacted
+//      in index order (ballots), so the output is ascending; padded with -1.
 // E = keys per lane of the register search (0 selects the LDS sort).
 // ---------------------------------------------------------------------------
 template <typename T, int D, int E>
@@ -144,6 +153,17 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     return;
   }
 
+  // 2a. the first candidate's summary row of every thread, requested first
+  constexpr int NV = D / 4;
+  const float* sbase = summ + (size_t)(b * Hkv + g) * nblk * D;
+  float4 srow0[NV];
+  {
+    const int i = threadIdx.x < nb ? threadIdx.x : 0;
+    const float4* rowp = reinterpret_cast<const float4*>(sbase + (size_t)i * D);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) srow0[u] = rowp[u];
+  }
+
   // 1. query-block mean over (head in group, token in block)
   {
     const int c = threadIdx.x % C, r = threadIdx.x / C;
@@ -151,25 +171,27 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 #pragma unroll
     for (int e = 0; e < EL; ++e) acc[e] = 0.f;
     const int rows = G * Bq;
-    constexpr int U = 16;  // row loads in flight per thread
+    constexpr int U = 16;  // row loads in flight per thread (raw 16-byte vectors)
     for (int row0 = r; row0 < rows; row0 += U * R) {
-      float f[U][EL];
+      uint4 f[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int row = row0 + u * R;
         if (row < rows) {
           const int hh = row / Bq, tt = row % Bq;
-          Vec16<T>::load(q + ((size_t)(b * Hq + g * G + hh) * S + t0 + j * Bq + tt) * D + c * EL,
-                         f[u]);
+          f[u] = *reinterpret_cast<const uint4*>(
+              q + ((size_t)(b * Hq + g * G + hh) * S + t0 + j * Bq + tt) * D + c * EL);
         } else {
-#pragma unroll
-          for (int e = 0; e < EL; ++e) f[u][e] = 0.f;
+          f[u] = make_uint4(0, 0, 0, 0);
         }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
+        float x[EL];
+        Vec16<T>::load(reinterpret_cast<const T*>(&f[u]), x);
 #pragma unroll
-        for (int e = 0; e < EL; ++e) acc[e] += f[u][e];
+        for (int e = 0; e < EL; ++e) acc[e] += x[e];
+      }
     }
 #pragma unroll
     for (int e = 0; e < EL; ++e) part[r][c * EL + e] = acc[e];
@@ -185,41 +207,67 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   }
 
   // 2. scores, one candidate per thread
-  const float* sbase = summ + (size_t)(b * Hkv + g) * nblk * D;
   for (int i = threadIdx.x; i < nb; i += kThreads) {
-    const float4* rowp = reinterpret_cast<const float4*>(sbase + (size_t)i * D);
     float sc = 0.f;
-    constexpr int NV = D / 4;
-    constexpr int UV = 16;
+    if (i == threadIdx.x) {
 #pragma unroll
-    for (int v0 = 0; v0 < NV; v0 += UV) {
-      float4 x[UV];
+      for (int u = 0; u < NV; ++u) {
+        const float4 qv = *reinterpret_cast<const float4*>(&qbar[4 * u]);
+        sc += qv.x * srow0[u].x + qv.y * srow0[u].y + qv.z * srow0[u].z + qv.w * srow0[u].w;
+      }
+    } else {
+      const float4* rowp = reinterpret_cast<const float4*>(sbase + (size_t)i * D);
+      constexpr int UV = 16;
 #pragma unroll
-      for (int u = 0; u < UV; ++u) x[u] = rowp[v0 + u];
+      for (int v0 = 0; v0 < NV; v0 += UV) {
+        float4 x[UV];
 #pragma unroll
-      for (int u = 0; u < UV; ++u) {
-        const float4 qv = *reinterpret_cast<const float4*>(&qbar[4 * (v0 + u)]);
-        sc += qv.x * x[u].x + qv.y * x[u].y + qv.z * x[u].z + qv.w * x[u].w;
+        for (int u = 0; u < UV; ++u) x[u] = rowp[v0 + u];
+#pragma unroll
+        for (int u = 0; u < UV; ++u) {
+          const float4 qv = *reinterpret_cast<const float4*>(&qbar[4 * (v0 + u)]);
+          sc += qv.x * x[u].x + qv.y * x[u].y + qv.z * x[u].z + qv.w * x[u].w;
+        }
       }
     }
     s_score[i] = sc;
   }
   __syncthreads();
 
-  // 3. the k-th largest key
   if constexpr (E > 0) {
+    // 3. the k-th largest score (with multiplicity) and how many ties at it
+    //    belong to the k best
     if (threadIdx.x < 64) {
       const int lane = threadIdx.x;
-      unsigned long long v[E];
+      uint32_t v[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int i = 64 * e + lane;
-        v[e] = i < nb ? rank_key(s_score[i], i) : 0ull;
+        v[e] = i < nb ? score_ord(s_score[i]) : 0u;
       }
-      const unsigned long long thr = wave_kth_largest<E>(v, K);
-      if (lane == 0) s_thresh = thr;
+      const uint32_t thr = wave_kth_largest32<E>(v, K);
+      int gt = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) gt += __popcll(__ballot(v[e] > thr));
+      // 4. every score above thr, then the lowest-index ties, in index order
+      const int need = K - gt;
+      const unsigned long long below = (1ull << lane) - 1ull;
+      int count = 0, ties = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = 64 * e + lane;
+        const bool ok = i < nb;
+        const bool eq = ok && v[e] == thr;
+        const unsigned long long meq = __ballot(eq);
+        const bool take = (ok && v[e] > thr) || (eq && ties + __popcll(meq & below) < need);
+        const unsigned long long m = __ballot(take);
+        if (take) out[count + __popcll(m & below)] = i;
+        count += __popcll(m);
+        ties += __popcll(meq);
+      }
     }
   } else {
+    // 3. the k-th largest (score, index) key by an LDS sort
     int W = 1;
     while (W < nb) W <<= 1;
     for (int i = threadIdx.x; i < W; i += kThreads)
@@ -227,21 +275,20 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     __syncthreads();
     bitonic_desc(keys, W);
     if (threadIdx.x == 0) s_thresh = keys[K - 1];
-  }
-  __syncthreads();
-
-  // 4. the k best in index order
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const unsigned long long thr = s_thresh;
-    int count = 0;
-    for (int base = 0; base < nb; base += 64) {
-      const int i = base + lane;
-      const bool take = i < nb && rank_key(s_score[i], i) >= thr;
-      const unsigned long long m = __ballot(take);
-      const int pos = count + __popcll(m & ((1ull << lane) - 1ull));
-      if (take && pos < K) out[pos] = i;  // keys are unique: exactly K are taken
-      count += __popcll(m);
+    __syncthreads();
+    // 4. the k best in index order
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const unsigned long long thr = s_thresh;
+      int count = 0;
+      for (int base = 0; base < nb; base += 64) {
+        const int i = base + lane;
+        const bool take = i < nb && rank_key(s_score[i], i) >= thr;
+        const unsigned long long m = __ballot(take);
+        const int pos = count + __popcll(m & ((1ull << lane) - 1ull));
+        if (take && pos < K) out[pos] = i;  // keys are unique: exactly K are taken
+        count += __popcll(m);
+      }
     }
   }
 }
