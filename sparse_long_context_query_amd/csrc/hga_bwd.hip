@@ -163,6 +163,20 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
     }
   }
 
+  // the query-side rows do not depend on the selection: request them first
+  // so that their latency overlaps the compaction
+  const int tq = qfirst + lq;
+  const bool row_ok = lq < nvalid;
+  const size_t qrow = (size_t)(b * a.Hq + h) * a.S + tq;
+  bf16x8 qreg[NKK], doreg[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    qreg[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(q + qrow * D + 16 * kk + 8 * hi) : bf16x8{};
+    doreg[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(dO + qrow * D + 16 * kk + 8 * hi) : bf16x8{};
+  }
+  const float lse2 = row_ok ? lse[qrow] * kLog2e : 0.f;
+  const float dlt = row_ok ? delta[(size_t)(b * a.Hq + h) * a.L + (tq - t0)] : 0.f;
+
   const int32_t* srow = sel + ((size_t)(b * a.Hkv + g) * a.nqb_all + (size_t)a.seg * a.nqb + j) * a.K;
   const int nsel = compact_selection(srow, a.K, nb, s_hlist, &s_hcount);
   KeySource<TK> src;
@@ -176,17 +190,6 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.S * (2 * D));
 
-  const int tq = qfirst + lq;
-  const bool row_ok = lq < nvalid;
-  const size_t qrow = (size_t)(b * a.Hq + h) * a.S + tq;
-  bf16x8 qreg[NKK], doreg[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    qreg[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(q + qrow * D + 16 * kk + 8 * hi) : bf16x8{};
-    doreg[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(dO + qrow * D + 16 * kk + 8 * hi) : bf16x8{};
-  }
-  const float lse2 = row_ok ? lse[qrow] * kLog2e : 0.f;
-  const float dlt = row_ok ? delta[(size_t)(b * a.Hq + h) * a.L + (tq - t0)] : 0.f;
 
   floatx16 dqacc[NDB];
 #pragma unroll
@@ -270,12 +273,14 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
   }
 
   // add the two halves' partial dQ^T through LDS, scale, round, store
-  float* park = reinterpret_cast<float*>(&s_tiles[0][0][0]) + wr * (NDB * 16 * 64);
+  float4* park = reinterpret_cast<float4*>(&s_tiles[0][0][0]) + wr * (NDB * 4 * 64);
   if (half == 1) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) park[(db * 16 + r) * 64 + lane] = dqacc[db][r];
+      for (int r4 = 0; r4 < 4; ++r4)
+        park[(db * 4 + r4) * 64 + lane] = make_float4(dqacc[db][4 * r4], dqacc[db][4 * r4 + 1],
+                                                      dqacc[db][4 * r4 + 2], dqacc[db][4 * r4 + 3]);
   }
   __syncthreads();
   if (half == 0 && active && row_ok) {
@@ -284,12 +289,11 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 p4 = park[(db * 4 + r4) * 64 + lane];
+        const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
         bf16x4 pk;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          pk[e] = (__bf16)((dqacc[db][r] + park[(db * 16 + r) * 64 + lane]) * a.scale);
-        }
+        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)((dqacc[db][4 * r4 + e] + pv[e]) * a.scale);
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * r4 + 4 * hi) = pk;
       }
     }

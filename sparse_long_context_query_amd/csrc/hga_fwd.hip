@@ -94,6 +94,18 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
     }
   }
 
+  // the query rows do not depend on the selection: request them first so
+  // that their latency overlaps the compaction
+  const int tq = qfirst + lq;
+  const bool row_ok = lq < nvalid;
+  bf16x8 qreg[NKK];
+  {
+    const __bf16* qp = q + ((size_t)(b * a.Hq + h) * a.S + tq) * D + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qreg[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * kk) : bf16x8{};
+  }
+
   const int32_t* srow = sel + ((size_t)(b * a.Hkv + g) * a.nqb_all + (size_t)a.seg * a.nqb + j) * a.K;
   const int nsel = compact_selection(srow, a.K, nb, s_hlist, &s_hcount);
   KeySource<TK> src;
@@ -107,15 +119,6 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.S * (2 * D));
 
-  const int tq = qfirst + lq;
-  const bool row_ok = lq < nvalid;
-  bf16x8 qreg[NKK];
-  {
-    const __bf16* qp = q + ((size_t)(b * a.Hq + h) * a.S + tq) * D + 8 * hi;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      qreg[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * kk) : bf16x8{};
-  }
 
   floatx16 oacc[NDB];
 #pragma unroll
@@ -241,13 +244,15 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
 
   // merge the two halves: half 1 parks (m, l, O^T) in LDS, half 0 combines
   float* park = reinterpret_cast<float*>(&s_tiles[0][0][0]);
-  float* park_o = park + wr * (NDB * 16 * 64);
+  float4* park_o = reinterpret_cast<float4*>(park) + wr * (NDB * 4 * 64);
   float* park_ml = park + 4 * (NDB * 16 * 64) + wr * 128;
   if (half == 1) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) park_o[(db * 16 + r) * 64 + lane] = oacc[db][r];
+      for (int r4 = 0; r4 < 4; ++r4)
+        park_o[(db * 4 + r4) * 64 + lane] = make_float4(oacc[db][4 * r4], oacc[db][4 * r4 + 1],
+                                                        oacc[db][4 * r4 + 2], oacc[db][4 * r4 + 3]);
     park_ml[lane] = m_run;
     park_ml[64 + lane] = l_run;
   }
@@ -266,12 +271,11 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 p4 = park_o[(db * 4 + r4) * 64 + lane];
+        const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
         bf16x4 pk;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          pk[e] = (__bf16)(oacc[db][r] * g0 + park_o[(db * 16 + r) * 64 + lane] * g1);
-        }
+        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(oacc[db][4 * r4 + e] * g0 + pv[e] * g1);
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * r4 + 4 * hi) = pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) dsum += (float)pk[e] * (float)dog[db][r4][e];
