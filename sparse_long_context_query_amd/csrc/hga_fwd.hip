@@ -118,6 +118,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
   const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.S * (2 * D));
+  const __amdgpu_buffer_rsrc_t kr_none = make_rsrc(k + kv_base, 0u);
+  const __amdgpu_buffer_rsrc_t vr_none = make_rsrc(v + kv_base, 0u);
 
 
   floatx16 oacc[NDB];
@@ -136,13 +138,19 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
   for (int i = 0; i < n0; ++i) {
     const int it = my_first + i;
     const bool mine = i < my_count;
-    if (i + 1 < my_count)
-      dma_kv_tile<D, TK>(src, it + 1, kr, vr, s_tiles[half][(i + 1) & 1],
-                         s_tiles[half][(i + 1) & 1] + TILE_B, wr, lane);
+    // the next tile's copies: offsets now, issue among the score MFMAs (an
+    // empty resource when there is no next tile)
+    const bool copy_next = i + 1 < my_count;
+    uint32_t coff[TK / (64 / ((2 * D) / 16)) / 4];
+    kv_tile_offsets<D, TK>(src, copy_next ? it + 1 : it, wr, lane, coff);
+    const __amdgpu_buffer_rsrc_t kr_n = copy_next ? kr : kr_none;
+    const __amdgpu_buffer_rsrc_t vr_n = copy_next ? vr : vr_none;
+    unsigned char* const knext = s_tiles[half][(i + 1) & 1];
 
     const bool is_local = it >= src.n_hist_tiles;
     const int local_first = t0 + (it - src.n_hist_tiles) * TK;
     const bool work = mine && active && (!is_local || local_first <= wave_qmax);
+    if (!work) kv_tile_issue<D, TK>(kr_n, vr_n, coff, knext, knext + TILE_B, wr);
     if (work) {
       const unsigned char* kt = s_tiles[half][i & 1];
       const unsigned char* vt = kt + TILE_B;
@@ -161,10 +169,16 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
 #pragma unroll
         for (int st = 0; st < 2; ++st) sacc[st] = mfma32(kf[kk][st], qreg[kk], sacc[st]);
       }
+      kv_tile_issue<D, TK>(kr_n, vr_n, coff, knext, knext + TILE_B, wr);
       // keep that order through instruction scheduling: 2*NKK LDS reads, then
-      // the 2*NKK MFMAs (each waits only for its own fragment)
+      // the MFMAs with the copies spread among them
+      constexpr int NCP = 2 * (TK / (64 / ((2 * D) / 16)) / 4);  // copy instructions
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * NKK, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NKK, 0);
+#pragma unroll
+      for (int u = 0; u < NCP; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NKK / NCP, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
       // tile max of the raw scores; mask only on tiles that can hold
       // invisible keys
       const bool need_mask = is_local ? (local_first + TK - 1 > qfirst)

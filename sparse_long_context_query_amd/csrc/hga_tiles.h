@@ -229,6 +229,45 @@ __device__ __forceinline__ void dma_kv_tile(const KeySource<TK>& src, int it,
   }
 }
 
+// Split form of dma_kv_tile: the per-lane byte offsets of key tile `it`'s rows
+// (branches allowed) and the issue of the copies (branch-free, so that it
+// can be interleaved with other work).  A resource of 0 bytes (a tile that
+// does not exist) turns the copies into loads of zeros from no memory.
+template <int D, int TK>
+__device__ __forceinline__ void kv_tile_offsets(const KeySource<TK>& src, int it, int wr,
+                                                int lane, uint32_t (&off)[TK / (64 / ((2 * D) / 16)) / 4]) {
+  constexpr int CPR = (2 * D) / 16;
+  constexpr int RPI = 64 / CPR;
+  constexpr int NI = TK / RPI;
+  if (src.tpb > 0) {
+    const int base = src.tile_base(it);
+#pragma unroll
+    for (int n = 0; n < NI / 4; ++n) {
+      const int row = (wr + 4 * n) * RPI + lane / CPR;
+      off[n] = (uint32_t)src.contiguous_row(it, base, row) * (2 * D) + ((lane % CPR) ^ swz<D>(row)) * 16;
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < NI / 4; ++n) {
+      const int row = (wr + 4 * n) * RPI + lane / CPR;
+      off[n] = (uint32_t)src.token_row(it, row) * (2 * D) + ((lane % CPR) ^ swz<D>(row)) * 16;
+    }
+  }
+}
+
+template <int D, int TK>
+__device__ __forceinline__ void kv_tile_issue(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                              const uint32_t (&off)[TK / (64 / ((2 * D) / 16)) / 4],
+                                              unsigned char* kdst, unsigned char* vdst, int wr) {
+  constexpr int NI = TK / (64 / ((2 * D) / 16));
+#pragma unroll
+  for (int n = 0; n < NI / 4; ++n) {
+    const int i = wr + 4 * n;
+    buffer_to_lds16(kr, off[n], kdst + i * 1024);
+    buffer_to_lds16(vr, off[n], vdst + i * 1024);
+  }
+}
+
 // ds_read_b64_tr_b16 behind a restrict-qualified pointer.  Once inlined the
 // read carries alias-scope metadata like any ordinary load, so the compiler's
 // wait insertion treats it like the plain LDS reads beside it: it no longer
