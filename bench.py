@@ -35,12 +35,14 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="train_16k")
     ap.add_argument("--mode", default="planted", choices=["planted", "diverse"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-self", action="store_true")
+    ap.add_argument("--no-diverse", action="store_true",
+                    help="skip the extra timing on diverse-selection inputs")
     ap.add_argument("--dense-sdpa", action="store_true",
                     help="also time torch SDPA (flash backend) dense causal fwd+bwd")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -300,6 +302,20 @@ def main():
         del dbuf
     if args.dense_sdpa:
         extras.update(dense_sdpa(dev, shape, bwd, ms))
+    if not args.no_diverse and args.mode == "planted":
+        # the same pass on inputs whose query blocks pick different history
+        # sets (less reuse of K/V tiles across blocks); throughput only
+        log("[bench] diverse-selection inputs")
+        dinp = make_inputs(shape, seed=0, mode="diverse")
+        ddev = {k: torch.from_numpy(dinp[k]).cuda().to(dt)
+                for k in ("q", "k", "v", "do") if dinp.get(k) is not None}
+        for _ in range(args.warmup):
+            buf.run_pass(ddev["q"], ddev["k"], ddev["v"], ddev.get("do"), bwd=bwd)
+        dms, _ = timed_passes(buf, ddev, bwd, args.steps)
+        extras["diverse"] = {"tokens_per_s": round(tokens / (dms / 1e3), 1),
+                             "ms_per_step": round(dms, 4),
+                             "data": "synthetic (one planted direction per query block)"}
+        del ddev, dinp
 
     out = {
         "metric": METRIC,
