@@ -62,6 +62,23 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o,
   if (row < nrows && c == 0) delta[row] = s;
 }
 
+// Fixed cost of one dkdv item (K/V copy, fold, stores) in units of the cost
+// of one (head, query tile) pair, measured at D = 128: the block that runs
+// two items gets that many fewer pairs.
+constexpr int kDkdvItemCost = 16;
+
+// Pairs of key tile p (of nkt) that block 2p takes; the rest of tile p, if
+// any, goes to block 2p+1 ahead of the mirror tile's wl pairs.  When the
+// result is below wh = G*(nkt-p), tile p is left as two fp32 partial sums.
+__device__ __forceinline__ int dkdv_split(int wh, int wl) {
+  if (wl == 0) return (wh + 1) >> 1;
+  const int s = (wh + wl + kDkdvItemCost + 1) >> 1;
+  return s < wh ? s : wh;
+}
+__device__ __forceinline__ int dkdv_mirror_pairs(int p, int nkt, int G) {
+  return p < (nkt >> 1) ? G * (p + 1) : 0;  // tiles below nkt/2 have a mirror
+}
+
 // Last step of a8 for the key tiles whose dk/dv work two dkdv blocks shared:
 // adds the two fp32 partial sums in a fixed order (part 0 + part 1), scales
 // dK and rounds to bf16.  Runs in the kernel launched right after the dkdv
@@ -73,6 +90,7 @@ __device__ __forceinline__ void dkdv_finish(const float* __restrict__ part_ws,
                                             __bf16* __restrict__ dk, __bf16* __restrict__ dv,
                                             const BwdArgs& a, int nph) {
   constexpr int C4 = D / 4;
+  const int nkt = (a.L + 31) / 32;
   const int total = a.B * a.Hkv * nph * 32 * C4;
   const int t0 = a.seg * a.L;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
@@ -83,6 +101,8 @@ __device__ __forceinline__ void dkdv_finish(const float* __restrict__ part_ws,
     const int bg = rest / nph;
     const int tk = t0 + slot * 32 + key;
     if (tk >= t0 + a.L) continue;
+    const int wh = a.G * (nkt - slot);  // pairs of key tile `slot`
+    if (dkdv_split(wh, dkdv_mirror_pairs(slot, nkt, a.G)) >= wh) continue;
     const float* p0 = part_ws + ((size_t)(bg * nph + slot) * 2) * 64 * D;
     const float* p1 = p0 + 64 * D;
     const float4 ka = reinterpret_cast<const float4*>(p0 + (size_t)key * D)[c4];
@@ -102,10 +122,10 @@ __device__ __forceinline__ void dkdv_finish(const float* __restrict__ part_ws,
 // ---------------------------------------------------------------------------
 // a7, bf16 MFMA: dq.  Same work split as the forward: 512 threads = 8 waves,
 // up to 4 wave rows (32 queries of one head each) of one (b, g, j) unit per
-// block of threads; the key tiles (64 keys) are split in two halves walked
-// by waves 0-3 and 4-7, each half double-buffering swizzled row-major K
-// and V tiles that are copied straight from memory into LDS.  Per wave and
-// 32-key sub-tile:
+// block of threads; the key tiles (64 keys) are dealt alternately to two
+// halves, waves 0-3 and 4-7, local tiles first (walk_tile), each half
+// double-buffering swizzled row-major K and V tiles that are copied straight
+// from memory into LDS.  Per wave and 32-key sub-tile:
 //   S^T  = K . Q^T          (Q^T in registers as B operand)
 //   dP^T = V . dO^T         (dO^T in registers as B operand)
 //   dS^T = P^T * (dP^T - delta),  P^T = exp2(S^T c2 - lse2)
@@ -130,8 +150,6 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char s_tiles[2][2][STAGE_B];  // [half][buf]
   __shared__ int s_hlist[kMaxTopK];
   __shared__ int s_hcount;
-
-  dkdv_finish<D>(part_ws, dk, dv, a, nph);
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int c = w % a.wpu;
@@ -163,8 +181,19 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
     }
   }
 
-  // the query-side rows do not depend on the selection: request them first
-  // so that their latency overlaps the compaction
+  // the first local tile's copies and the query-side rows do not depend on
+  // the selection: request them first so that their latency overlaps the
+  // partial-sum finish and the compaction (local tiles come first in the
+  // walk order)
+  const int nloc = (blk_qmax - t0) / TK + 1;  // local tiles any wave of the block sees
+  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.S * (2 * D));
+  if (half < nloc) {
+    KeySource<TK> loc;
+    loc.init(s_hlist, 0, a.Bh, t0, t0 + a.L);
+    dma_kv_tile<D, TK>(loc, half, kr, vr, s_tiles[half][0], s_tiles[half][0] + TILE_B, wr, lane);
+  }
   const int tq = qfirst + lq;
   const bool row_ok = lq < nvalid;
   const size_t qrow = (size_t)(b * a.Hq + h) * a.S + tq;
@@ -177,18 +206,15 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
   const float lse2 = row_ok ? lse[qrow] * kLog2e : 0.f;
   const float dlt = row_ok ? delta[(size_t)(b * a.Hq + h) * a.L + (tq - t0)] : 0.f;
 
+  dkdv_finish<D>(part_ws, dk, dv, a, nph);
+
   const int32_t* srow = sel + ((size_t)(b * a.Hkv + g) * a.nqb_all + (size_t)a.seg * a.nqb + j) * a.K;
   const int nsel = compact_selection(srow, a.K, nb, s_hlist, &s_hcount);
   KeySource<TK> src;
   src.init(s_hlist, nsel, a.Bh, t0, t0 + a.L);
-  const int ntiles = src.n_hist_tiles + (blk_qmax - t0) / TK + 1;
-  const int n0 = (ntiles + 1) / 2;
-  const int my_first = half ? n0 : 0;
-  const int my_count = half ? ntiles - n0 : n0;
-
-  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.S * (2 * D));
+  const int ntiles = src.n_hist_tiles + nloc;
+  const int n0 = (ntiles + 1) / 2;  // walk positions of half 0; half 1 has ntiles - n0
+  const int nht = src.n_hist_tiles;
 
 
   floatx16 dqacc[NDB];
@@ -197,17 +223,18 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
   FragOffsets<D> fo;
   fo.init(lane);
 
-  if (my_count > 0)
-    dma_kv_tile<D, TK>(src, my_first, kr, vr, s_tiles[half][0], s_tiles[half][0] + TILE_B, wr,
-                       lane);
+  if (half >= nloc && half < ntiles)  // a history tile first: after the compaction
+    dma_kv_tile<D, TK>(src, walk_tile(half, nloc, nht), kr, vr, s_tiles[half][0],
+                       s_tiles[half][0] + TILE_B, wr, lane);
   drain_vmem_loads();
   __syncthreads();
 
   for (int i = 0; i < n0; ++i) {
-    const int it = my_first + i;
-    const bool mine = i < my_count;
-    if (i + 1 < my_count)
-      dma_kv_tile<D, TK>(src, it + 1, kr, vr, s_tiles[half][(i + 1) & 1],
+    const int wpos = 2 * i + half;
+    const bool mine = wpos < ntiles;
+    const int it = walk_tile(mine ? wpos : half, nloc, nht);
+    if (wpos + 2 < ntiles)
+      dma_kv_tile<D, TK>(src, walk_tile(wpos + 2, nloc, nht), kr, vr, s_tiles[half][(i + 1) & 1],
                          s_tiles[half][(i + 1) & 1] + TILE_B, wr, lane);
     const bool is_local = it >= src.n_hist_tiles;
     const int local_first = t0 + (it - src.n_hist_tiles) * TK;
@@ -305,12 +332,13 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
 // its (query head, 32-query tile) pairs: query tiles kt.. of every head of
 // the group, G*(nqt-kt) of them, so causality makes early key tiles up to
 // nqt times heavier than late ones.  Blocks are balanced by pairing key tile
-// p with its mirror nqt-1-p: their combined pairs are split evenly between
-// block 2p (first part of tile p) and block 2p+1 (rest of tile p, then the
-// whole mirror tile).  Both blocks publish their fp32 partial sums of tile p
-// in the workspace, and the dq kernel, launched next in the same backward
-// call, adds them in a fixed order and writes the rows (dkdv_finish).  The
-// mirror tile is written directly.
+// p with its mirror nqt-1-p: their combined pairs are split between block 2p
+// (first part of tile p) and block 2p+1 (rest of tile p, then the whole
+// mirror tile), the latter taking kDkdvItemCost fewer pairs for its second
+// item.  When tile p is split, both blocks publish fp32 partial sums of it in
+// the workspace, and the dq kernel, launched next in the same backward call,
+// adds them in a fixed order and writes the rows (dkdv_finish).  Other tiles
+// are written directly.
 //
 // Per item (one key tile and a range of its pairs) the pairs are dealt
 // round-robin to the 8 waves, two per SIMD, so one wave's loads and softmax
@@ -321,35 +349,47 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
 //   P  = exp2(S c2 - lse2), dS = P * (dP - delta)
 //   dV^T += dO^T . P,  dK^T += Q^T . dS   (A operands: transposed reads of
 //                                          the same tiles)
-// The 8 partial dK^T, dV^T are folded pairwise through LDS at the end of the
-// item.
+// The 8 waves' partial dK^T, dV^T are folded through LDS at the end of the
+// item by three halving exchanges, after which every wave stores one eighth.
 // ---------------------------------------------------------------------------
 
-// Key-tile schedule of dkdv block n of one (sequence, KV head): item 0 is
-// part `part` of key tile p (a partial sum), item 1 (block 2p+1 only, when p
-// has a distinct mirror) is the whole mirror tile.  Scalars only, so that
-// nothing is indexed at run time.
-struct DkdvItems {
-  int count;
-  int p, part;  // mirror pair index (= key tile of item 0, partial slot), part
-  int a0, a1;   // pair range of item 0
-  int mirror;   // key tile of item 1
-  int wl;       // pairs of item 1
-};
 
-__device__ __forceinline__ DkdvItems dkdv_items(int n, int nkt, int G) {
-  DkdvItems it;
-  it.p = n >> 1;
-  it.part = n & 1;
-  const int nh = nkt >> 1;  // tiles that have a distinct mirror
-  const int wh = G * (nkt - it.p);
-  it.wl = it.p < nh ? G * (it.p + 1) : 0;
-  const int split = (wh + it.wl + 1) >> 1;  // never above wh
-  it.a0 = it.part ? split : 0;
-  it.a1 = it.part ? wh : split;
-  it.mirror = nkt - 1 - it.p;
-  it.count = (it.part == 1 && it.wl > 0) ? 2 : 1;
-  return it;
+// (m & a) | (~m & b), per 32-bit element
+__device__ __forceinline__ float blend1(uint32_t m, float a, float b) {
+  return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
+}
+__device__ __forceinline__ float4 blend4(uint32_t m, float4 a, float4 b) {
+  return make_float4(blend1(m, a.x, b.x), blend1(m, a.y, b.y), blend1(m, a.z, b.z),
+                     blend1(m, a.w, b.w));
+}
+
+// One halving exchange of the dkdv fold.  Each of the NW waves holds N float4
+// groups per lane in f[0, N); the wave with bit `bit` clear keeps the lower
+// half, its partner (wave ^ bit) the upper half.  A wave writes the half it
+// gives away to its own slot of `xch` (N/2 groups x 64 lanes) and, after a
+// barrier, adds the partner's slot into the half it keeps, which it moves to
+// f[0, N/2).  `pre_barrier`: wait first for every wave to be done with the
+// LDS this level overwrites.
+template <int N>
+__device__ __forceinline__ void fold_level(const float4 (&f)[N], float4 (&out)[N / 2],
+                                           float4* xch, int wave, int bit, int lane,
+                                           bool pre_barrier) {
+  constexpr int H = N / 2;
+  if (pre_barrier) __syncthreads();
+  // the halves are chosen with bit masks rather than a select, which the
+  // compiler may turn into a run-time index that keeps f out of registers
+  const uint32_t m = (wave & bit) ? 0xffffffffu : 0u;  // 1s: keep the upper half
+  float4* mine = xch + (size_t)wave * H * 64 + lane;
+#pragma unroll
+  for (int i = 0; i < H; ++i) mine[i * 64] = blend4(m, f[i], f[H + i]);
+  __syncthreads();
+  const float4* theirs = xch + (size_t)(wave ^ bit) * H * 64 + lane;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float4 t = theirs[i * 64];
+    const float4 k = blend4(m, f[H + i], f[i]);
+    out[i] = make_float4(k.x + t.x, k.y + t.y, k.z + t.z, k.w + t.w);
+  }
 }
 
 // One dkdv item: key tile kt, pairs [pbeg, pend) dealt to the 8 waves, fold,
@@ -368,7 +408,6 @@ __device__ __forceinline__ void dkdv_item(
   constexpr int TILE_B = TQ * 2 * D;     // bytes of one row-major tile
   constexpr int SLICE_B = 2 * TILE_B + 256;  // Q tile, dO tile, lse + delta
   constexpr int NW = 8;
-  constexpr int PART_F = 2 * NDB * 16 * 64;  // floats of one wave's (dK^T, dV^T)
   const int t0 = a.seg * a.L;
   const int tend = t0 + a.L;
   const int tid = threadIdx.x;
@@ -459,80 +498,48 @@ __device__ __forceinline__ void dkdv_item(
     wave_lds_sync();  // this slice's reads are done before the next pair's loads land
   }
 
-  // fold the 8 partial sums pairwise through LDS: 8 -> 4 -> 2 -> 1, 16 bytes
-  // per lane and access (the first barrier also retires every wave's reads
-  // of the K/V tiles)
-  float4* fold = reinterpret_cast<float4*>(s_raw);
-  constexpr int PART_F4 = PART_F / 4;
-  for (int span = NW / 2; span >= 1; span >>= 1) {
-    __syncthreads();
-    if (wave >= span && wave < 2 * span) {
-      float4* dst = fold + (wave - span) * PART_F4;
+  // fold the 8 waves' partial sums by halving exchanges through LDS: at each
+  // of three levels a wave sends the half of its list of float4 groups that
+  // its partner (wave ^ 4, ^ 2, ^ 1) keeps and adds the partner's copy of the
+  // half it keeps, so that wave w ends with groups [w NF/8, (w+1) NF/8) fully
+  // summed.  Group f = (tensor, db, r4) holds items 4 r4 .. 4 r4 + 3 of
+  // (tensor ? dV^T : dK^T)[db].  The first barrier also retires every wave's
+  // reads of the K/V tiles and slices.
+  constexpr int NF = 2 * NDB * 4;
+  float4 f4[NF];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const floatx16& x = dkacc[db];
-          const floatx16& y = dvacc[db];
-          dst[((0 * NDB + db) * 4 + r4) * 64 + lane] =
-              make_float4(x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]);
-          dst[((1 * NDB + db) * 4 + r4) * 64 + lane] =
-              make_float4(y[4 * r4], y[4 * r4 + 1], y[4 * r4 + 2], y[4 * r4 + 3]);
-        }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f4[db * 4 + r4] = make_float4(dkacc[db][4 * r4], dkacc[db][4 * r4 + 1],
+                                    dkacc[db][4 * r4 + 2], dkacc[db][4 * r4 + 3]);
+      f4[(NDB + db) * 4 + r4] = make_float4(dvacc[db][4 * r4], dvacc[db][4 * r4 + 1],
+                                            dvacc[db][4 * r4 + 2], dvacc[db][4 * r4 + 3]);
     }
-    __syncthreads();
-    if (wave < span) {
-      const float4* src_ = fold + wave * PART_F4;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const float4 x = src_[((0 * NDB + db) * 4 + r4) * 64 + lane];
-          const float4 y = src_[((1 * NDB + db) * 4 + r4) * 64 + lane];
-          dkacc[db][4 * r4] += x.x; dkacc[db][4 * r4 + 1] += x.y;
-          dkacc[db][4 * r4 + 2] += x.z; dkacc[db][4 * r4 + 3] += x.w;
-          dvacc[db][4 * r4] += y.x; dvacc[db][4 * r4 + 1] += y.y;
-          dvacc[db][4 * r4 + 2] += y.z; dvacc[db][4 * r4 + 3] += y.w;
-        }
-    }
-  }
-  if (wave != 0) return;
+  float4* xch = reinterpret_cast<float4*>(s_raw);
+  static_assert(NW == 8, "three halving levels");
+  float4 f2[NF / 2], f3[NF / 4], f5[NF / 8];
+  fold_level<NF>(f4, f2, xch, wave, 4, lane, true);
+  fold_level<NF / 2>(f2, f3, xch, wave, 2, lane, true);
+  // this level's slots lie beyond the previous level's: no barrier first
+  fold_level<NF / 4>(f3, f5, xch + NW * (NF / 4) * 64, wave, 1, lane, false);
 
-  if (partial) {
-    // one of the two partial sums of this key tile: raw fp32 rows
-    // [dK^T keys 0..31 | dV^T keys 0..31] x D, added by the dq kernel that
-    // follows in the same backward call
+  // wave w stores groups f = w NF/8 + i
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = 32 * db + 8 * r4 + 4 * hi;
-        *reinterpret_cast<float4*>(pp + (size_t)lq * D + d) =
-            make_float4(dkacc[db][4 * r4], dkacc[db][4 * r4 + 1], dkacc[db][4 * r4 + 2],
-                        dkacc[db][4 * r4 + 3]);
-        *reinterpret_cast<float4*>(pp + (size_t)(32 + lq) * D + d) =
-            make_float4(dvacc[db][4 * r4], dvacc[db][4 * r4 + 1], dvacc[db][4 * r4 + 2],
-                        dvacc[db][4 * r4 + 3]);
-      }
-    }
-    return;
-  }
-  if (key_ok) {
-    __bf16* kp = dk + kv_base + (size_t)tk * D;
-    __bf16* vp = dv + kv_base + (size_t)tk * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x4 pk, pw;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pk[e] = (__bf16)(dkacc[db][4 * r4 + e] * a.scale);
-          pw[e] = (__bf16)(dvacc[db][4 * r4 + e]);
-        }
-        *reinterpret_cast<bf16x4*>(kp + 32 * db + 8 * r4 + 4 * hi) = pk;
-        *reinterpret_cast<bf16x4*>(vp + 32 * db + 8 * r4 + 4 * hi) = pw;
-      }
+  for (int i = 0; i < NF / 8; ++i) {
+    const int f = wave * (NF / 8) + i;
+    const int tensor = f / (4 * NDB), db = (f / 4) % NDB, r4 = f % 4;
+    const int d = 32 * db + 8 * r4 + 4 * hi;
+    const float4 x = f5[i];
+    if (partial) {
+      // raw fp32 rows [dK^T keys 0..31 | dV^T keys 0..31] x D, added by the
+      // dq kernel that follows in the same backward call
+      *reinterpret_cast<float4*>(pp + (size_t)(32 * tensor + lq) * D + d) = x;
+    } else if (key_ok) {
+      const float sc = tensor ? 1.f : a.scale;
+      const bf16x4 o4 = {(__bf16)(x.x * sc), (__bf16)(x.y * sc), (__bf16)(x.z * sc),
+                         (__bf16)(x.w * sc)};
+      *reinterpret_cast<bf16x4*>((tensor ? dv : dk) + kv_base + (size_t)tk * D + d) = o4;
     }
   }
 }
@@ -548,9 +555,9 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   constexpr int TILE_B = TQ * 2 * D;
   constexpr int SLICE_B = 2 * TILE_B + 256;
   constexpr int NW = 8;
-  constexpr int PART_F = 2 * NDB * 16 * 64;
+  constexpr int FOLD_B = NW * (2 * NDB * 4 / 2) * 64 * 16;  // first fold level's slots
   constexpr int STAGE_B = 2 * TILE_B + NW * SLICE_B;  // K, V tiles + wave slices
-  constexpr int LDS_BYTES = STAGE_B > 4 * PART_F * 4 ? STAGE_B : 4 * PART_F * 4;
+  constexpr int LDS_BYTES = STAGE_B > FOLD_B ? STAGE_B : FOLD_B;
   __shared__ __attribute__((aligned(1024))) unsigned char s_raw[LDS_BYTES];
 
   const int nkt = (a.L + 31) / 32;
@@ -560,11 +567,24 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   const int n = w % nbk;
   const int g = (w / nbk) % a.Hkv;
   const int b = w / (nbk * a.Hkv);
-  const DkdvItems it = dkdv_items(n, nkt, a.G);
-  float* pp = part_ws + ((size_t)((b * a.Hkv + g) * nph + it.p) * 2 + it.part) * 64 * D;
-  dkdv_item<D>(q, k, v, lse, dO, delta, dk, dv, pp, a, s_raw, b, g, it.p, it.a0, it.a1, true);
-  if (it.count == 2)
-    dkdv_item<D>(q, k, v, lse, dO, delta, dk, dv, pp, a, s_raw, b, g, it.mirror, 0, it.wl, false);
+  // block 2p: pairs [0, split) of tile p; block 2p+1: the rest of tile p,
+  // then the mirror tile (scalars only, nothing indexed at run time)
+  const int p = n >> 1, part = n & 1;
+  const int wh = a.G * (nkt - p);
+  const int wl = dkdv_mirror_pairs(p, nkt, a.G);
+  const int split = dkdv_split(wh, wl);
+  const bool tile_split = split < wh;
+  const bool rest_first = part == 1 && tile_split;
+  const int kt1 = (part == 0 || tile_split) ? p : nkt - 1 - p;
+  const int b1 = rest_first ? split : 0;
+  const int e1 = part == 0 ? split : (tile_split ? wh : wl);
+  const bool has2 = rest_first && wl > 0;
+  float* pp = part_ws + ((size_t)((b * a.Hkv + g) * nph + p) * 2 + part) * 64 * D;
+  if (e1 > b1)
+    dkdv_item<D>(q, k, v, lse, dO, delta, dk, dv, pp, a, s_raw, b, g, kt1, b1, e1,
+                 kt1 == p && tile_split);
+  if (has2)
+    dkdv_item<D>(q, k, v, lse, dO, delta, dk, dv, pp, a, s_raw, b, g, nkt - 1 - p, 0, wl, false);
 }
 
 

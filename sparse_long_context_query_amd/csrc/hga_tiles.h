@@ -90,6 +90,14 @@ struct KeySource {
   }
 };
 
+// Walk order of the key tiles of KeySource for a block whose two halves share
+// them out: the local tiles first (their rows are known before the selection
+// has been read, so the first copies can start at once), then the history
+// tiles; half h takes walk positions h, h + 2, h + 4, ...
+__device__ __forceinline__ int walk_tile(int wpos, int nloc, int n_hist_tiles) {
+  return wpos < nloc ? n_hist_tiles + wpos : wpos - nloc;
+}
+
 // Orders LDS traffic of one wave: its earlier LDS stores are visible to its
 // later LDS loads from any lane (no other wave involved).
 __device__ __forceinline__ void wave_lds_sync() {
