@@ -326,3 +326,63 @@ def gather_blocks(x: np.ndarray, sel: np.ndarray, hist_block: int) -> np.ndarray
                     if blk >= 0:
                         out[b, g, j, t] = x[b, g, blk * hist_block:(blk + 1) * hist_block]
     return out
+
+
+# --------------------------------------------------------------------------
+# Decode step ([JA] 深掘り分析: after training, inference runs over sequences
+# of up to 131,072 tokens while the resident block summaries grow; [JA]
+# 業界への影響 and [FR] Contexte: HGA as a module for retrieval and
+# generation).  The pages describe no decode procedure; the reading here is
+# the forward above applied to a query block made of the new tokens.
+# --------------------------------------------------------------------------
+def decode_step(q_new, k, v, shape, pos: int, scale: Optional[float] = None,
+                precision: str = "f64", kbar: Optional[np.ndarray] = None):
+    """One step for n new tokens at positions pos .. pos+n-1, all inside one
+    segment.  q_new [B,Hq,n,D]; k, v [B,Hkv,S,D] hold every token up to
+    pos+n-1.  Readings (pages silent):
+      * the new tokens form one query block of the segment that holds them,
+        t0 = floor(pos / L) * L; history = the whole blocks before t0;
+      * selection as for a segment's query block: qbar = mean of q_new over
+        the G heads of the group and the n tokens, score = qbar . kbar,
+        top-k by (score desc, index asc), ascending, -1 padded;
+      * token pos+i attends to the selected history tokens and the local
+        tokens t0 .. pos+i with one joint softmax.
+    Returns (sel [B,Hkv,k] int32, O [B,Hq,n,D], LSE [B,Hq,n])."""
+    B, Hq, n, D = q_new.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    L, Bh, kk = shape.seg_len, shape.hist_block, shape.top_k
+    t0 = (pos // L) * L
+    if n < 1 or (pos + n - 1) // L != pos // L:
+        raise ValueError("the new tokens must lie inside one segment")
+    nb = t0 // Bh
+    sc = softmax_scale(D, scale)
+    sel = np.full((B, Hkv, kk), -1, dtype=np.int32)
+    if nb > 0:
+        if kbar is None:
+            kbar = block_summaries(k[:, :, :t0], Bh)
+        qbar = _f64(q_new).reshape(B, Hkv, G, n, D).mean(axis=(2, 3))[:, :, None]
+        scores = block_scores(qbar, kbar, nb, precision)[:, :, 0]   # [B,Hkv,nb]
+        for b in range(B):
+            for g in range(Hkv):
+                sel[b, g] = topk_blocks(scores[b, g], kk)
+    O = np.zeros((B, Hq, n, D))
+    LSE = np.zeros((B, Hq, n))
+    qpos = pos + np.arange(n)
+    nloc = pos + n - t0
+    for b in range(B):
+        for g in range(Hkv):
+            blocks = sel[b, g][sel[b, g] >= 0]
+            hist = (blocks[:, None] * Bh + np.arange(Bh)[None, :]).reshape(-1)
+            keys = np.concatenate([hist, np.arange(t0, t0 + nloc)]).astype(np.int64)
+            vis = np.concatenate([np.ones((n, hist.size), dtype=bool),
+                                  np.arange(t0, t0 + nloc)[None, :] <= qpos[:, None]], axis=1)
+            Kset = _f64(k[b, g, keys])
+            Vset = _f64(v[b, g, keys])
+            Qg = _f64(q_new[b, g * G:(g + 1) * G])                 # [G,n,D]
+            Z = np.where(vis[None], sc * (Qg @ Kset.T), -np.inf)
+            m = Z.max(axis=-1, keepdims=True)
+            lse = m[..., 0] + np.log(np.exp(Z - m).sum(axis=-1))
+            O[b, g * G:(g + 1) * G] = np.exp(Z - lse[..., None]) @ Vset
+            LSE[b, g * G:(g + 1) * G] = lse
+    return sel, O, LSE
