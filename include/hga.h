@@ -160,9 +160,35 @@ int hga_segment_step(const hga_config* cfg, int32_t seg, int32_t flags,
                      float* lse, void* dq, void* dk, void* dv, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* Decode step for n new tokens at positions pos .. pos+n-1, all inside one
+ * segment (t0 = floor(pos/L)*L) ([JA] 深掘り分析: inference over up to
+ * 131,072 tokens with the resident summaries growing; [JA] 業界への影響 and
+ * [FR] Contexte: HGA as a module for retrieval and generation).  The pages
+ * give no decode procedure; the new tokens are read as one query block of
+ * their segment:
+ *   - if pos == t0 > 0, the L/Bh blocks of the previous segment are
+ *     summarized into summ first (as hga_segment_step does); summ rows
+ *     [0, t0/Bh) must otherwise be current;
+ *   - qbar = mean of q over the G heads of a group and the n tokens; the k
+ *     best history blocks before t0 by (score desc, index asc), or all of
+ *     them, are written ascending, -1 padded, to sel[b,g,:];
+ *   - token pos+i attends, with one softmax, to the selected history
+ *     tokens and the local tokens t0 .. pos+i.
+ * Layouts: q and o [B, Hq, n, D] (dtype of the config, dense), lse
+ * [B, Hq, n] float32 natural log (may be NULL), sel [B, Hkv, k] int32; k and
+ * v are the full [B, Hkv, S, D] caches holding every token up to pos+n-1.
+ * Requirements: 0 <= pos, n >= 1, pos+n <= S, the n tokens in one segment
+ * (else HGA_ERR_ARG); G*n <= 64 (else HGA_ERR_UNSUPPORTED).  ws:
+ * hga_workspace_size(cfg, HGA_OP_DECODE) bytes of scratch (per-chunk
+ * partial sums, combined in a fixed order: results are deterministic);
+ * calls sharing a workspace must not overlap. */
+int hga_decode_step(const hga_config* cfg, int32_t pos, int32_t n, const void* q,
+                    const void* k, const void* v, float* summ, int32_t* sel, void* o,
+                    float* lse, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for an operation (0 if none is needed), or 0 with
  * hga_last_error() set if the config is invalid. */
-enum { HGA_OP_FWD = 0, HGA_OP_BWD = 1, HGA_OP_STEP = 2 };
+enum { HGA_OP_FWD = 0, HGA_OP_BWD = 1, HGA_OP_STEP = 2, HGA_OP_DECODE = 3 };
 size_t hga_workspace_size(const hga_config* cfg, int32_t op);
 
 /* Message of the last failure on this thread ("" if none). */
@@ -186,7 +212,9 @@ enum {
   HGA_K_BWD_PRE = 4,
   HGA_K_BWD_DQ = 5,
   HGA_K_BWD_DKDV = 6,
-  HGA_KCLASS_COUNT = 7
+  HGA_K_DECODE = 7,
+  HGA_K_DECODE_MERGE = 8,
+  HGA_KCLASS_COUNT = 9
 };
 int hga_profile_begin(uint32_t mask);
 int hga_profile_end(double* ms, int64_t* count);

@@ -27,8 +27,9 @@ HGA_ERR_HIP = -4
 HGA_F32 = 0
 HGA_BF16 = 1
 HGA_STEP_BWD = 1
-HGA_OP_FWD, HGA_OP_BWD, HGA_OP_STEP = 0, 1, 2
-KERNEL_CLASSES = ("summarize", "select", "gather", "fwd", "bwd_pre", "bwd_dq", "bwd_dkdv")
+HGA_OP_FWD, HGA_OP_BWD, HGA_OP_STEP, HGA_OP_DECODE = 0, 1, 2, 3
+KERNEL_CLASSES = ("summarize", "select", "gather", "fwd", "bwd_pre", "bwd_dq", "bwd_dkdv",
+                  "decode", "decode_merge")
 
 
 class HGAError(RuntimeError):
@@ -77,6 +78,8 @@ _SIGNATURES = {
                                     _P, _P, ctypes.c_size_t, _P]),
     "hga_segment_step": (ctypes.c_int, [_CP, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P,
                                         _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "hga_decode_step": (ctypes.c_int, [_CP, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P,
+                                       _P, _P, _P, ctypes.c_size_t, _P]),
     "hga_workspace_size": (ctypes.c_size_t, [_CP, ctypes.c_int32]),
     "hga_last_error": (ctypes.c_char_p, []),
     "hga_version": (ctypes.c_char_p, []),
@@ -228,6 +231,30 @@ def segment_step(cfg: Config, seg: int, q, k, v, summ, sel, o, lse=None, do=None
         _ptr(dv, "dv", s.dt, s.kv, allow_none=not bwd),
         _ptr(ws, "ws", allow_none=not bwd),
         0 if ws is None else ws.numel() * ws.element_size(), _stream()))
+
+
+def decode_step(cfg: Config, pos: int, q_new, k, v, summ, sel, o, lse=None, ws=None) -> None:
+    """n = q_new.shape[2] new tokens at positions pos .. pos+n-1 (one
+    segment): q_new and o [B, Hq, n, D], sel [B, Hkv, k] int32, lse
+    [B, Hq, n] float32 or None; k, v the full caches.  ws defaults to a fresh
+    buffer of workspace_size(cfg, HGA_OP_DECODE) bytes."""
+    s = Shapes(cfg)
+    torch = _torch()
+    if q_new.dim() != 4:
+        raise ValueError("q_new must be [B, Hq, n, D]")
+    n = int(q_new.shape[2])
+    B, Hq, Hkv, D = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    if ws is None:
+        ws = torch.empty(max(workspace_size(cfg, HGA_OP_DECODE), 256), dtype=torch.uint8,
+                         device=q_new.device)
+    _check(lib().hga_decode_step(
+        ctypes.byref(cfg), pos, n, _ptr(q_new, "q_new", s.dt, (B, Hq, n, D)),
+        _ptr(k, "k", s.dt, s.kv), _ptr(v, "v", s.dt, s.kv),
+        _ptr(summ, "summ", torch.float32, s.summ),
+        _ptr(sel, "sel", torch.int32, (B, Hkv, cfg.top_k)),
+        _ptr(o, "o", s.dt, (B, Hq, n, D)),
+        _ptr(lse, "lse", torch.float32, (B, Hq, n), allow_none=True),
+        _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream()))
 
 
 def profile_begin(classes=None) -> None:

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhga.so")
-SOURCES = ["hga_api.cpp", "hga_select.hip", "hga_fwd.hip", "hga_bwd.hip"]
+SOURCES = ["hga_api.cpp", "hga_select.hip", "hga_fwd.hip", "hga_bwd.hip", "hga_decode.hip"]
 
 
 def hipcc() -> str:

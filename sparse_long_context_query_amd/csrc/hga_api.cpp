@@ -165,6 +165,9 @@ size_t hga_workspace_size(const hga_config* cfg, int32_t op) {
     case HGA_OP_STEP:
       ok();
       return hga::bwd_workspace_bytes(p);
+    case HGA_OP_DECODE:
+      ok();
+      return hga::decode_workspace_bytes(p);
     default:
       fail(HGA_ERR_ARG, "unknown op %d", op);
       return 0;
@@ -311,6 +314,46 @@ int hga_segment_step(const hga_config* cfg, int32_t seg, int32_t flags, const vo
     e = hga::launch_bwd(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, (float*)ws, st, fuse);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
   }
+  return ok();
+}
+
+int hga_decode_step(const hga_config* cfg, int32_t pos, int32_t n, const void* q,
+                    const void* k, const void* v, float* summ, int32_t* sel, void* o,
+                    float* lse, void* ws, size_t ws_bytes, void* stream) {
+  hga::Prob p;
+  int rc = make_prob(cfg, &p);
+  if (rc) return rc;
+  if (n < 1 || pos < 0 || (int64_t)pos + n > p.S)
+    return fail(HGA_ERR_ARG, "tokens [%d, %d + %d) outside [0, %d)", pos, pos, n, p.S);
+  if (pos / p.L != (pos + n - 1) / p.L)
+    return fail(HGA_ERR_ARG, "tokens [%d, %d) cross a segment boundary (seg_len %d)", pos,
+                pos + n, p.L);
+  if (p.G * n > hga::decode_max_rows())
+    return fail(HGA_ERR_UNSUPPORTED, "G*n = %d exceeds %d query rows per KV head", p.G * n,
+                hga::decode_max_rows());
+  HGA_REQUIRE(q);
+  HGA_REQUIRE(k);
+  HGA_REQUIRE(v);
+  HGA_REQUIRE(summ);
+  HGA_REQUIRE(sel);
+  HGA_REQUIRE(o);
+  HGA_REQUIRE(ws);
+  const size_t need = hga::decode_workspace_bytes(p);
+  if (ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  const int t0 = pos / p.L * p.L;
+  hipError_t e;
+  if (pos == t0 && t0 > 0) {
+    // the first tokens of a segment: the previous segment's blocks become history
+    e = hga::launch_summarize(p, k, (t0 - p.L) / p.Bh, t0 / p.Bh, summ, st);
+    if (e != hipSuccess) return hip_fail(e, "summarize launch");
+  }
+  e = hga::launch_select_decode(p, q, n, t0, summ, sel, st);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  e = hga::launch_decode(p, pos, n, q, k, v, sel, o, lse, (float*)ws, st);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }
 

@@ -1,0 +1,290 @@
+// Decode step of HGA for gfx950: attention of a few new tokens over the
+// history blocks selected for them and the causal local part of their
+// segment.
+//
+// [JA] 深掘り分析: after training, inference runs over sequences of up to
+// 131,072 tokens while the resident block summaries grow; [JA] 業界への影響
+// and [FR] Contexte: HGA as a module that speeds up retrieval and
+// generation.  The pages give no decode procedure.  Reading: the n new
+// tokens (positions pos .. pos+n-1, inside one segment starting at t0) form
+// one query block of that segment: one selection per (sequence, KV head)
+// from the mean of their queries over the G heads, then one joint softmax
+// over the selected history tokens and the local tokens t0 .. pos+i.
+//
+// Work split (split over keys): per (sequence, KV head) the step's key list
+// -- the selected history tokens in ascending order, then the local tokens
+// t0 .. pos+n-1 -- is cut into chunks of 64 keys.  One wave per (chunk, KV
+// head, sequence) stages the chunk's K and V rows in LDS (coalesced 16-byte
+// loads, each row read once) and, for the R = G*n query rows of the group,
+// writes the chunk's max, sum of exponentials and unnormalised P.V (fp32)
+// to the workspace.  A merge kernel then combines the chunks of every row in
+// chunk order (deterministic) into o and lse.  With a handful of query rows
+// against thousands of keys the step is bound by HBM, not by arithmetic, so
+// it runs on the vector ALU; MFMA tiles would sit mostly empty.
+#include <hip/hip_runtime.h>
+
+#include "hga_internal.h"
+
+namespace hga {
+namespace {
+
+constexpr int kCK = 64;     // keys per chunk (one per lane)
+constexpr int kMaxRows = 64;  // G * n limit
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct DecArgs {
+  int S, Bh, Hq, Hkv, G, n, pos, t0, K;
+  int nht;    // selected history tokens (k_eff * Bh)
+  int nch_h;  // history chunks
+  int nc;     // chunks in all
+  float c2;   // softmax scale * log2(e)
+};
+
+template <typename T> struct Elt;
+template <> struct Elt<__bf16> {
+  __device__ __forceinline__ static float get(const __bf16* p, int i) { return (float)p[i]; }
+};
+template <> struct Elt<float> {
+  __device__ __forceinline__ static float get(const float* p, int i) { return p[i]; }
+};
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// LDS layout of one wave (dynamic): q rows [R][D] f32, K rows [kCK][D + pad]
+// (the 16-byte pad per row makes the lane-per-key reads conflict-free),
+// V rows [kCK][D], then P [R][kCK] f32.
+template <typename T, int D>
+struct DecLds {
+  static constexpr int EPP = 16 / sizeof(T);  // elements per 16-byte piece
+  static constexpr int KP = D + EPP;          // K row pitch in elements
+  static size_t bytes(int R) {
+    return (size_t)R * D * 4 + (size_t)kCK * KP * sizeof(T) + (size_t)kCK * D * sizeof(T) +
+           (size_t)R * kCK * 4;
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_attn_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ sel, float* __restrict__ part_o, float* __restrict__ part_ml,
+    DecArgs a) {
+  using Lay = DecLds<T, D>;
+  constexpr int EPP = Lay::EPP, KP = Lay::KP;
+  constexpr int CPR = D / EPP;  // 16-byte pieces per row
+  constexpr int ND = D / 64;    // output columns per lane
+  extern __shared__ float4 dyn_lds[];
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int R = a.G * a.n;
+  float* qs = reinterpret_cast<float*>(dyn_lds);
+  T* ks = reinterpret_cast<T*>(qs + (size_t)R * D);
+  T* vs = ks + kCK * KP;
+  float* ps = reinterpret_cast<float*>(vs + kCK * D);
+
+  // token of key `lane` of this chunk; rows that hold no key read a valid
+  // row (masked below)
+  int tok;
+  bool valid;
+  bool local;
+  if (c < a.nch_h) {
+    const int hp = c * kCK + lane;
+    valid = hp < a.nht;
+    local = false;
+    tok = valid ? sel[(size_t)(b * a.Hkv + g) * a.K + hp / a.Bh] * a.Bh + hp % a.Bh : 0;
+  } else {
+    tok = a.t0 + (c - a.nch_h) * kCK + lane;
+    valid = tok < a.pos + a.n;
+    local = true;
+    if (!valid) tok = a.t0;
+  }
+
+  // stage K and V rows (16-byte pieces, consecutive lanes on consecutive
+  // pieces of a row) and the group's query rows
+  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S;
+  for (int idx = lane; idx < kCK * CPR; idx += 64) {
+    const int r = idx / CPR, pc = idx % CPR;
+    const int tr = __shfl(tok, r, 64);
+    const size_t src = (kv_base + tr) * D + pc * EPP;
+    *reinterpret_cast<uint4*>(ks + r * KP + pc * EPP) = *reinterpret_cast<const uint4*>(k + src);
+    *reinterpret_cast<uint4*>(vs + r * D + pc * EPP) = *reinterpret_cast<const uint4*>(v + src);
+  }
+  for (int idx = lane; idx < R * D; idx += 64) {
+    const int r = idx / D, d = idx % D;
+    const int hh = r / a.n, i = r % a.n;
+    qs[idx] = Elt<T>::get(q, (int)(((size_t)(b * a.Hq + g * a.G + hh) * a.n + i) * D + d));
+  }
+  __syncthreads();
+
+  // scores in log2 units, one key per lane; then per row the chunk max,
+  // exponentials and their sum
+  float krow[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) krow[d] = Elt<T>::get(ks + lane * KP, d);
+  float* ml = part_ml + ((size_t)(b * a.Hkv + g) * a.nc + c) * kMaxRows * 2;
+  for (int r = 0; r < R; ++r) {
+    const float* qr = qs + (size_t)r * D;
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; d += 4) {
+      const float4 q4 = *reinterpret_cast<const float4*>(qr + d);
+      s += q4.x * krow[d] + q4.y * krow[d + 1] + q4.z * krow[d + 2] + q4.w * krow[d + 3];
+    }
+    const int i = r % a.n;
+    const bool vis = valid && (!local || tok <= a.pos + i);
+    const float z = vis ? s * a.c2 : -INFINITY;
+    const float m = wave_max(z);
+    const float p = vis ? exp2f(z - m) : 0.f;
+    const float l = wave_sum(p);
+    ps[r * kCK + lane] = p;
+    if (lane == 0) {
+      ml[2 * r] = m;
+      ml[2 * r + 1] = l;
+    }
+  }
+  __syncthreads();
+
+  // unnormalised P.V: lane owns columns lane + 64 e
+  float vcol[ND][kCK];
+#pragma unroll
+  for (int e = 0; e < ND; ++e)
+#pragma unroll
+    for (int kk = 0; kk < kCK; ++kk) vcol[e][kk] = Elt<T>::get(vs + kk * D, lane + 64 * e);
+  float* po = part_o + ((size_t)(b * a.Hkv + g) * a.nc + c) * kMaxRows * D;
+  for (int r = 0; r < R; ++r) {
+    float acc[ND];
+#pragma unroll
+    for (int e = 0; e < ND; ++e) acc[e] = 0.f;
+    const float* pr = ps + r * kCK;
+#pragma unroll
+    for (int kk = 0; kk < kCK; kk += 4) {
+      const float4 p4 = *reinterpret_cast<const float4*>(pr + kk);
+#pragma unroll
+      for (int e = 0; e < ND; ++e)
+        acc[e] += p4.x * vcol[e][kk] + p4.y * vcol[e][kk + 1] + p4.z * vcol[e][kk + 2] +
+                  p4.w * vcol[e][kk + 3];
+    }
+#pragma unroll
+    for (int e = 0; e < ND; ++e) po[(size_t)r * D + lane + 64 * e] = acc[e];
+  }
+}
+
+// One wave per (query row, KV head, sequence): combines the chunks in
+// order.  With M = max_c m_c: l = sum_c l_c 2^(m_c - M),
+// o = sum_c O_c 2^(m_c - M) / l, lse = (M + log2 l) ln 2.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, T* __restrict__ o,
+    float* __restrict__ lse, DecArgs a) {
+  constexpr int ND = D / 64;
+  const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const size_t base = (size_t)(b * a.Hkv + g) * a.nc;
+  float M = -INFINITY;
+  for (int c = 0; c < a.nc; ++c) M = fmaxf(M, part_ml[((base + c) * kMaxRows + r) * 2]);
+  float l = 0.f, acc[ND];
+#pragma unroll
+  for (int e = 0; e < ND; ++e) acc[e] = 0.f;
+  for (int c = 0; c < a.nc; ++c) {
+    const float* ml = part_ml + ((base + c) * kMaxRows + r) * 2;
+    if (!(ml[1] > 0.f)) continue;  // no visible key of this row in chunk c
+    const float f = exp2f(ml[0] - M);
+    l += ml[1] * f;
+    const float* po = part_o + ((base + c) * kMaxRows + r) * D;
+#pragma unroll
+    for (int e = 0; e < ND; ++e) acc[e] += po[lane + 64 * e] * f;
+  }
+  const int hh = r / a.n, i = r % a.n;
+  const size_t orow = (size_t)(b * a.Hq + g * a.G + hh) * a.n + i;
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int e = 0; e < ND; ++e) o[orow * D + lane + 64 * e] = (T)(acc[e] * inv);
+  if (lse != nullptr && lane == 0) lse[orow] = (M + log2f(l)) * kLn2;
+}
+
+struct DecPlan {
+  DecArgs a;
+  int R;
+};
+
+DecPlan plan(const Prob& p, int pos, int n) {
+  DecPlan d;
+  DecArgs& a = d.a;
+  a.S = p.S;
+  a.Bh = p.Bh;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.G = p.G;
+  a.n = n;
+  a.pos = pos;
+  a.t0 = pos / p.L * p.L;
+  a.K = p.K;
+  const int nb = a.t0 / p.Bh;
+  a.nht = (nb < p.K ? nb : p.K) * p.Bh;
+  a.nch_h = (a.nht + kCK - 1) / kCK;
+  a.nc = a.nch_h + (pos + n - a.t0 + kCK - 1) / kCK;
+  a.c2 = p.scale * kLog2e;
+  d.R = p.G * n;
+  return d;
+}
+
+int max_chunks(const Prob& p) {
+  const int nb_max = (p.S - p.L) / p.Bh;  // history blocks of the last segment
+  const int nht = (nb_max < p.K ? nb_max : p.K) * p.Bh;
+  return (nht + kCK - 1) / kCK + (p.L + kCK - 1) / kCK;
+}
+
+template <typename T, int D>
+hipError_t decode_t(const Prob& p, int pos, int n, const void* q_new, const void* k,
+                    const void* v, const int32_t* sel, void* o, float* lse, float* ws,
+                    hipStream_t st) {
+  const DecPlan d = plan(p, pos, n);
+  float* part_o = ws;
+  float* part_ml = ws + (size_t)p.B * p.Hkv * max_chunks(p) * kMaxRows * p.D;
+  const size_t shm = DecLds<T, D>::bytes(d.R);
+  if (shm > 32768) {
+    hipError_t e = hipFuncSetAttribute((const void*)decode_attn_kernel<T, D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+  }
+  {
+    ProfScope ps(HGA_K_DECODE, st);
+    hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3(d.a.nc, p.Hkv, p.B), dim3(64), shm, st,
+                       (const T*)q_new, (const T*)k, (const T*)v, sel, part_o, part_ml, d.a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  ProfScope ps(HGA_K_DECODE_MERGE, st);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(d.R, p.Hkv, p.B), dim3(64), 0, st,
+                     (const float*)part_o, (const float*)part_ml, (T*)o, lse, d.a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int decode_max_rows() { return kMaxRows; }
+
+size_t decode_workspace_bytes(const Prob& p) {
+  return (size_t)p.B * p.Hkv * max_chunks(p) * kMaxRows * (p.D + 2) * sizeof(float);
+}
+
+hipError_t launch_decode(const Prob& p, int pos, int n, const void* q_new, const void* k,
+                         const void* v, const int32_t* sel, void* o, float* lse, float* ws,
+                         hipStream_t st) {
+  if (p.dtype == HGA_BF16)
+    return p.D == 64 ? decode_t<__bf16, 64>(p, pos, n, q_new, k, v, sel, o, lse, ws, st)
+                     : decode_t<__bf16, 128>(p, pos, n, q_new, k, v, sel, o, lse, ws, st);
+  return p.D == 64 ? decode_t<float, 64>(p, pos, n, q_new, k, v, sel, o, lse, ws, st)
+                   : decode_t<float, 128>(p, pos, n, q_new, k, v, sel, o, lse, ws, st);
+}
+
+}  // namespace hga

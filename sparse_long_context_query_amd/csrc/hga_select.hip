@@ -16,6 +16,17 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Where the query rows of selection unit j are and where its k indices go:
+// q rows qS*(b*Hq + h) + q0 + j*qstep + [0, nrows) (q holds qS rows per
+// head), output row out_units*(b*Hkv + g) + out_j0 + j of sel, nb candidate
+// blocks.  A segment's unit is a query block; a decode step's single unit is
+// its new tokens.
+struct SelGeom {
+  int qS, q0, qstep, nrows;
+  int out_units, out_j0;
+  int nb;
+};
+
 // ---------------------------------------------------------------------------
 // a1: summ[b,g,i,:] = mean of the Bh keys of block i.
 // One block of threads per (history block, KV head, sequence).  Threads read
@@ -111,10 +122,11 @@ __device__ __forceinline__ uint32_t wave_kth_largest32(const uint32_t (&v)[E], i
 }
 
 // ---------------------------------------------------------------------------
-// a2 + a3: one block of threads per (query block j, KV head g, sequence b).
-//   1. qbar = mean of q over the G heads of the group and the Bq tokens of
-//      the block (float32; every row load of a thread in flight at once,
-//      then an LDS fold); the summary row of each thread's first candidate
+// a2 + a3: one block of threads per (unit j, KV head g, sequence b); a unit
+// is a query block of a segment, or the new tokens of a decode step.
+//   1. qbar = mean of q over the G heads of the group and the unit's rows
+//      (float32; every row load of a thread in flight at once, then an LDS
+//      fold); the summary row of each thread's first candidate
 //      is requested before the q rows so that both round trips overlap;
 //   2. score_i = qbar . summ_i (unscaled), one candidate per thread, qbar
 //      broadcast from LDS;
@@ -131,8 +143,7 @@ __device__ __forceinline__ uint32_t wave_kth_largest32(const uint32_t (&v)[E], i
 template <typename T, int D, int E>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const T* __restrict__ q, const float* __restrict__ summ,
-    int32_t* __restrict__ sel, int S, int L, int Bq, int Bh, int K, int Hq,
-    int Hkv, int G, int nqb_all, int nblk, int seg) {
+    int32_t* __restrict__ sel, SelGeom geo, int K, int Hq, int Hkv, int G, int nblk) {
   constexpr int EL = Vec16<T>::N;
   constexpr int C = D / EL;
   constexpr int R = kThreads / C;
@@ -143,10 +154,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   __shared__ unsigned long long s_thresh;
 
   const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int t0 = seg * L;
-  const int nb = t0 / Bh;
-  const int nqb = L / Bq;
-  int32_t* out = sel + ((size_t)(b * Hkv + g) * nqb_all + (size_t)seg * nqb + j) * K;
+  const int nb = geo.nb;
+  int32_t* out = sel + ((size_t)(b * Hkv + g) * geo.out_units + geo.out_j0 + j) * K;
 
   if (nb <= K) {  // every history block is taken (none at seg 0)
     for (int t = threadIdx.x; t < K; t += kThreads) out[t] = (t < nb) ? t : -1;
@@ -170,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     float acc[EL];
 #pragma unroll
     for (int e = 0; e < EL; ++e) acc[e] = 0.f;
-    const int rows = G * Bq;
+    const int rows = G * geo.nrows;
     constexpr int U = 16;  // row loads in flight per thread (raw 16-byte vectors)
     for (int row0 = r; row0 < rows; row0 += U * R) {
       uint4 f[U];
@@ -178,9 +187,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       for (int u = 0; u < U; ++u) {
         const int row = row0 + u * R;
         if (row < rows) {
-          const int hh = row / Bq, tt = row % Bq;
+          const int hh = row / geo.nrows, tt = row % geo.nrows;
           f[u] = *reinterpret_cast<const uint4*>(
-              q + ((size_t)(b * Hq + g * G + hh) * S + t0 + j * Bq + tt) * D + c * EL);
+              q + ((size_t)(b * Hq + g * G + hh) * geo.qS + geo.q0 + j * geo.qstep + tt) * D +
+              c * EL);
         } else {
           f[u] = make_uint4(0, 0, 0, 0);
         }
@@ -342,35 +352,45 @@ hipError_t summarize_t(const Prob& p, const void* k, int b0, int b1, float* summ
 }
 
 template <typename T, int D, int E>
-hipError_t select_launch(const Prob& p, const void* q, const float* summ, int seg, int32_t* sel,
-                         size_t shm, hipStream_t st) {
+hipError_t select_launch(const Prob& p, const void* q, const float* summ, const SelGeom& geo,
+                         int units, int32_t* sel, size_t shm, hipStream_t st) {
   if (shm > 32768) {  // large candidate sets need more than the default LDS cap
     hipError_t e = hipFuncSetAttribute((const void*)select_kernel<T, D, E>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)(kMaxCandidates * sizeof(unsigned long long)));
     if (e != hipSuccess) return e;
   }
-  dim3 grid(p.nqb, p.Hkv, p.B);
+  dim3 grid(units, p.Hkv, p.B);
   ProfScope ps(HGA_K_SELECT, st);
   hipLaunchKernelGGL((select_kernel<T, D, E>), grid, dim3(kThreads), shm, st, (const T*)q, summ,
-                     sel, p.S, p.L, p.Bq, p.Bh, p.K, p.Hq, p.Hkv, p.G, p.nqb_all, p.nblk, seg);
+                     sel, geo, p.K, p.Hq, p.Hkv, p.G, p.nblk);
   return hipGetLastError();
 }
 
 // Register search for up to 1024 candidates (E = 1..16 keys per lane), LDS
 // sort beyond.
 template <typename T, int D>
-hipError_t select_t(const Prob& p, const void* q, const float* summ, int seg, int32_t* sel,
-                    hipStream_t st) {
-  const int nb = seg * p.L / p.Bh;
+hipError_t select_t(const Prob& p, const void* q, const float* summ, const SelGeom& geo,
+                    int units, int32_t* sel, hipStream_t st) {
+  const int nb = geo.nb;
   int W = 64;
   while (W < nb) W <<= 1;
-  if (nb <= p.K || W <= 64) return select_launch<T, D, 1>(p, q, summ, seg, sel, 0, st);
-  if (W <= 128) return select_launch<T, D, 2>(p, q, summ, seg, sel, 0, st);
-  if (W <= 256) return select_launch<T, D, 4>(p, q, summ, seg, sel, 0, st);
-  if (W <= 512) return select_launch<T, D, 8>(p, q, summ, seg, sel, 0, st);
-  if (W <= 1024) return select_launch<T, D, 16>(p, q, summ, seg, sel, 0, st);
-  return select_launch<T, D, 0>(p, q, summ, seg, sel, (size_t)W * sizeof(unsigned long long), st);
+  if (nb <= p.K || W <= 64) return select_launch<T, D, 1>(p, q, summ, geo, units, sel, 0, st);
+  if (W <= 128) return select_launch<T, D, 2>(p, q, summ, geo, units, sel, 0, st);
+  if (W <= 256) return select_launch<T, D, 4>(p, q, summ, geo, units, sel, 0, st);
+  if (W <= 512) return select_launch<T, D, 8>(p, q, summ, geo, units, sel, 0, st);
+  if (W <= 1024) return select_launch<T, D, 16>(p, q, summ, geo, units, sel, 0, st);
+  return select_launch<T, D, 0>(p, q, summ, geo, units, sel,
+                                (size_t)W * sizeof(unsigned long long), st);
+}
+
+hipError_t select_any(const Prob& p, const void* q, const float* summ, const SelGeom& geo,
+                      int units, int32_t* sel, hipStream_t st) {
+  if (p.dtype == HGA_BF16)
+    return p.D == 64 ? select_t<__bf16, 64>(p, q, summ, geo, units, sel, st)
+                     : select_t<__bf16, 128>(p, q, summ, geo, units, sel, st);
+  return p.D == 64 ? select_t<float, 64>(p, q, summ, geo, units, sel, st)
+                   : select_t<float, 128>(p, q, summ, geo, units, sel, st);
 }
 
 }  // namespace
@@ -387,11 +407,17 @@ hipError_t launch_summarize(const Prob& p, const void* k, int b0, int b1, float*
 
 hipError_t launch_select(const Prob& p, const void* q, const float* summ, int seg,
                          int32_t* sel, hipStream_t st) {
-  if (p.dtype == HGA_BF16)
-    return p.D == 64 ? select_t<__bf16, 64>(p, q, summ, seg, sel, st)
-                     : select_t<__bf16, 128>(p, q, summ, seg, sel, st);
-  return p.D == 64 ? select_t<float, 64>(p, q, summ, seg, sel, st)
-                   : select_t<float, 128>(p, q, summ, seg, sel, st);
+  // unit j = query block j of the segment, rows [t0 + j Bq, t0 + (j+1) Bq)
+  const int t0 = seg * p.L;
+  const SelGeom geo{p.S, t0, p.Bq, p.Bq, p.nqb_all, seg * p.nqb, t0 / p.Bh};
+  return select_any(p, q, summ, geo, p.nqb, sel, st);
+}
+
+hipError_t launch_select_decode(const Prob& p, const void* q_new, int n, int t0,
+                                const float* summ, int32_t* sel, hipStream_t st) {
+  // one unit: the n new tokens of q_new [B, Hq, n, D]; sel is [B, Hkv, k]
+  const SelGeom geo{n, 0, 0, n, 1, 0, t0 / p.Bh};
+  return select_any(p, q_new, summ, geo, 1, sel, st);
 }
 
 hipError_t launch_gather(const Prob& p, const void* k, const void* v, const int32_t* sel,

@@ -151,3 +151,23 @@ def test_binding_rejects_cpu_tensors(L):
 
 def test_version(L):
     assert "gfx950" in hga.version()
+
+
+def test_decode_step_validation(L):
+    cfg = good_cfg()  # S 16384, L 1024, G 4
+    ws = L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_DECODE)
+    # per (b, g): 32 history chunks (k 32 x Bh 64 / 64) + 16 local chunks of
+    # 64 keys, 64 query rows each, D + 2 floats per row
+    assert ws == 1 * 8 * (32 + 16) * 64 * (128 + 2) * 4
+
+    def call(pos, n, ws_bytes=ws, sel=FAKE):
+        return L.hga_decode_step(ctypes.byref(cfg), pos, n, FAKE, FAKE, FAKE, FAKE, sel, FAKE,
+                                 None, FAKE, ws_bytes, None)
+
+    assert call(-1, 1) == hga.HGA_ERR_ARG and "outside" in hga.last_error()
+    assert call(16383, 2) == hga.HGA_ERR_ARG and "outside" in hga.last_error()
+    assert call(5, 0) == hga.HGA_ERR_ARG
+    assert call(1020, 8) == hga.HGA_ERR_ARG and "segment boundary" in hga.last_error()
+    assert call(0, 17) == hga.HGA_ERR_UNSUPPORTED and "G*n" in hga.last_error()
+    assert call(2048, 4, sel=None) == hga.HGA_ERR_ARG and "sel is NULL" in hga.last_error()
+    assert call(2048, 4, ws_bytes=ws - 1) == hga.HGA_ERR_WORKSPACE
