@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--dense-sdpa", action="store_true",
                     help="also time torch SDPA (flash backend) dense causal fwd+bwd")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-step timing at the 131,072-token inference shape")
+    ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size "
                          "reference for HBM byte counters)")
@@ -157,6 +160,83 @@ def timed_passes(buf, dev, bwd, n, profile_classes=None):
     torch.cuda.synchronize()
     prof = hga.profile_end() if profile_classes else None
     return start.elapsed_time(end) / n, prof
+
+
+def decode_bench(n_steps, news=(1, 16)):
+    """Decode steps (hga_decode_step) at the 131,072-token inference shape:
+    B 1, 32 query / 8 KV heads, D 128, segments of 1,024, blocks of 128,
+    top-k 16, bf16.  The steps lie in the last segment, whose history is the
+    1,016 summarized blocks before it; positions are spread evenly over the
+    segment so that the local part averages half a segment.  Inputs are
+    N(0,1) drawn on the GPU: a step's work is fixed by the shapes (k*Bh
+    history keys plus the local keys), not by which blocks win.  Reports
+    microseconds per step and, for the attention kernel, algorithmic HBM
+    bytes (K/V rows of the key set, the query rows, the chunk partial sums
+    written) over its measured time against the 8 TB/s peak."""
+    import torch
+    import sparse_long_context_query_amd as hga
+    from synth import WORKLOADS
+    shape = WORKLOADS["infer_131k"]
+    cfg = hga.Config.from_shape(shape)
+    B, S, L, Bh, K = shape.batch, shape.seq_len, shape.seg_len, shape.hist_block, shape.top_k
+    Hq, Hkv, D = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    G = Hq // Hkv
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    kv = (B, Hkv, S, D)
+    k = torch.randn(kv, generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn(kv, generator=gen, device="cuda").to(torch.bfloat16)
+    qseg = torch.randn((B, Hq, L, D), generator=gen, device="cuda").to(torch.bfloat16)
+    t0 = S - L
+    s = hga.Shapes(cfg)
+    summ = torch.zeros(s.summ, dtype=torch.float32, device="cuda")
+    hga.summarize(cfg, k, 0, t0 // Bh, summ)
+    sel = torch.empty((B, Hkv, K), dtype=torch.int32, device="cuda")
+    ws = torch.empty(hga.workspace_size(cfg, hga.HGA_OP_DECODE), dtype=torch.uint8, device="cuda")
+    nht = min(K, t0 // Bh) * Bh
+    res = {"workload": "infer_131k decode (last segment, history 1,016 blocks)",
+           "data": "synthetic N(0,1) drawn on the GPU"}
+    for n in news:
+        steps = min(n_steps, (L - 1) // n)
+        stride = (L - 1 - n) // max(steps - 1, 1)
+        pos = [t0 + 1 + i * stride for i in range(steps)]
+        qs = [qseg[:, :, p - t0:p - t0 + n].contiguous() for p in pos]
+        o = torch.empty((B, Hq, n, D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, Hq, n), dtype=torch.float32, device="cuda")
+        for i in range(3):
+            hga.decode_step(cfg, pos[i], qs[i], k, v, summ, sel, o, lse, ws)
+        torch.cuda.synchronize()
+        # whole steps, timed with events around the loop
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        for p, q in zip(pos, qs):
+            hga.decode_step(cfg, p, q, k, v, summ, sel, o, lse, ws)
+        en.record()
+        torch.cuda.synchronize()
+        step_ms = st.elapsed_time(en) / steps
+        # per-kernel times in a second loop (events around each launch)
+        hga.profile_begin(["select", "decode", "decode_merge"])
+        for p, q in zip(pos, qs):
+            hga.decode_step(cfg, p, q, k, v, summ, sel, o, lse, ws)
+        prof = hga.profile_end()
+        R = G * n
+        nbytes = 0
+        for p in pos:
+            nloc = p + n - t0
+            nc = -(-nht // 64) + -(-nloc // 64)
+            nbytes += B * Hkv * ((nht + nloc) * D * 2 * 2 + R * D * 2 + nc * R * (D + 2) * 4)
+        attn_ms = prof["decode"][0]
+        gbs = nbytes / (attn_ms * 1e-3) / 1e9
+        res[f"n{n}"] = {
+            "steps": steps, "us_per_step": round(step_ms * 1e3, 2),
+            "tokens_per_s": round(B * n / (step_ms * 1e-3), 1),
+            "kernel_us_per_step": {c: round(prof[c][0] * 1e3 / prof[c][1], 2)
+                                   for c in ("select", "decode", "decode_merge") if prof[c][1]},
+            "attn_bytes_per_step": int(nbytes / steps),
+            "attn_hbm_gbs": round(gbs, 1), "attn_frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        }
+        log(f"[bench] decode n={n}: {res[f'n{n}']}")
+    del k, v, qseg, summ, ws
+    return res
 
 
 def cpu_baseline(inp, shape, budget_s):
@@ -316,6 +396,11 @@ def main():
                              "ms_per_step": round(dms, 4),
                              "data": "synthetic (one planted direction per query block)"}
         del ddev, dinp
+
+    if not args.no_decode:
+        log("[bench] decode steps at 131K")
+        del buf
+        extras["decode_131k"] = decode_bench(args.decode_steps)
 
     out = {
         "metric": METRIC,

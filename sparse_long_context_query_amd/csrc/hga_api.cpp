@@ -350,7 +350,7 @@ int hga_decode_step(const hga_config* cfg, int32_t pos, int32_t n, const void* q
     e = hga::launch_summarize(p, k, (t0 - p.L) / p.Bh, t0 / p.Bh, summ, st);
     if (e != hipSuccess) return hip_fail(e, "summarize launch");
   }
-  e = hga::launch_select_decode(p, q, n, t0, summ, sel, st);
+  e = hga::launch_select_decode(p, q, n, t0, summ, sel, hga::decode_score_ws(p, ws), st);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   e = hga::launch_decode(p, pos, n, q, k, v, sel, o, lse, (float*)ws, st);
   if (e != hipSuccess) return hip_fail(e, "decode launch");

@@ -13,9 +13,10 @@
 //
 // Work split (split over keys): per (sequence, KV head) the step's key list
 // -- the selected history tokens in ascending order, then the local tokens
-// t0 .. pos+n-1 -- is cut into chunks of 64 keys.  One wave per (chunk, KV
-// head, sequence) stages the chunk's K and V rows in LDS (coalesced 16-byte
-// loads, each row read once) and, for the R = G*n query rows of the group,
+// t0 .. pos+n-1 -- is cut into chunks of 64 keys.  One block of 4 waves per
+// (chunk, KV head, sequence) stages the chunk's K and V rows in LDS (16-byte
+// loads, every one in flight at once, each row read once); wave w then
+// takes the query rows r = w, w+4, ... of the R = G*n rows of the group and
 // writes the chunk's max, sum of exponentials and unnormalised P.V (fp32)
 // to the workspace.  A merge kernel then combines the chunks of every row in
 // chunk order (deterministic) into o and lse.  With a handful of query rows
@@ -49,6 +50,13 @@ template <> struct Elt<float> {
   __device__ __forceinline__ static float get(const float* p, int i) { return p[i]; }
 };
 
+// the wave's own LDS stores are visible to its later LDS loads
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int m = 32; m > 0; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
@@ -73,8 +81,10 @@ struct DecLds {
   }
 };
 
+constexpr int kWaves = 4;  // waves per chunk block
+
 template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_attn_kernel(
+__global__ __launch_bounds__(64 * kWaves) void decode_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ sel, float* __restrict__ part_o, float* __restrict__ part_ml,
     DecArgs a) {
@@ -84,41 +94,56 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(
   constexpr int ND = D / 64;    // output columns per lane
   extern __shared__ float4 dyn_lds[];
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int R = a.G * a.n;
   float* qs = reinterpret_cast<float*>(dyn_lds);
   T* ks = reinterpret_cast<T*>(qs + (size_t)R * D);
   T* vs = ks + kCK * KP;
   float* ps = reinterpret_cast<float*>(vs + kCK * D);
 
-  // token of key `lane` of this chunk; rows that hold no key read a valid
+  // token of key `key` of this chunk; rows that hold no key read a valid
   // row (masked below)
-  int tok;
-  bool valid;
-  bool local;
-  if (c < a.nch_h) {
-    const int hp = c * kCK + lane;
-    valid = hp < a.nht;
-    local = false;
-    tok = valid ? sel[(size_t)(b * a.Hkv + g) * a.K + hp / a.Bh] * a.Bh + hp % a.Bh : 0;
-  } else {
-    tok = a.t0 + (c - a.nch_h) * kCK + lane;
-    valid = tok < a.pos + a.n;
+  auto token_of = [&](int key, bool& valid, bool& local) {
+    if (c < a.nch_h) {
+      const int hp = c * kCK + key;
+      valid = hp < a.nht;
+      local = false;
+      return valid ? sel[(size_t)(b * a.Hkv + g) * a.K + hp / a.Bh] * a.Bh + hp % a.Bh : 0;
+    }
+    const int t = a.t0 + (c - a.nch_h) * kCK + key;
+    valid = t < a.pos + a.n;
     local = true;
-    if (!valid) tok = a.t0;
-  }
+    return valid ? t : a.t0;
+  };
+  bool valid, local;
+  const int tok = token_of(lane, valid, local);
 
-  // stage K and V rows (16-byte pieces, consecutive lanes on consecutive
-  // pieces of a row) and the group's query rows
+  // stage K and V rows: thread tid moves pieces tid + 256 u of the chunk
+  // (row = piece / CPR), all loads issued before the first LDS store
+  constexpr int NPT = kCK * CPR / (64 * kWaves);  // pieces per thread
   const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S;
-  for (int idx = lane; idx < kCK * CPR; idx += 64) {
-    const int r = idx / CPR, pc = idx % CPR;
-    const int tr = __shfl(tok, r, 64);
-    const size_t src = (kv_base + tr) * D + pc * EPP;
-    *reinterpret_cast<uint4*>(ks + r * KP + pc * EPP) = *reinterpret_cast<const uint4*>(k + src);
-    *reinterpret_cast<uint4*>(vs + r * D + pc * EPP) = *reinterpret_cast<const uint4*>(v + src);
+  {
+    uint4 kb[NPT], vb[NPT];
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int idx = tid + 64 * kWaves * u;
+      const int r = idx / CPR, pc = idx % CPR;
+      bool vr, lr;
+      const int tr = token_of(r, vr, lr);
+      const size_t src = (kv_base + tr) * D + pc * EPP;
+      kb[u] = *reinterpret_cast<const uint4*>(k + src);
+      vb[u] = *reinterpret_cast<const uint4*>(v + src);
+    }
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int idx = tid + 64 * kWaves * u;
+      const int r = idx / CPR, pc = idx % CPR;
+      *reinterpret_cast<uint4*>(ks + r * KP + pc * EPP) = kb[u];
+      *reinterpret_cast<uint4*>(vs + r * D + pc * EPP) = vb[u];
+    }
   }
-  for (int idx = lane; idx < R * D; idx += 64) {
+  for (int idx = tid; idx < R * D; idx += 64 * kWaves) {
     const int r = idx / D, d = idx % D;
     const int hh = r / a.n, i = r % a.n;
     qs[idx] = Elt<T>::get(q, (int)(((size_t)(b * a.Hq + g * a.G + hh) * a.n + i) * D + d));
@@ -131,7 +156,7 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(
 #pragma unroll
   for (int d = 0; d < D; ++d) krow[d] = Elt<T>::get(ks + lane * KP, d);
   float* ml = part_ml + ((size_t)(b * a.Hkv + g) * a.nc + c) * kMaxRows * 2;
-  for (int r = 0; r < R; ++r) {
+  for (int r = wave; r < R; r += kWaves) {
     const float* qr = qs + (size_t)r * D;
     float s = 0.f;
 #pragma unroll
@@ -151,7 +176,7 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(
       ml[2 * r + 1] = l;
     }
   }
-  __syncthreads();
+  wave_lds_fence();  // this wave's P rows, read back below by the same wave
 
   // unnormalised P.V: lane owns columns lane + 64 e
   float vcol[ND][kCK];
@@ -160,7 +185,7 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(
 #pragma unroll
     for (int kk = 0; kk < kCK; ++kk) vcol[e][kk] = Elt<T>::get(vs + kk * D, lane + 64 * e);
   float* po = part_o + ((size_t)(b * a.Hkv + g) * a.nc + c) * kMaxRows * D;
-  for (int r = 0; r < R; ++r) {
+  for (int r = wave; r < R; r += kWaves) {
     float acc[ND];
 #pragma unroll
     for (int e = 0; e < ND; ++e) acc[e] = 0.f;
@@ -189,20 +214,46 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const size_t base = (size_t)(b * a.Hkv + g) * a.nc;
+  // chunk maxima and sums, lane c holding chunk c (+ 64 j)
   float M = -INFINITY;
-  for (int c = 0; c < a.nc; ++c) M = fmaxf(M, part_ml[((base + c) * kMaxRows + r) * 2]);
+  for (int c0 = 0; c0 < a.nc; c0 += 64) {
+    const int c = c0 + lane;
+    if (c < a.nc) M = fmaxf(M, part_ml[((base + c) * kMaxRows + r) * 2]);
+  }
+  M = wave_max(M);
   float l = 0.f, acc[ND];
 #pragma unroll
   for (int e = 0; e < ND; ++e) acc[e] = 0.f;
-  for (int c = 0; c < a.nc; ++c) {
-    const float* ml = part_ml + ((base + c) * kMaxRows + r) * 2;
-    if (!(ml[1] > 0.f)) continue;  // no visible key of this row in chunk c
-    const float f = exp2f(ml[0] - M);
-    l += ml[1] * f;
-    const float* po = part_o + ((base + c) * kMaxRows + r) * D;
+  for (int c0 = 0; c0 < a.nc; c0 += 64) {
+    const int c = c0 + lane;
+    float f = 0.f, lc = 0.f;
+    if (c < a.nc) {
+      const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((base + c) * kMaxRows + r) * 2);
+      // a chunk with no visible key of this row has ml = (-inf, 0)
+      f = ml.y > 0.f ? exp2f(ml.x - M) : 0.f;
+      lc = ml.y * f;
+    }
+    l += lc;
+    const int cn = min(64, a.nc - c0);
+    for (int j = 0; j < cn; j += 8) {
+      // eight chunks' rows requested together, then accumulated in order
+      float x[8][ND], fj[8];
 #pragma unroll
-    for (int e = 0; e < ND; ++e) acc[e] += po[lane + 64 * e] * f;
+      for (int u = 0; u < 8; ++u) {
+        fj[u] = __shfl(f, j + u, 64);
+        const int cc = min(c0 + j + u, a.nc - 1);
+        const float* po = part_o + ((base + cc) * kMaxRows + r) * D;
+#pragma unroll
+        for (int e = 0; e < ND; ++e) x[u][e] = po[lane + 64 * e];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j + u < cn)
+#pragma unroll
+          for (int e = 0; e < ND; ++e) acc[e] += x[u][e] * fj[u];
+    }
   }
+  l = wave_sum(l);
   const int hh = r / a.n, i = r % a.n;
   const size_t orow = (size_t)(b * a.Hq + g * a.G + hh) * a.n + i;
   const float inv = 1.f / l;
@@ -258,7 +309,8 @@ hipError_t decode_t(const Prob& p, int pos, int n, const void* q_new, const void
   }
   {
     ProfScope ps(HGA_K_DECODE, st);
-    hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3(d.a.nc, p.Hkv, p.B), dim3(64), shm, st,
+    hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3(d.a.nc, p.Hkv, p.B), dim3(64 * kWaves),
+                       shm, st,
                        (const T*)q_new, (const T*)k, (const T*)v, sel, part_o, part_ml, d.a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -273,8 +325,19 @@ hipError_t decode_t(const Prob& p, int pos, int n, const void* q_new, const void
 
 int decode_max_rows() { return kMaxRows; }
 
+// Workspace: chunk partial O [B, Hkv, chunks, 64, D], then the chunk (max,
+// sum) pairs [B, Hkv, chunks, 64, 2], then the selection scores
+// [B, Hkv, nblk], all float32.
+static size_t partial_floats(const Prob& p) {
+  return (size_t)p.B * p.Hkv * max_chunks(p) * kMaxRows * (p.D + 2);
+}
+
 size_t decode_workspace_bytes(const Prob& p) {
-  return (size_t)p.B * p.Hkv * max_chunks(p) * kMaxRows * (p.D + 2) * sizeof(float);
+  return (partial_floats(p) + (size_t)p.B * p.Hkv * p.nblk) * sizeof(float);
+}
+
+float* decode_score_ws(const Prob& p, void* ws) {
+  return reinterpret_cast<float*>(ws) + partial_floats(p);
 }
 
 hipError_t launch_decode(const Prob& p, int pos, int n, const void* q_new, const void* k,

@@ -52,14 +52,17 @@ hipError_t launch_bwd(const Prob& p, const void* q, const void* k,
 size_t bwd_workspace_bytes(const Prob& p);
 
 // Decode step: selection of the n new tokens of q_new [B, Hq, n, D] (one
-// unit, sel [B, Hkv, k]), then their attention (o [B, Hq, n, D], lse
-// [B, Hq, n]) with the chunk partial sums in ws.
+// unit, sel [B, Hkv, k]; scores: B*Hkv*nblk floats of scratch), then their
+// attention (o [B, Hq, n, D], lse [B, Hq, n]) with the chunk partial sums
+// in ws.  decode_score_ws points at the scores' part of the decode workspace.
 hipError_t launch_select_decode(const Prob& p, const void* q_new, int n, int t0,
-                                const float* summ, int32_t* sel, hipStream_t st);
+                                const float* summ, int32_t* sel, float* scores,
+                                hipStream_t st);
 hipError_t launch_decode(const Prob& p, int pos, int n, const void* q_new, const void* k,
                          const void* v, const int32_t* sel, void* o, float* lse, float* ws,
                          hipStream_t st);
 size_t decode_workspace_bytes(const Prob& p);
+float* decode_score_ws(const Prob& p, void* ws);
 int decode_max_rows();  // limit of G * n
 
 // ---- profiling hooks (no-ops unless hga_profile_begin() was called) -----

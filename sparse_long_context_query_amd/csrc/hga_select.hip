@@ -121,6 +121,94 @@ __device__ __forceinline__ uint32_t wave_kth_largest32(const uint32_t (&v)[E], i
   return t;
 }
 
+// qbar[d] = mean over the G heads of group g and the nrows query rows of
+// unit j of q (float32): every row load of a thread in flight at once, then
+// an LDS fold over the R row slots.  Ends with a barrier (qbar is ready).
+template <typename T, int D>
+__device__ __forceinline__ void group_query_mean(const T* __restrict__ q, const SelGeom& geo,
+                                                 int b, int g, int j, int Hq, int G,
+                                                 float (*part)[D + 1], float* qbar) {
+  constexpr int EL = Vec16<T>::N;
+  constexpr int C = D / EL;
+  constexpr int R = kThreads / C;
+  const int c = threadIdx.x % C, r = threadIdx.x / C;
+  float acc[EL];
+#pragma unroll
+  for (int e = 0; e < EL; ++e) acc[e] = 0.f;
+  const int rows = G * geo.nrows;
+  constexpr int U = 16;  // row loads in flight per thread (raw 16-byte vectors)
+  for (int row0 = r; row0 < rows; row0 += U * R) {
+    uint4 f[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = row0 + u * R;
+      if (row < rows) {
+        const int hh = row / geo.nrows, tt = row % geo.nrows;
+        f[u] = *reinterpret_cast<const uint4*>(
+            q + ((size_t)(b * Hq + g * G + hh) * geo.qS + geo.q0 + j * geo.qstep + tt) * D +
+            c * EL);
+      } else {
+        f[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x[EL];
+      Vec16<T>::load(reinterpret_cast<const T*>(&f[u]), x);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) acc[e] += x[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EL; ++e) part[r][c * EL + e] = acc[e];
+  __syncthreads();
+  const float inv = 1.0f / (float)rows;
+  for (int d = threadIdx.x; d < D; d += kThreads) {
+    float sum = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) sum += part[rr][d];
+    qbar[d] = sum * inv;
+  }
+  __syncthreads();
+}
+
+// The k best of nb scores (nb <= 64 E) by (score desc, index asc), written
+// ascending to out[0, k): one wave finds the k-th largest score thr (with
+// multiplicity) by a bitwise search over the 32-bit score order held in its
+// registers, then keeps every score above thr and the lowest-index ties at
+// thr, compacting them in index order with ballots.  Called by the 64
+// threads of one wave; `score` may be in LDS or global memory.
+template <int E>
+__device__ __forceinline__ void wave_topk(const float* score, int nb, int K, int32_t* out,
+                                          int lane) {
+  uint32_t v[E];
+  float sv[E];
+  // unconditional loads (index clamped) so that all E are in flight at once
+#pragma unroll
+  for (int e = 0; e < E; ++e) sv[e] = score[min(64 * e + lane, nb - 1)];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = 64 * e + lane < nb ? score_ord(sv[e]) : 0u;
+  const uint32_t thr = wave_kth_largest32<E>(v, K);
+  int gt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) gt += __popcll(__ballot(v[e] > thr));
+  const int need = K - gt;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int count = 0, ties = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = 64 * e + lane;
+    const bool ok = i < nb;
+    const bool eq = ok && v[e] == thr;
+    const unsigned long long meq = __ballot(eq);
+    const bool take = (ok && v[e] > thr) || (eq && ties + __popcll(meq & below) < need);
+    const unsigned long long m = __ballot(take);
+    if (take) out[count + __popcll(m & below)] = i;
+    count += __popcll(m);
+    ties += __popcll(meq);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // a2 + a3: one block of threads per (unit j, KV head g, sequence b); a unit
 // is a query block of a segment, or the new tokens of a decode step.
@@ -174,47 +262,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   }
 
   // 1. query-block mean over (head in group, token in block)
-  {
-    const int c = threadIdx.x % C, r = threadIdx.x / C;
-    float acc[EL];
-#pragma unroll
-    for (int e = 0; e < EL; ++e) acc[e] = 0.f;
-    const int rows = G * geo.nrows;
-    constexpr int U = 16;  // row loads in flight per thread (raw 16-byte vectors)
-    for (int row0 = r; row0 < rows; row0 += U * R) {
-      uint4 f[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int row = row0 + u * R;
-        if (row < rows) {
-          const int hh = row / geo.nrows, tt = row % geo.nrows;
-          f[u] = *reinterpret_cast<const uint4*>(
-              q + ((size_t)(b * Hq + g * G + hh) * geo.qS + geo.q0 + j * geo.qstep + tt) * D +
-              c * EL);
-        } else {
-          f[u] = make_uint4(0, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float x[EL];
-        Vec16<T>::load(reinterpret_cast<const T*>(&f[u]), x);
-#pragma unroll
-        for (int e = 0; e < EL; ++e) acc[e] += x[e];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < EL; ++e) part[r][c * EL + e] = acc[e];
-    __syncthreads();
-    const float inv = 1.0f / (float)rows;
-    for (int d = threadIdx.x; d < D; d += kThreads) {
-      float sum = 0.f;
-#pragma unroll
-      for (int rr = 0; rr < R; ++rr) sum += part[rr][d];
-      qbar[d] = sum * inv;
-    }
-    __syncthreads();
-  }
+  group_query_mean<T, D>(q, geo, b, g, j, Hq, G, part, qbar);
 
   // 2. scores, one candidate per thread
   for (int i = threadIdx.x; i < nb; i += kThreads) {
@@ -245,37 +293,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   __syncthreads();
 
   if constexpr (E > 0) {
-    // 3. the k-th largest score (with multiplicity) and how many ties at it
-    //    belong to the k best
-    if (threadIdx.x < 64) {
-      const int lane = threadIdx.x;
-      uint32_t v[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int i = 64 * e + lane;
-        v[e] = i < nb ? score_ord(s_score[i]) : 0u;
-      }
-      const uint32_t thr = wave_kth_largest32<E>(v, K);
-      int gt = 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) gt += __popcll(__ballot(v[e] > thr));
-      // 4. every score above thr, then the lowest-index ties, in index order
-      const int need = K - gt;
-      const unsigned long long below = (1ull << lane) - 1ull;
-      int count = 0, ties = 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int i = 64 * e + lane;
-        const bool ok = i < nb;
-        const bool eq = ok && v[e] == thr;
-        const unsigned long long meq = __ballot(eq);
-        const bool take = (ok && v[e] > thr) || (eq && ties + __popcll(meq & below) < need);
-        const unsigned long long m = __ballot(take);
-        if (take) out[count + __popcll(m & below)] = i;
-        count += __popcll(m);
-        ties += __popcll(meq);
-      }
-    }
+    // 3. + 4. the k-th largest score and the k best, one wave
+    if (threadIdx.x < 64) wave_topk<E>(s_score, nb, K, out, threadIdx.x);
   } else {
     // 3. the k-th largest (score, index) key by an LDS sort
     int W = 1;
@@ -301,6 +320,50 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Selection of a decode step, which has a single unit per (b, g) but up to
+// 1,024 candidates: two launches so that reading the summaries spreads over
+// many CUs.  score_kernel: one candidate per thread, 256 per block of
+// threads, writes the fp32 scores (the same dot products select_kernel
+// forms); topk_kernel: one wave per (b, g) picks the k best (wave_topk).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void score_kernel(
+    const T* __restrict__ q, const float* __restrict__ summ, float* __restrict__ scores,
+    SelGeom geo, int Hq, int Hkv, int G, int nblk) {
+  constexpr int EL = Vec16<T>::N;
+  constexpr int C = D / EL;
+  constexpr int R = kThreads / C;
+  constexpr int NV = D / 4;
+  __shared__ float part[R][D + 1];
+  __shared__ __attribute__((aligned(16))) float qbar[D];
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  // the candidate's summary row first, so that it overlaps the query mean
+  const float4* rowp = reinterpret_cast<const float4*>(
+      summ + ((size_t)(b * Hkv + g) * nblk + (i < geo.nb ? i : 0)) * D);
+  float4 x[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) x[u] = rowp[u];
+  group_query_mean<T, D>(q, geo, b, g, 0, Hq, G, part, qbar);
+  float sc = 0.f;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const float4 qv = *reinterpret_cast<const float4*>(&qbar[4 * u]);
+    sc += qv.x * x[u].x + qv.y * x[u].y + qv.z * x[u].z + qv.w * x[u].w;
+  }
+  if (i < geo.nb) scores[(size_t)(b * Hkv + g) * nblk + i] = sc;
+}
+
+template <int E>
+__global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ scores,
+                                                  int32_t* __restrict__ sel, int nb, int K,
+                                                  int Hkv, int nblk) {
+  const int g = blockIdx.y, b = blockIdx.z;
+  wave_topk<E>(scores + (size_t)(b * Hkv + g) * nblk, nb, K, sel + (size_t)(b * Hkv + g) * K,
+               threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -414,10 +477,44 @@ hipError_t launch_select(const Prob& p, const void* q, const float* summ, int se
 }
 
 hipError_t launch_select_decode(const Prob& p, const void* q_new, int n, int t0,
-                                const float* summ, int32_t* sel, hipStream_t st) {
+                                const float* summ, int32_t* sel, float* scores,
+                                hipStream_t st) {
   // one unit: the n new tokens of q_new [B, Hq, n, D]; sel is [B, Hkv, k]
   const SelGeom geo{n, 0, 0, n, 1, 0, t0 / p.Bh};
-  return select_any(p, q_new, summ, geo, 1, sel, st);
+  const int nb = geo.nb;
+  if (nb <= p.K || nb > 1024) return select_any(p, q_new, summ, geo, 1, sel, st);
+  ProfScope ps(HGA_K_SELECT, st);
+  const dim3 grid((nb + kThreads - 1) / kThreads, p.Hkv, p.B);
+  if (p.dtype == HGA_BF16) {
+    if (p.D == 64)
+      hipLaunchKernelGGL((score_kernel<__bf16, 64>), grid, dim3(kThreads), 0, st,
+                         (const __bf16*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk);
+    else
+      hipLaunchKernelGGL((score_kernel<__bf16, 128>), grid, dim3(kThreads), 0, st,
+                         (const __bf16*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk);
+  } else {
+    if (p.D == 64)
+      hipLaunchKernelGGL((score_kernel<float, 64>), grid, dim3(kThreads), 0, st,
+                         (const float*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk);
+    else
+      hipLaunchKernelGGL((score_kernel<float, 128>), grid, dim3(kThreads), 0, st,
+                         (const float*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 g1(1, p.Hkv, p.B);
+  if (nb <= 64)
+    hipLaunchKernelGGL(topk_kernel<1>, g1, dim3(64), 0, st, scores, sel, nb, p.K, p.Hkv, p.nblk);
+  else if (nb <= 128)
+    hipLaunchKernelGGL(topk_kernel<2>, g1, dim3(64), 0, st, scores, sel, nb, p.K, p.Hkv, p.nblk);
+  else if (nb <= 256)
+    hipLaunchKernelGGL(topk_kernel<4>, g1, dim3(64), 0, st, scores, sel, nb, p.K, p.Hkv, p.nblk);
+  else if (nb <= 512)
+    hipLaunchKernelGGL(topk_kernel<8>, g1, dim3(64), 0, st, scores, sel, nb, p.K, p.Hkv, p.nblk);
+  else
+    hipLaunchKernelGGL(topk_kernel<16>, g1, dim3(64), 0, st, scores, sel, nb, p.K, p.Hkv,
+                       p.nblk);
+  return hipGetLastError();
 }
 
 hipError_t launch_gather(const Prob& p, const void* k, const void* v, const int32_t* sel,

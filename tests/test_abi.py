@@ -157,8 +157,9 @@ def test_decode_step_validation(L):
     cfg = good_cfg()  # S 16384, L 1024, G 4
     ws = L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_DECODE)
     # per (b, g): 32 history chunks (k 32 x Bh 64 / 64) + 16 local chunks of
-    # 64 keys, 64 query rows each, D + 2 floats per row
-    assert ws == 1 * 8 * (32 + 16) * 64 * (128 + 2) * 4
+    # 64 keys, 64 query rows each, D + 2 floats per row; then one score per
+    # history block
+    assert ws == 1 * 8 * (32 + 16) * 64 * (128 + 2) * 4 + 1 * 8 * 256 * 4
 
     def call(pos, n, ws_bytes=ws, sel=FAKE):
         return L.hga_decode_step(ctypes.byref(cfg), pos, n, FAKE, FAKE, FAKE, FAKE, sel, FAKE,
