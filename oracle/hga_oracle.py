@@ -268,6 +268,58 @@ def segment_backward(q, k, v, do, sel, shape, seg: int, O=None, LSE=None,
 
 
 # --------------------------------------------------------------------------
+# Exact-gradient backward ([SeCO] 提案手法: the forward keeps each chunk's KV
+# as a checkpoint; the backward visits the chunks from the last one,
+# rebuilds one chunk's graph at a time and yields exact gradients).  Applied
+# to HGA, the history keys and values of a segment are no longer detached:
+# they receive the gradient of every later query that selected their block.
+# The selection itself is discrete and receives none.
+# --------------------------------------------------------------------------
+def backward_exact(q, k, v, do, sel_all, shape, O, LSE, scale: Optional[float] = None,
+                   groups=None):
+    """Full-sequence dQ [B,Hq,S,D], dK and dV [B,Hkv,S,D] of the loss
+    sum(O * dO), where O [B,Hq,S,D] and LSE [B,Hq,S] come from the segment
+    forward and sel_all [B,Hkv,S/Bq,k] holds every segment's selection.
+    Segments are visited from the last to the first; each adds its queries'
+    contributions to the K/V rows of its whole key set (selected history and
+    causal local part), so that a segment's rows are complete when it is
+    reached."""
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    L, Bq, Bh = shape.seg_len, shape.query_block, shape.hist_block
+    sc = softmax_scale(D, scale)
+    nqb = L // Bq
+    dQ = np.zeros((B, Hq, S, D))
+    dK = np.zeros((B, Hkv, S, D))
+    dV = np.zeros((B, Hkv, S, D))
+    for s in reversed(range(S // L)):
+        t0 = s * L
+        for b, g in (groups if groups is not None else _all_groups(B, Hkv)):
+            for j in range(nqb):
+                keys, nh = key_indices(sel_all[b, g, s * nqb + j], Bh, t0, L)
+                Kset = _f64(k[b, g, keys])
+                Vset = _f64(v[b, g, keys])
+                qpos = t0 + j * Bq + np.arange(Bq)
+                mask = _block_mask(nh, t0, L, qpos)
+                hs = slice(g * G, (g + 1) * G)
+                qrows = slice(t0 + j * Bq, t0 + (j + 1) * Bq)
+                Qj = _f64(q[b, hs, qrows])
+                dOj = _f64(do[b, hs, qrows])
+                lse = _f64(LSE[b, hs, qrows])
+                Z = sc * (Qj @ Kset.T)
+                P = np.where(mask[None], np.exp(Z - lse[..., None]), 0.0)
+                dP = dOj @ Vset.T
+                delta = (dOj * _f64(O[b, hs, qrows])).sum(axis=-1)
+                dS = P * (dP - delta[..., None])
+                dQ[b, hs, qrows] = sc * (dS @ Kset)
+                # keys are distinct within one key set, so plain indexed adds
+                dK[b, g, keys] += sc * np.einsum("hqk,hqd->kd", dS, Qj)
+                dV[b, g, keys] += np.einsum("hqk,hqd->kd", P, dOj)
+    return dQ, dK, dV
+
+
+# --------------------------------------------------------------------------
 # a9: the segment loop ([FR] Analyse approfondie: the input is processed in
 # segments, one after another)
 # --------------------------------------------------------------------------
