@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step timing at the 131,072-token inference shape")
     ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-exact", action="store_true",
+                    help="skip the exact-gradient (history not detached) pass timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size "
                          "reference for HBM byte counters)")
@@ -160,6 +162,51 @@ def timed_passes(buf, dev, bwd, n, profile_classes=None):
     torch.cuda.synchronize()
     prof = hga.profile_end() if profile_classes else None
     return start.elapsed_time(end) / n, prof
+
+
+def exact_bench(shape, dev, steps, warmup):
+    """The exact-gradient form of the pass (hga_segment_step_exact): all
+    block summaries, then every segment from the last to the first, each
+    giving its queries' dK/dV to the history blocks it selected.  Same
+    inputs as the headline pass."""
+    import torch
+    import sparse_long_context_query_amd as hga
+    cfg = hga.Config.from_shape(shape)
+    s = hga.Shapes(cfg)
+    z = lambda shp_, dt: torch.zeros(shp_, dtype=dt, device="cuda")  # noqa: E731
+    summ, sel = z(s.summ, torch.float32), z(s.sel, torch.int32)
+    o, lse, dq = z(s.q, s.dt), z(s.lse, torch.float32), z(s.q, s.dt)
+    dk, dv = z(s.kv, s.dt), z(s.kv, s.dt)
+    hdk, hdv = z(s.kv, torch.float32), z(s.kv, torch.float32)
+    ws = torch.empty(hga.workspace_size(cfg, hga.HGA_OP_STEP_EXACT), dtype=torch.uint8,
+                     device="cuda")
+
+    def one_pass():
+        hdk.zero_()
+        hdv.zero_()
+        hga.summarize(cfg, dev["k"], 0, shape.seq_len // shape.hist_block, summ)
+        for seg in reversed(range(shape.nseg)):
+            hga.segment_step_exact(cfg, seg, dev["q"], dev["k"], dev["v"], dev["do"], summ, sel,
+                                   o, lse, dq, dk, dv, hdk, hdv, ws)
+
+    for _ in range(warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    for _ in range(steps):
+        one_pass()
+    en.record()
+    torch.cuda.synchronize()
+    ms = st.elapsed_time(en) / steps
+    hga.profile_begin()
+    one_pass()
+    prof = hga.profile_end()
+    return {"ms_per_step": round(ms, 4),
+            "tokens_per_s": round(shape.batch * shape.seq_len / (ms * 1e-3), 1),
+            "kernels_ms_per_pass": {c: round(v[0], 4) for c, v in prof.items() if v[1]},
+            "note": "history not detached: later segments' queries also give dK/dV to the "
+                    "blocks they selected; segments visited last to first"}
 
 
 def decode_bench(n_steps, news=(1, 16)):
@@ -397,6 +444,9 @@ def main():
                              "data": "synthetic (one planted direction per query block)"}
         del ddev, dinp
 
+    if not args.no_exact and bwd and shape.dtype == "bf16":
+        log("[bench] exact-gradient pass")
+        extras["exact_gradient"] = exact_bench(shape, dev, max(3, args.steps // 4), 1)
     if not args.no_decode:
         log("[bench] decode steps at 131K")
         del buf

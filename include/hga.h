@@ -186,9 +186,34 @@ int hga_decode_step(const hga_config* cfg, int32_t pos, int32_t n, const void* q
                     const void* k, const void* v, float* summ, int32_t* sel, void* o,
                     float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* Exact-gradient form of hga_segment_step with the backward ([SeCO] 提案手法:
+ * the forward keeps each chunk's KV; the backward visits the chunks from
+ * the last one, rebuilding one chunk's graph at a time, and the gradient is
+ * exact).  History is not detached: the keys and values of the blocks a
+ * segment's query blocks selected also receive those queries' gradient
+ * (the selection itself, being discrete, receives none).
+ *   - summ must hold every block before the segment (call hga_summarize
+ *     over [0, S/Bh) first; this step summarizes nothing);
+ *   - hist_dk, hist_dv: float32 [B, Hkv, S, D], zeroed by the caller before
+ *     the first step; the steps must visit the segments in descending
+ *     order.  Step seg adds scale * sum dS q (dk) and sum P dO (dv) of its
+ *     queries into the rows of the history blocks they selected, and writes
+ *     dk/dv of its own rows as its local part plus the sums later segments
+ *     left in those rows (complete, since later segments came first);
+ *   - select, forward and dq are those of hga_segment_step.
+ * Requirements: bf16 (else HGA_ERR_UNSUPPORTED); L/Bq <= 64 and
+ * (L/Bq)*k <= 8192 (else HGA_ERR_UNSUPPORTED).  ws:
+ * hga_workspace_size(cfg, HGA_OP_STEP_EXACT) bytes.  Results are
+ * deterministic (every row has one writer per step; no atomics). */
+int hga_segment_step_exact(const hga_config* cfg, int32_t seg, const void* q, const void* k,
+                           const void* v, const void* dO, const float* summ, int32_t* sel,
+                           void* o, float* lse, void* dq, void* dk, void* dv, float* hist_dk,
+                           float* hist_dv, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for an operation (0 if none is needed), or 0 with
  * hga_last_error() set if the config is invalid. */
-enum { HGA_OP_FWD = 0, HGA_OP_BWD = 1, HGA_OP_STEP = 2, HGA_OP_DECODE = 3 };
+enum { HGA_OP_FWD = 0, HGA_OP_BWD = 1, HGA_OP_STEP = 2, HGA_OP_DECODE = 3,
+       HGA_OP_STEP_EXACT = 4 };
 size_t hga_workspace_size(const hga_config* cfg, int32_t op);
 
 /* Message of the last failure on this thread ("" if none). */
@@ -214,7 +239,8 @@ enum {
   HGA_K_BWD_DKDV = 6,
   HGA_K_DECODE = 7,
   HGA_K_DECODE_MERGE = 8,
-  HGA_KCLASS_COUNT = 9
+  HGA_K_BWD_HIST = 9,
+  HGA_KCLASS_COUNT = 10
 };
 int hga_profile_begin(uint32_t mask);
 int hga_profile_end(double* ms, int64_t* count);

@@ -27,9 +27,9 @@ HGA_ERR_HIP = -4
 HGA_F32 = 0
 HGA_BF16 = 1
 HGA_STEP_BWD = 1
-HGA_OP_FWD, HGA_OP_BWD, HGA_OP_STEP, HGA_OP_DECODE = 0, 1, 2, 3
+HGA_OP_FWD, HGA_OP_BWD, HGA_OP_STEP, HGA_OP_DECODE, HGA_OP_STEP_EXACT = 0, 1, 2, 3, 4
 KERNEL_CLASSES = ("summarize", "select", "gather", "fwd", "bwd_pre", "bwd_dq", "bwd_dkdv",
-                  "decode", "decode_merge")
+                  "decode", "decode_merge", "bwd_hist")
 
 
 class HGAError(RuntimeError):
@@ -78,6 +78,9 @@ _SIGNATURES = {
                                     _P, _P, ctypes.c_size_t, _P]),
     "hga_segment_step": (ctypes.c_int, [_CP, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P,
                                         _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "hga_segment_step_exact": (ctypes.c_int, [_CP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
+                                              _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                              _P]),
     "hga_decode_step": (ctypes.c_int, [_CP, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P,
                                        _P, _P, _P, ctypes.c_size_t, _P]),
     "hga_workspace_size": (ctypes.c_size_t, [_CP, ctypes.c_int32]),
@@ -231,6 +234,24 @@ def segment_step(cfg: Config, seg: int, q, k, v, summ, sel, o, lse=None, do=None
         _ptr(dv, "dv", s.dt, s.kv, allow_none=not bwd),
         _ptr(ws, "ws", allow_none=not bwd),
         0 if ws is None else ws.numel() * ws.element_size(), _stream()))
+
+
+def segment_step_exact(cfg: Config, seg: int, q, k, v, do, summ, sel, o, lse, dq, dk, dv,
+                       hist_dk, hist_dv, ws) -> None:
+    """Exact-gradient step (history not detached); see hga_segment_step_exact:
+    summ must be complete, hist_dk / hist_dv float32 [B, Hkv, S, D] zeroed
+    before the first call, segments visited in descending order."""
+    s = Shapes(cfg)
+    torch = _torch()
+    _check(lib().hga_segment_step_exact(
+        ctypes.byref(cfg), seg, _ptr(q, "q", s.dt, s.q), _ptr(k, "k", s.dt, s.kv),
+        _ptr(v, "v", s.dt, s.kv), _ptr(do, "do", s.dt, s.q),
+        _ptr(summ, "summ", torch.float32, s.summ), _ptr(sel, "sel", torch.int32, s.sel),
+        _ptr(o, "o", s.dt, s.q), _ptr(lse, "lse", torch.float32, s.lse),
+        _ptr(dq, "dq", s.dt, s.q), _ptr(dk, "dk", s.dt, s.kv), _ptr(dv, "dv", s.dt, s.kv),
+        _ptr(hist_dk, "hist_dk", torch.float32, s.kv),
+        _ptr(hist_dv, "hist_dv", torch.float32, s.kv),
+        _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream()))
 
 
 def decode_step(cfg: Config, pos: int, q_new, k, v, summ, sel, o, lse=None, ws=None) -> None:

@@ -168,6 +168,9 @@ size_t hga_workspace_size(const hga_config* cfg, int32_t op) {
     case HGA_OP_DECODE:
       ok();
       return hga::decode_workspace_bytes(p);
+    case HGA_OP_STEP_EXACT:
+      ok();
+      return hga::bwd_exact_workspace_bytes(p);
     default:
       fail(HGA_ERR_ARG, "unknown op %d", op);
       return 0;
@@ -314,6 +317,51 @@ int hga_segment_step(const hga_config* cfg, int32_t seg, int32_t flags, const vo
     e = hga::launch_bwd(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, (float*)ws, st, fuse);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
   }
+  return ok();
+}
+
+int hga_segment_step_exact(const hga_config* cfg, int32_t seg, const void* q, const void* k,
+                           const void* v, const void* dO, const float* summ, int32_t* sel,
+                           void* o, float* lse, void* dq, void* dk, void* dv, float* hist_dk,
+                           float* hist_dv, void* ws, size_t ws_bytes, void* stream) {
+  hga::Prob p;
+  int rc = make_prob(cfg, &p);
+  if (rc) return rc;
+  if ((rc = check_seg(p, seg))) return rc;
+  if (p.dtype != HGA_BF16)
+    return fail(HGA_ERR_UNSUPPORTED, "the exact-gradient step needs bf16");
+  if (p.nqb > 64 || p.nqb * p.K > hga::kHistMaxEntries)
+    return fail(HGA_ERR_UNSUPPORTED,
+                "the exact-gradient step needs seg_len/query_block <= 64 and "
+                "(seg_len/query_block)*top_k <= %d", hga::kHistMaxEntries);
+  HGA_REQUIRE(q);
+  HGA_REQUIRE(k);
+  HGA_REQUIRE(v);
+  HGA_REQUIRE(dO);
+  HGA_REQUIRE(summ);
+  HGA_REQUIRE(sel);
+  HGA_REQUIRE(o);
+  HGA_REQUIRE(lse);
+  HGA_REQUIRE(dq);
+  HGA_REQUIRE(dk);
+  HGA_REQUIRE(dv);
+  HGA_REQUIRE(hist_dk);
+  HGA_REQUIRE(hist_dv);
+  HGA_REQUIRE(ws);
+  const size_t need = hga::bwd_exact_workspace_bytes(p);
+  if (ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hga::launch_select(p, q, summ, seg, sel, st);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  const bool fuse = hga::fused_delta(p);
+  e = hga::launch_fwd(p, q, k, v, sel, seg, o, lse, st, fuse ? dO : nullptr,
+                      fuse ? (float*)ws : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  e = hga::launch_bwd(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, (float*)ws, st, fuse,
+                      hist_dk, hist_dv);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();
 }
 

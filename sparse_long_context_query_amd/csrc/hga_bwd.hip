@@ -32,6 +32,10 @@ struct BwdArgs {
   int nq32;     // 32-row query sub-blocks per query block
   float c2;     // scale * log2(e)
   float scale;
+  // exact-gradient backward only (else null): fp32 [B, Hkv, S, D] sums of
+  // the gradient that later segments' queries gave each key (dK scaled)
+  float* hdk;
+  float* hdv;
 };
 
 // ---------------------------------------------------------------------------
@@ -109,11 +113,18 @@ __device__ __forceinline__ void dkdv_finish(const float* __restrict__ part_ws,
     const float4 kb = reinterpret_cast<const float4*>(p1 + (size_t)key * D)[c4];
     const float4 va = reinterpret_cast<const float4*>(p0 + (size_t)(32 + key) * D)[c4];
     const float4 vb = reinterpret_cast<const float4*>(p1 + (size_t)(32 + key) * D)[c4];
-    const bf16x4 ko = {(__bf16)((ka.x + kb.x) * a.scale), (__bf16)((ka.y + kb.y) * a.scale),
-                       (__bf16)((ka.z + kb.z) * a.scale), (__bf16)((ka.w + kb.w) * a.scale)};
-    const bf16x4 vo = {(__bf16)(va.x + vb.x), (__bf16)(va.y + vb.y), (__bf16)(va.z + vb.z),
-                       (__bf16)(va.w + vb.w)};
     const size_t off = ((size_t)bg * a.S + tk) * D + 4 * c4;
+    float4 hk = make_float4(0.f, 0.f, 0.f, 0.f), hv = hk;
+    if (a.hdk != nullptr) {  // exact gradient: what later segments added
+      hk = *reinterpret_cast<const float4*>(a.hdk + off);
+      hv = *reinterpret_cast<const float4*>(a.hdv + off);
+    }
+    const bf16x4 ko = {(__bf16)((ka.x + kb.x) * a.scale + hk.x),
+                       (__bf16)((ka.y + kb.y) * a.scale + hk.y),
+                       (__bf16)((ka.z + kb.z) * a.scale + hk.z),
+                       (__bf16)((ka.w + kb.w) * a.scale + hk.w)};
+    const bf16x4 vo = {(__bf16)(va.x + vb.x + hv.x), (__bf16)(va.y + vb.y + hv.y),
+                       (__bf16)(va.z + vb.z + hv.z), (__bf16)(va.w + vb.w + hv.w)};
     *reinterpret_cast<bf16x4*>(dk + off) = ko;
     *reinterpret_cast<bf16x4*>(dv + off) = vo;
   }
@@ -392,16 +403,24 @@ __device__ __forceinline__ void fold_level(const float4 (&f)[N], float4 (&out)[N
   }
 }
 
-// One dkdv item: key tile kt, pairs [pbeg, pend) dealt to the 8 waves, fold,
-// then either the final bf16 rows or (partial) the raw fp32 sums in slot pp.
-template <int D>
+// One dkdv item: a 32-key tile, pairs [pbeg, pend) dealt to the 8 waves,
+// fold, then the rows.
+//   HIST = false: local key tile kt of the segment; pair pi = (query tile
+//     kt + pi/G, head pi%G), causal; writes the final bf16 rows (plus, for the
+//     exact gradient, the fp32 sums later segments left in a.hdk / a.hdv) or
+//     (partial) the raw fp32 sums in slot pp.
+//   HIST = true (exact gradient): the tile of history rows kbase ..
+//     kbase+kvalid-1 of a block selected by the query blocks jlist[0..]; pair
+//     pi = (jlist[pi / (G nq32)], then head and 32-query tile), every key
+//     visible; adds its dK (scaled) and dV into a.hdk / a.hdv.
+template <int D, bool HIST = false>
 __device__ __forceinline__ void dkdv_item(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, const float* __restrict__ lse,
     const __bf16* __restrict__ dO, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, float* __restrict__ pp,
     const BwdArgs& a, unsigned char* s_raw, int b, int g, int kt, int pbeg, int pend,
-    bool partial) {
+    bool partial, const int* jlist = nullptr, int kbase = 0, int kvalid = 0) {
   constexpr int TQ = 32;                 // queries per tile
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
@@ -422,12 +441,13 @@ __device__ __forceinline__ void dkdv_item(
   // K and V rows of this key tile, shared by the 8 waves (lane (key lq, hi)
   // reads K[key][16kk + 8hi .. +7]); the barrier also retires the previous
   // item's reads of the fold buffer that overlaps these tiles
-  const int kfirst = t0 + kt * 32;
+  const int kfirst = HIST ? kbase : t0 + kt * 32;
+  const int nkey = HIST ? kvalid : min(32, tend - kfirst);  // key rows that exist
   const int tk = kfirst + lq;
-  const bool key_ok = tk < tend;
+  const bool key_ok = lq < nkey;
   __syncthreads();
-  if (wave == 0) dma_rows<D>(k + kv_base + (size_t)kfirst * D, 32, tend - kfirst, s_k, lane);
-  if (wave == 1) dma_rows<D>(v + kv_base + (size_t)kfirst * D, 32, tend - kfirst, s_v, lane);
+  if (wave == 0) dma_rows<D>(k + kv_base + (size_t)kfirst * D, 32, nkey, s_k, lane);
+  if (wave == 1) dma_rows<D>(v + kv_base + (size_t)kfirst * D, 32, nkey, s_v, lane);
   drain_vmem_loads();
   __syncthreads();
 
@@ -438,11 +458,20 @@ __device__ __forceinline__ void dkdv_item(
   fo.init(lane);
 
   for (int pi = pbeg + wave; pi < pend; pi += NW) {
-    const int qt = kt + pi / a.G;
-    const int h = g * a.G + pi % a.G;
-    const int tq0 = t0 + qt * TQ;
+    int h, tq0, nvalid;
+    if constexpr (HIST) {
+      const int per_j = a.G * a.nq32;
+      const int jj = jlist[pi / per_j], rem = pi % per_j;
+      const int qs = rem / a.G;
+      h = g * a.G + rem % a.G;
+      tq0 = t0 + jj * a.Bq + qs * TQ;
+      nvalid = min(TQ, a.Bq - qs * TQ);
+    } else {
+      h = g * a.G + pi % a.G;
+      tq0 = t0 + (kt + pi / a.G) * TQ;
+      nvalid = min(TQ, tend - tq0);
+    }
     const size_t hrow = (size_t)(b * a.Hq + h) * a.S;
-    const int nvalid = min(TQ, tend - tq0);
     // stage the pair: tiles by direct loads, lse / delta one dword per lane
     dma_rows<D>(q + (hrow + tq0) * D, TQ, nvalid, s_q, lane);
     dma_rows<D>(dO + (hrow + tq0) * D, TQ, nvalid, s_do, lane);
@@ -462,7 +491,8 @@ __device__ __forceinline__ void dkdv_item(
       pacc = mfma32(fo.row(s_do, 0, kk), fo.row(s_v, 0, kk), pacc);
     }
     // C layout: lane = key lq, item r = query row 8(r/4)+4hi+(r%4) of the tile
-    const bool need_mask = (tq0 < kfirst + 31) || (nvalid < TQ) || (kfirst + 32 > tend);
+    const bool need_mask = HIST ? (nvalid < TQ || nkey < 32)
+                                : ((tq0 < kfirst + 31) || (nvalid < TQ) || (nkey < 32));
     float pv[16];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -475,8 +505,8 @@ __device__ __forceinline__ void dkdv_item(
         const int r = 4 * r4 + e;
         float p = fast_exp2(fmaf(sacc[r], a.c2, -lv[e] * kLog2e));
         if (need_mask) {
-          const int tqr = tq0 + 8 * r4 + 4 * hi + e;
-          p = (key_ok && tk <= tqr && tqr < tend) ? p : 0.f;
+          const int row = 8 * r4 + 4 * hi + e;
+          p = (key_ok && row < nvalid && (HIST || tk <= tq0 + row)) ? p : 0.f;
         }
         pv[r] = p;
         sacc[r] = p * (pacc[r] - dv_[e]);  // dS
@@ -531,14 +561,27 @@ __device__ __forceinline__ void dkdv_item(
     const int tensor = f / (4 * NDB), db = (f / 4) % NDB, r4 = f % 4;
     const int d = 32 * db + 8 * r4 + 4 * hi;
     const float4 x = f5[i];
-    if (partial) {
+    if constexpr (HIST) {
+      // exact gradient: this segment's part of the history rows' gradient
+      if (key_ok) {
+        float* dst = (tensor ? a.hdv : a.hdk) + kv_base + (size_t)tk * D + d;
+        const float sc = tensor ? 1.f : a.scale;
+        float4 y = *reinterpret_cast<float4*>(dst);
+        y.x += x.x * sc; y.y += x.y * sc; y.z += x.z * sc; y.w += x.w * sc;
+        *reinterpret_cast<float4*>(dst) = y;
+      }
+    } else if (partial) {
       // raw fp32 rows [dK^T keys 0..31 | dV^T keys 0..31] x D, added by the
       // dq kernel that follows in the same backward call
       *reinterpret_cast<float4*>(pp + (size_t)(32 * tensor + lq) * D + d) = x;
     } else if (key_ok) {
       const float sc = tensor ? 1.f : a.scale;
-      const bf16x4 o4 = {(__bf16)(x.x * sc), (__bf16)(x.y * sc), (__bf16)(x.z * sc),
-                         (__bf16)(x.w * sc)};
+      float4 hx = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (a.hdk != nullptr)  // exact gradient: what later segments added
+        hx = *reinterpret_cast<const float4*>((tensor ? a.hdv : a.hdk) + kv_base +
+                                              (size_t)tk * D + d);
+      const bf16x4 o4 = {(__bf16)(x.x * sc + hx.x), (__bf16)(x.y * sc + hx.y),
+                         (__bf16)(x.z * sc + hx.z), (__bf16)(x.w * sc + hx.w)};
       *reinterpret_cast<bf16x4*>((tensor ? dv : dk) + kv_base + (size_t)tk * D + d) = o4;
     }
   }
@@ -588,6 +631,116 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
 }
 
 
+
+// ---------------------------------------------------------------------------
+// Exact-gradient backward ([SeCO] 提案手法: the chunks are visited from the
+// last one and the gradient is exact; here the history keys of a segment
+// are not detached).  The segment's queries also give dK/dV to the history
+// blocks they selected.  hist_blocks_kernel lists, per (sequence, KV head),
+// every distinct selected block with the mask of the query blocks that chose
+// it (one wave; the segment's selection rows staged in LDS, membership by
+// binary search in the ascending rows); dkdv_hist_kernel then walks (block,
+// 32-key tile) items, each owned by one block of threads, which adds the
+// tile's dK/dV into the fp32 sums a.hdk / a.hdv (no atomics: one owner per
+// row, so the sums are deterministic).
+// ---------------------------------------------------------------------------
+struct HistEntry {
+  int blk;
+  int pad;
+  unsigned long long jmask;  // bit j: query block j of the segment chose blk
+};
+
+
+__global__ __launch_bounds__(64) void hist_blocks_kernel(const int32_t* __restrict__ sel,
+                                                         HistEntry* __restrict__ list,
+                                                         int* __restrict__ counts, BwdArgs a,
+                                                         int maxd) {
+  __shared__ int s_sel[kHistMaxEntries];
+  const int bg = blockIdx.x;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int lane = threadIdx.x;
+  const int nb = a.seg * a.L / a.Bh;
+  const int n_ent = a.nqb * a.K;
+  const int32_t* rows = sel + ((size_t)(b * a.Hkv + g) * a.nqb_all + (size_t)a.seg * a.nqb) * a.K;
+  for (int e = lane; e < n_ent; e += 64) {
+    const int x = rows[e];
+    s_sel[e] = (x >= 0 && x < nb) ? x : 0x7fffffff;  // padding sorts last
+  }
+  __syncthreads();
+  int count = 0;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int e0 = 0; e0 < n_ent; e0 += 64) {
+    const int e = e0 + lane;
+    const int blk = e < n_ent ? s_sel[e] : 0x7fffffff;
+    const int j = e / a.K;
+    bool owner = blk != 0x7fffffff;
+    unsigned long long jmask = 0;
+    for (int jj = 0; jj < a.nqb; ++jj) {
+      // lower bound of blk in row jj (ascending)
+      const int* row = s_sel + jj * a.K;
+      int lo = 0, hi = a.K;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (row[mid] < blk) lo = mid + 1; else hi = mid;
+      }
+      const bool found = lo < a.K && row[lo] == blk;
+      if (found && jj < j) owner = false;  // an earlier query block lists it first
+      if (found) jmask |= 1ull << jj;
+    }
+    const unsigned long long m = __ballot(owner);
+    if (owner) {
+      HistEntry* out = list + (size_t)bg * maxd + count + __popcll(m & below);
+      out->blk = blk;
+      out->pad = 0;
+      out->jmask = jmask;
+    }
+    count += __popcll(m);
+  }
+  if (lane == 0) counts[bg] = count;
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void dkdv_hist_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, const float* __restrict__ lse,
+    const __bf16* __restrict__ dO, const float* __restrict__ delta,
+    const HistEntry* __restrict__ list, const int* __restrict__ counts, BwdArgs a, int maxd,
+    int ntpb) {
+  constexpr int TQ = 32;
+  constexpr int NDB = D / 32;
+  constexpr int TILE_B = TQ * 2 * D;
+  constexpr int SLICE_B = 2 * TILE_B + 256;
+  constexpr int NW = 8;
+  constexpr int STAGE_B = 2 * TILE_B + NW * SLICE_B;
+  constexpr int FOLD_B = NW * (2 * NDB * 4 / 2) * 64 * 16;
+  constexpr int LDS_BYTES = STAGE_B > FOLD_B ? STAGE_B : FOLD_B;
+  __shared__ __attribute__((aligned(1024))) unsigned char s_raw[LDS_BYTES];
+  __shared__ int s_j[64];
+  __shared__ int s_nj;
+  const int nbg = a.B * a.Hkv;
+  const int total = maxd * ntpb * nbg;
+  // items t = (entry idx, key tile kt, bg) with bg fastest, so that the live
+  // entries (idx < count) come first and are dealt evenly over the grid
+  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    const int bg = t % nbg, rest = t / nbg;
+    const int kt = rest % ntpb, idx = rest / ntpb;
+    if (idx >= counts[bg]) continue;  // uniform over the block
+    const HistEntry ent = list[(size_t)bg * maxd + idx];
+    __syncthreads();  // the previous item's reads of s_j are done
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const bool bit = lane < a.nqb && ((ent.jmask >> lane) & 1ull);
+      const unsigned long long m = __ballot(bit);
+      if (bit) s_j[__popcll(m & ((1ull << lane) - 1ull))] = lane;
+      if (lane == 0) s_nj = __popcll(m);
+    }
+    __syncthreads();
+    const int pairs = s_nj * a.G * a.nq32;
+    dkdv_item<D, true>(q, k, v, lse, dO, delta, nullptr, nullptr, nullptr, a, s_raw,
+                       bg / a.Hkv, bg % a.Hkv, kt, 0, pairs, false, s_j,
+                       ent.blk * a.Bh + 32 * kt, min(32, a.Bh - 32 * kt));
+  }
+}
 
 // ---------------------------------------------------------------------------
 // float32 kernels (reference-precision path, plain VALU).
@@ -746,6 +899,7 @@ BwdArgs make_args(const Prob& p, int seg) {
   a.wpu = (p.G * a.nq32 + 3) / 4;
   a.c2 = p.scale * kLog2e;
   a.scale = p.scale;
+  a.hdk = a.hdv = nullptr;
   return a;
 }
 
@@ -762,6 +916,17 @@ size_t partial_bytes(const Prob& p) {
 }
 float* dkdv_partials(const Prob& p, float* delta) {
   return reinterpret_cast<float*>(reinterpret_cast<char*>(delta) + delta_bytes(p));
+}
+// exact backward: after the above, per (b, g) a count and up to maxd entries
+int hist_max_entries(const Prob& p) {
+  const int nb_max = (p.S - p.L) / p.Bh;
+  const int n_ent = p.nqb * p.K;
+  return nb_max < n_ent ? nb_max : n_ent;
+}
+size_t hist_list_bytes(const Prob& p) {
+  return round256((size_t)p.B * p.Hkv * sizeof(int)) +
+         round256((size_t)p.B * p.Hkv * (hist_max_entries(p) > 0 ? hist_max_entries(p) : 1) *
+                  sizeof(HistEntry));
 }
 
 template <typename T, int D>
@@ -780,10 +945,12 @@ template <int D>
 hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
                     const void* o, const float* lse, const void* dO, const int32_t* sel,
                     int seg, void* dq, void* dk, void* dv, float* delta, hipStream_t st,
-                    bool delta_ready) {
+                    bool delta_ready, float* hdk, float* hdv) {
   hipError_t e = delta_ready ? hipSuccess : delta_t<__bf16, D>(p, o, dO, seg, delta, st);
   if (e != hipSuccess) return e;
   BwdArgs a = make_args(p, seg);
+  a.hdk = hdk;
+  a.hdv = hdv;
   const int nkt = (p.L + 31) / 32;
   const int nph = (nkt + 1) / 2;
   float* part_ws = dkdv_partials(p, delta);
@@ -794,6 +961,25 @@ hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
     hipLaunchKernelGGL((dkdv_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, lse,
                        (const __bf16*)dO, delta, (__bf16*)dk, (__bf16*)dv, part_ws, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int maxd = hist_max_entries(p);
+  if (hdk != nullptr && seg > 0 && maxd > 0) {
+    // exact gradient: this segment's contribution to its history blocks
+    char* base = reinterpret_cast<char*>(part_ws) + partial_bytes(p);
+    int* counts = reinterpret_cast<int*>(base);
+    HistEntry* list =
+        reinterpret_cast<HistEntry*>(base + round256((size_t)p.B * p.Hkv * sizeof(int)));
+    ProfScope ps(HGA_K_BWD_HIST, st);
+    hipLaunchKernelGGL(hist_blocks_kernel, dim3(p.B * p.Hkv), dim3(64), 0, st, sel, list, counts,
+                       a, maxd);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int ntpb = (p.Bh + 31) / 32;
+    hipLaunchKernelGGL((dkdv_hist_kernel<D>), dim3(256), dim3(512), 0, st, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dO, delta,
+                       (const HistEntry*)list, (const int*)counts, a, maxd, ntpb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -841,15 +1027,19 @@ size_t bwd_workspace_bytes(const Prob& p) {
   return delta_bytes(p) + partial_bytes(p);
 }
 
+size_t bwd_exact_workspace_bytes(const Prob& p) {
+  return delta_bytes(p) + partial_bytes(p) + hist_list_bytes(p);
+}
+
 hipError_t launch_bwd(const Prob& p, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, const int32_t* sel,
                       int seg, void* dq, void* dk, void* dv, float* delta_ws, hipStream_t st,
-                      bool delta_ready) {
+                      bool delta_ready, float* hist_dk, float* hist_dv) {
   if (p.dtype == HGA_BF16)
     return p.D == 64 ? bwd_bf16<64>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st,
-                                    delta_ready)
+                                    delta_ready, hist_dk, hist_dv)
                      : bwd_bf16<128>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st,
-                                     delta_ready);
+                                     delta_ready, hist_dk, hist_dv);
   return p.D == 64 ? bwd_f32<64>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st)
                    : bwd_f32<128>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st);
 }

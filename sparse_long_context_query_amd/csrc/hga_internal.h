@@ -27,6 +27,7 @@ struct Prob {
 
 constexpr int kMaxCandidates = 8192;   // S / Bh limit of the selection sort
 constexpr int kMaxTopK = 1024;
+constexpr int kHistMaxEntries = 8192;  // (L / Bq) * k limit of the exact backward
 
 // ---- launchers (host side; return hipSuccess or the launch error) --------
 hipError_t launch_summarize(const Prob& p, const void* k, int blk_begin,
@@ -44,12 +45,17 @@ hipError_t launch_fwd(const Prob& p, const void* q, const void* k,
                       const void* v, const int32_t* sel, int seg, void* o,
                       float* lse, hipStream_t st, const void* dO = nullptr,
                       float* delta = nullptr);
+// hist_dk / hist_dv (exact gradient, bf16 only): fp32 [B, Hkv, S, D] sums
+// of the gradient later segments gave each key; the backward adds them to
+// its own rows and adds its queries' part to the history rows it selected.
 hipError_t launch_bwd(const Prob& p, const void* q, const void* k,
                       const void* v, const void* o, const float* lse,
                       const void* dO, const int32_t* sel, int seg, void* dq,
                       void* dk, void* dv, float* delta_ws, hipStream_t st,
-                      bool delta_ready = false);
+                      bool delta_ready = false, float* hist_dk = nullptr,
+                      float* hist_dv = nullptr);
 size_t bwd_workspace_bytes(const Prob& p);
+size_t bwd_exact_workspace_bytes(const Prob& p);
 
 // Decode step: selection of the n new tokens of q_new [B, Hq, n, D] (one
 // unit, sel [B, Hkv, k]; scores: B*Hkv*nblk floats of scratch), then their

@@ -172,3 +172,22 @@ def test_decode_step_validation(L):
     assert call(0, 17) == hga.HGA_ERR_UNSUPPORTED and "G*n" in hga.last_error()
     assert call(2048, 4, sel=None) == hga.HGA_ERR_ARG and "sel is NULL" in hga.last_error()
     assert call(2048, 4, ws_bytes=ws - 1) == hga.HGA_ERR_WORKSPACE
+
+
+def test_exact_step_validation(L):
+    cfg = good_cfg()
+    need = L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_STEP_EXACT)
+    assert need > L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_STEP)
+
+    def call(c, seg=1, ws_bytes=need, hdk=FAKE):
+        return L.hga_segment_step_exact(ctypes.byref(c), seg, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, FAKE, FAKE, FAKE, hdk, FAKE, FAKE, ws_bytes,
+                                        None)
+
+    assert call(cfg, seg=16) == hga.HGA_ERR_ARG
+    assert call(cfg, hdk=None) == hga.HGA_ERR_ARG and "hist_dk is NULL" in hga.last_error()
+    assert call(cfg, ws_bytes=need - 1) == hga.HGA_ERR_WORKSPACE
+    f32 = good_cfg(dtype=hga.HGA_F32)
+    assert call(f32) == hga.HGA_ERR_UNSUPPORTED and "bf16" in hga.last_error()
+    wide = good_cfg(seg_len=2048, query_block=16)  # 128 query blocks per segment (> 64)
+    assert call(wide) == hga.HGA_ERR_UNSUPPORTED and "64" in hga.last_error()
