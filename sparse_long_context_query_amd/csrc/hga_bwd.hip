@@ -490,6 +490,15 @@ __device__ __forceinline__ void dkdv_item(
       sacc = mfma32(fo.row(s_q, 0, kk), fo.row(s_k, 0, kk), sacc);
       pacc = mfma32(fo.row(s_do, 0, kk), fo.row(s_v, 0, kk), pacc);
     }
+    // the fragments of the next MFMA are requested before the current one
+    // issues (two reads ahead), so LDS latency overlaps the matrix work
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int u = 0; u < 2 * NKK - 2; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     // C layout: lane = key lq, item r = query row 8(r/4)+4hi+(r%4) of the tile
     const bool need_mask = HIST ? (nvalid < TQ || nkey < 32)
                                 : ((tq0 < kfirst + 31) || (nvalid < TQ) || (nkey < 32));
