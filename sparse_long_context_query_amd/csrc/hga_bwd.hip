@@ -646,9 +646,9 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
 // last one and the gradient is exact; here the history keys of a segment
 // are not detached).  The segment's queries also give dK/dV to the history
 // blocks they selected.  hist_blocks_kernel lists, per (sequence, KV head),
-// every distinct selected block with the mask of the query blocks that chose
-// it (one wave; the segment's selection rows staged in LDS, membership by
-// binary search in the ascending rows); dkdv_hist_kernel then walks (block,
+// every distinct selected block, ascending, with the mask of the query
+// blocks that chose it (an LDS bit table per history block, filled by
+// integer ORs, then compacted with ballots); dkdv_hist_kernel then walks (block,
 // 32-key tile) items, each owned by one block of threads, which adds the
 // tile's dK/dV into the fp32 sums a.hdk / a.hdv (no atomics: one owner per
 // row, so the sums are deterministic).
@@ -660,52 +660,48 @@ struct HistEntry {
 };
 
 
-__global__ __launch_bounds__(64) void hist_blocks_kernel(const int32_t* __restrict__ sel,
-                                                         HistEntry* __restrict__ list,
-                                                         int* __restrict__ counts, BwdArgs a,
-                                                         int maxd) {
-  __shared__ int s_sel[kHistMaxEntries];
+__global__ __launch_bounds__(256) void hist_blocks_kernel(const int32_t* __restrict__ sel,
+                                                          HistEntry* __restrict__ list,
+                                                          int* __restrict__ counts, BwdArgs a,
+                                                          int maxd) {
+  __shared__ unsigned long long s_mask[kMaxCandidates];  // per history block
+  __shared__ int s_wtot[4];
   const int bg = blockIdx.x;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = a.seg * a.L / a.Bh;
   const int n_ent = a.nqb * a.K;
   const int32_t* rows = sel + ((size_t)(b * a.Hkv + g) * a.nqb_all + (size_t)a.seg * a.nqb) * a.K;
-  for (int e = lane; e < n_ent; e += 64) {
+  for (int i = tid; i < nb; i += 256) s_mask[i] = 0ull;
+  __syncthreads();
+  // bit j of block x's mask: query block j chose x (integer OR: the result
+  // does not depend on the order of the updates)
+  for (int e = tid; e < n_ent; e += 256) {
     const int x = rows[e];
-    s_sel[e] = (x >= 0 && x < nb) ? x : 0x7fffffff;  // padding sorts last
+    if (x >= 0 && x < nb) atomicOr(&s_mask[x], 1ull << (e / a.K));
   }
   __syncthreads();
+  // the chosen blocks in ascending order
   int count = 0;
   const unsigned long long below = (1ull << lane) - 1ull;
-  for (int e0 = 0; e0 < n_ent; e0 += 64) {
-    const int e = e0 + lane;
-    const int blk = e < n_ent ? s_sel[e] : 0x7fffffff;
-    const int j = e / a.K;
-    bool owner = blk != 0x7fffffff;
-    unsigned long long jmask = 0;
-    for (int jj = 0; jj < a.nqb; ++jj) {
-      // lower bound of blk in row jj (ascending)
-      const int* row = s_sel + jj * a.K;
-      int lo = 0, hi = a.K;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (row[mid] < blk) lo = mid + 1; else hi = mid;
-      }
-      const bool found = lo < a.K && row[lo] == blk;
-      if (found && jj < j) owner = false;  // an earlier query block lists it first
-      if (found) jmask |= 1ull << jj;
-    }
-    const unsigned long long m = __ballot(owner);
-    if (owner) {
-      HistEntry* out = list + (size_t)bg * maxd + count + __popcll(m & below);
-      out->blk = blk;
+  for (int base = 0; base < nb; base += 256) {
+    const int i = base + tid;
+    const unsigned long long m = i < nb ? s_mask[i] : 0ull;
+    const unsigned long long bal = __ballot(m != 0ull);
+    if (lane == 0) s_wtot[wave] = __popcll(bal);
+    __syncthreads();
+    int off = count;
+    for (int w = 0; w < wave; ++w) off += s_wtot[w];
+    if (m != 0ull) {
+      HistEntry* out = list + (size_t)bg * maxd + off + __popcll(bal & below);
+      out->blk = i;
       out->pad = 0;
-      out->jmask = jmask;
+      out->jmask = m;
     }
-    count += __popcll(m);
+    count += s_wtot[0] + s_wtot[1] + s_wtot[2] + s_wtot[3];
+    __syncthreads();
   }
-  if (lane == 0) counts[bg] = count;
+  if (tid == 0) counts[bg] = count;
 }
 
 template <int D>
@@ -981,8 +977,8 @@ hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
     HistEntry* list =
         reinterpret_cast<HistEntry*>(base + round256((size_t)p.B * p.Hkv * sizeof(int)));
     ProfScope ps(HGA_K_BWD_HIST, st);
-    hipLaunchKernelGGL(hist_blocks_kernel, dim3(p.B * p.Hkv), dim3(64), 0, st, sel, list, counts,
-                       a, maxd);
+    hipLaunchKernelGGL(hist_blocks_kernel, dim3(p.B * p.Hkv), dim3(256), 0, st, sel, list,
+                       counts, a, maxd);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int ntpb = (p.Bh + 31) / 32;
