@@ -223,9 +223,10 @@ const char* hga_last_error(void);
 const char* hga_version(void);
 
 /* ---- optional profiling hooks (timing only, never change results) ----
- * hga_profile_begin(mask) makes later launches on this thread record a HIP
- * event pair on the launch stream around each kernel whose class bit
- * (1 << class) is set in mask.  hga_profile_end() waits for those events,
+ * hga_profile_begin(mask) makes later launches on this thread of each kernel
+ * whose class bit (1 << class) is set in mask carry a HIP start / stop event
+ * pair that the kernel's own dispatch stamps (hipExtLaunchKernel), so the
+ * timing adds nothing between kernels on the stream.  hga_profile_end() waits for those events,
  * writes per-class total milliseconds and launch counts into ms[] and
  * count[] (arrays of HGA_KCLASS_COUNT entries), stops recording and
  * releases the events.  Kernel classes: */

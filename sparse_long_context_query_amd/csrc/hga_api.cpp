@@ -117,7 +117,6 @@ thread_local bool g_prof_on = false;
 thread_local uint32_t g_prof_mask = 0;
 thread_local std::vector<ProfEvent> g_prof_events;
 thread_local std::vector<hipEvent_t> g_prof_pool;
-thread_local hipEvent_t g_prof_pending_start = nullptr;
 
 hipEvent_t pool_get() {
   if (!g_prof_pool.empty()) {
@@ -133,18 +132,18 @@ hipEvent_t pool_get() {
 }  // namespace
 
 namespace hga {
-void prof_mark_begin(int kclass, hipStream_t st) {
-  if (!g_prof_on || !((g_prof_mask >> kclass) & 1u)) return;
-  g_prof_pending_start = pool_get();
-  if (g_prof_pending_start) hipEventRecord(g_prof_pending_start, st);
-}
-void prof_mark_end(int kclass, hipStream_t st) {
-  if (!g_prof_on || g_prof_pending_start == nullptr) return;
-  hipEvent_t stop = pool_get();
-  if (stop == nullptr) return;
-  hipEventRecord(stop, st);
-  g_prof_events.push_back({kclass, g_prof_pending_start, stop});
-  g_prof_pending_start = nullptr;
+bool prof_events(int kclass, hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_prof_on || !((g_prof_mask >> kclass) & 1u)) return false;
+  hipEvent_t a = pool_get();
+  hipEvent_t b = a ? pool_get() : nullptr;
+  if (b == nullptr) {
+    if (a) g_prof_pool.push_back(a);
+    return false;
+  }
+  g_prof_events.push_back({kclass, a, b});
+  *start = a;
+  *stop = b;
+  return true;
 }
 }  // namespace hga
 

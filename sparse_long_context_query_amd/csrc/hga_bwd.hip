@@ -940,8 +940,7 @@ hipError_t delta_t(const Prob& p, const void* o, const void* dO, int seg, float*
   constexpr int C = D / Vec16<T>::N;
   constexpr int RPB = 256 / C;
   const int nrows = p.B * p.Hq * p.L;
-  ProfScope ps(HGA_K_BWD_PRE, st);
-  hipLaunchKernelGGL((delta_kernel<T, D>), dim3((nrows + RPB - 1) / RPB), dim3(256), 0, st,
+  HGA_LAUNCH(HGA_K_BWD_PRE, (delta_kernel<T, D>), dim3((nrows + RPB - 1) / RPB), dim3(256), 0, st,
                      (const T*)o, (const T*)dO, delta, p.S, p.L, seg * p.L, nrows);
   return hipGetLastError();
 }
@@ -962,8 +961,7 @@ hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
   {
     // dk/dv first: the dq kernel finishes the key tiles it left as partial sums
     const int nblocks = p.B * p.Hkv * (nkt + (nkt & 1));
-    ProfScope ps(HGA_K_BWD_DKDV, st);
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st,
+    HGA_LAUNCH(HGA_K_BWD_DKDV, (dkdv_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, lse,
                        (const __bf16*)dO, delta, (__bf16*)dk, (__bf16*)dv, part_ws, a);
     e = hipGetLastError();
@@ -976,13 +974,12 @@ hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
     int* counts = reinterpret_cast<int*>(base);
     HistEntry* list =
         reinterpret_cast<HistEntry*>(base + round256((size_t)p.B * p.Hkv * sizeof(int)));
-    ProfScope ps(HGA_K_BWD_HIST, st);
-    hipLaunchKernelGGL(hist_blocks_kernel, dim3(p.B * p.Hkv), dim3(256), 0, st, sel, list,
+    HGA_LAUNCH(HGA_K_BWD_HIST, hist_blocks_kernel, dim3(p.B * p.Hkv), dim3(256), 0, st, sel, list,
                        counts, a, maxd);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int ntpb = (p.Bh + 31) / 32;
-    hipLaunchKernelGGL((dkdv_hist_kernel<D>), dim3(256), dim3(512), 0, st, (const __bf16*)q,
+    HGA_LAUNCH(HGA_K_BWD_HIST, (dkdv_hist_kernel<D>), dim3(256), dim3(512), 0, st, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dO, delta,
                        (const HistEntry*)list, (const int*)counts, a, maxd, ntpb);
     e = hipGetLastError();
@@ -990,8 +987,7 @@ hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
   }
   {
     const int nblocks = p.B * p.Hkv * p.nqb * a.wpu;
-    ProfScope ps(HGA_K_BWD_DQ, st);
-    hipLaunchKernelGGL((dq_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st, (const __bf16*)q,
+    HGA_LAUNCH(HGA_K_BWD_DQ, (dq_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dO, delta, sel,
                        (__bf16*)dq, part_ws, (__bf16*)dk, (__bf16*)dv, nph, a);
     e = hipGetLastError();
@@ -1008,8 +1004,7 @@ hipError_t bwd_f32(const Prob& p, const void* q, const void* k, const void* v,
   BwdArgs a = make_args(p, seg);
   {
     const int nblocks = p.B * p.Hq * p.nqb * ((p.Bq + 63) / 64);
-    ProfScope ps(HGA_K_BWD_DQ, st);
-    hipLaunchKernelGGL((dq_f32_kernel<D>), dim3(nblocks), dim3(64), 0, st, (const float*)q,
+    HGA_LAUNCH(HGA_K_BWD_DQ, (dq_f32_kernel<D>), dim3(nblocks), dim3(64), 0, st, (const float*)q,
                        (const float*)k, (const float*)v, lse, (const float*)dO, delta, sel,
                        (float*)dq, a);
     e = hipGetLastError();
@@ -1017,8 +1012,8 @@ hipError_t bwd_f32(const Prob& p, const void* q, const void* k, const void* v,
   }
   {
     const int nblocks = p.B * p.Hkv * ((p.L + 63) / 64);
-    ProfScope ps(HGA_K_BWD_DKDV, st);
-    hipLaunchKernelGGL((dkdv_f32_kernel<D>), dim3(nblocks), dim3(64), 0, st, (const float*)q,
+    HGA_LAUNCH(HGA_K_BWD_DKDV, (dkdv_f32_kernel<D>), dim3(nblocks), dim3(64), 0, st,
+               (const float*)q,
                        (const float*)k, (const float*)v, lse, (const float*)dO, delta,
                        (float*)dk, (float*)dv, a);
     e = hipGetLastError();

@@ -308,15 +308,14 @@ hipError_t decode_t(const Prob& p, int pos, int n, const void* q_new, const void
     if (e != hipSuccess) return e;
   }
   {
-    ProfScope ps(HGA_K_DECODE, st);
-    hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3(d.a.nc, p.Hkv, p.B), dim3(64 * kWaves),
+    HGA_LAUNCH(HGA_K_DECODE, (decode_attn_kernel<T, D>), dim3(d.a.nc, p.Hkv, p.B), dim3(64 * kWaves),
                        shm, st,
                        (const T*)q_new, (const T*)k, (const T*)v, sel, part_o, part_ml, d.a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  ProfScope ps(HGA_K_DECODE_MERGE, st);
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(d.R, p.Hkv, p.B), dim3(64), 0, st,
+  HGA_LAUNCH(HGA_K_DECODE_MERGE, (decode_merge_kernel<T, D>), dim3(d.R, p.Hkv, p.B), dim3(64), 0, st,
+             
                      (const float*)part_o, (const float*)part_ml, (T*)o, lse, d.a);
   return hipGetLastError();
 }

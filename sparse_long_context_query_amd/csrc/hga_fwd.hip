@@ -407,8 +407,7 @@ hipError_t fwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
                     const void* dO, float* delta) {
   FwdArgs a = make_args(p, seg);
   const int nblocks = p.B * p.Hkv * p.nqb * a.wpu;
-  ProfScope ps(HGA_K_FWD, st);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st,
+  HGA_LAUNCH(HGA_K_FWD, (fwd_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, sel, (__bf16*)o,
                      lse, (const __bf16*)dO, delta, a);
   return hipGetLastError();
@@ -419,8 +418,7 @@ hipError_t fwd_f32(const Prob& p, const void* q, const void* k, const void* v,
                    const int32_t* sel, int seg, void* o, float* lse, hipStream_t st) {
   FwdArgs a = make_args(p, seg);
   const int nblocks = p.B * p.Hq * p.nqb * ((p.Bq + 63) / 64);
-  ProfScope ps(HGA_K_FWD, st);
-  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3(nblocks), dim3(64), 0, st, (const float*)q,
+  HGA_LAUNCH(HGA_K_FWD, (fwd_f32_kernel<D>), dim3(nblocks), dim3(64), 0, st, (const float*)q,
                      (const float*)k, (const float*)v, sel, (float*)o, lse, a, p.scale);
   return hipGetLastError();
 }

@@ -7,6 +7,7 @@
 //        d'optimisation avec attention globale hiérarchique », sns.style
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -72,15 +73,25 @@ float* decode_score_ws(const Prob& p, void* ws);
 int decode_max_rows();  // limit of G * n
 
 // ---- profiling hooks (no-ops unless hga_profile_begin() was called) -----
-void prof_mark_begin(int kclass, hipStream_t st);
-void prof_mark_end(int kclass, hipStream_t st);
+// While kernel class kclass is profiled, returns true with a start / stop
+// event pair for one launch (owned by the profiler until hga_profile_end).
+bool prof_events(int kclass, hipEvent_t* start, hipEvent_t* stop);
 
-struct ProfScope {
-  int c;
-  hipStream_t s;
-  ProfScope(int cls, hipStream_t st) : c(cls), s(st) { prof_mark_begin(c, s); }
-  ~ProfScope() { prof_mark_end(c, s); }
-};
+}  // namespace hga
+
+// Launches a kernel of class kc.  When that class is profiled, the dispatch
+// itself stamps the start / stop events (hipExtLaunchKernelGGL), so timing
+// adds no event packets, and no gaps, between kernels on the stream.
+#define HGA_LAUNCH(kc, kern, grid, block, shm, st, ...)                                       \
+  do {                                                                                        \
+    hipEvent_t hga_ev0_ = nullptr, hga_ev1_ = nullptr;                                        \
+    if (::hga::prof_events((kc), &hga_ev0_, &hga_ev1_))                                       \
+      hipExtLaunchKernelGGL(kern, grid, block, shm, st, hga_ev0_, hga_ev1_, 0, __VA_ARGS__);  \
+    else                                                                                      \
+      hipLaunchKernelGGL(kern, grid, block, shm, st, __VA_ARGS__);                            \
+  } while (0)
+
+namespace hga {
 
 }  // namespace hga
 

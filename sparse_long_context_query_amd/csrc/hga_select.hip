@@ -408,8 +408,7 @@ template <typename T, int D>
 hipError_t summarize_t(const Prob& p, const void* k, int b0, int b1, float* summ,
                        hipStream_t st) {
   dim3 grid(b1 - b0, p.Hkv, p.B);
-  ProfScope ps(HGA_K_SUMMARIZE, st);
-  hipLaunchKernelGGL((summarize_kernel<T, D>), grid, dim3(kThreads), 0, st,
+  HGA_LAUNCH(HGA_K_SUMMARIZE, (summarize_kernel<T, D>), grid, dim3(kThreads), 0, st,
                      (const T*)k, summ, p.S, p.Bh, p.Hkv, p.nblk, b0);
   return hipGetLastError();
 }
@@ -424,8 +423,8 @@ hipError_t select_launch(const Prob& p, const void* q, const float* summ, const 
     if (e != hipSuccess) return e;
   }
   dim3 grid(units, p.Hkv, p.B);
-  ProfScope ps(HGA_K_SELECT, st);
-  hipLaunchKernelGGL((select_kernel<T, D, E>), grid, dim3(kThreads), shm, st, (const T*)q, summ,
+  HGA_LAUNCH(HGA_K_SELECT, (select_kernel<T, D, E>), grid, dim3(kThreads), shm, st,
+             (const T*)q, summ,
                      sel, geo, p.K, p.Hq, p.Hkv, p.G, p.nblk);
   return hipGetLastError();
 }
@@ -483,36 +482,39 @@ hipError_t launch_select_decode(const Prob& p, const void* q_new, int n, int t0,
   const SelGeom geo{n, 0, 0, n, 1, 0, t0 / p.Bh};
   const int nb = geo.nb;
   if (nb <= p.K || nb > 1024) return select_any(p, q_new, summ, geo, 1, sel, st);
-  ProfScope ps(HGA_K_SELECT, st);
   const dim3 grid((nb + kThreads - 1) / kThreads, p.Hkv, p.B);
   if (p.dtype == HGA_BF16) {
     if (p.D == 64)
-      hipLaunchKernelGGL((score_kernel<__bf16, 64>), grid, dim3(kThreads), 0, st,
+      HGA_LAUNCH(HGA_K_SELECT, (score_kernel<__bf16, 64>), grid, dim3(kThreads), 0, st,
                          (const __bf16*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk);
     else
-      hipLaunchKernelGGL((score_kernel<__bf16, 128>), grid, dim3(kThreads), 0, st,
+      HGA_LAUNCH(HGA_K_SELECT, (score_kernel<__bf16, 128>), grid, dim3(kThreads), 0, st,
                          (const __bf16*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk);
   } else {
     if (p.D == 64)
-      hipLaunchKernelGGL((score_kernel<float, 64>), grid, dim3(kThreads), 0, st,
+      HGA_LAUNCH(HGA_K_SELECT, (score_kernel<float, 64>), grid, dim3(kThreads), 0, st,
                          (const float*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk);
     else
-      hipLaunchKernelGGL((score_kernel<float, 128>), grid, dim3(kThreads), 0, st,
+      HGA_LAUNCH(HGA_K_SELECT, (score_kernel<float, 128>), grid, dim3(kThreads), 0, st,
                          (const float*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 g1(1, p.Hkv, p.B);
   if (nb <= 64)
-    hipLaunchKernelGGL(topk_kernel<1>, g1, dim3(64), 0, st, scores, sel, nb, p.K, p.Hkv, p.nblk);
+    HGA_LAUNCH(HGA_K_SELECT, topk_kernel<1>, g1, dim3(64), 0, st,
+               scores, sel, nb, p.K, p.Hkv, p.nblk);
   else if (nb <= 128)
-    hipLaunchKernelGGL(topk_kernel<2>, g1, dim3(64), 0, st, scores, sel, nb, p.K, p.Hkv, p.nblk);
+    HGA_LAUNCH(HGA_K_SELECT, topk_kernel<2>, g1, dim3(64), 0, st,
+               scores, sel, nb, p.K, p.Hkv, p.nblk);
   else if (nb <= 256)
-    hipLaunchKernelGGL(topk_kernel<4>, g1, dim3(64), 0, st, scores, sel, nb, p.K, p.Hkv, p.nblk);
+    HGA_LAUNCH(HGA_K_SELECT, topk_kernel<4>, g1, dim3(64), 0, st,
+               scores, sel, nb, p.K, p.Hkv, p.nblk);
   else if (nb <= 512)
-    hipLaunchKernelGGL(topk_kernel<8>, g1, dim3(64), 0, st, scores, sel, nb, p.K, p.Hkv, p.nblk);
+    HGA_LAUNCH(HGA_K_SELECT, topk_kernel<8>, g1, dim3(64), 0, st,
+               scores, sel, nb, p.K, p.Hkv, p.nblk);
   else
-    hipLaunchKernelGGL(topk_kernel<16>, g1, dim3(64), 0, st, scores, sel, nb, p.K, p.Hkv,
+    HGA_LAUNCH(HGA_K_SELECT, topk_kernel<16>, g1, dim3(64), 0, st, scores, sel, nb, p.K, p.Hkv,
                        p.nblk);
   return hipGetLastError();
 }
@@ -523,8 +525,7 @@ hipError_t launch_gather(const Prob& p, const void* k, const void* v, const int3
   const int row16 = p.D * esz / 16;
   const int nblocks = p.B * p.Hkv * p.nqb * p.K;
   const int nb = seg * p.L / p.Bh;
-  ProfScope ps(HGA_K_GATHER, st);
-  hipLaunchKernelGGL(gather_kernel, dim3(nblocks), dim3(kThreads), 0, st, (const uint4*)k,
+  HGA_LAUNCH(HGA_K_GATHER, gather_kernel, dim3(nblocks), dim3(kThreads), 0, st, (const uint4*)k,
                      (const uint4*)v, sel, (uint4*)ko, (uint4*)vo, p.S, p.Bh, p.K, p.Hkv,
                      p.nqb, p.nqb_all, seg, row16, nb);
   return hipGetLastError();
