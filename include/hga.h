@@ -153,7 +153,9 @@ int hga_attn_bwd(const hga_config* cfg, const void* q, const void* k,
  * earlier steps wrote).  dO, dq, dk, dv may be NULL without HGA_STEP_BWD;
  * lse may be NULL without HGA_STEP_BWD.  ws: hga_workspace_size(cfg,
  * HGA_OP_STEP) bytes. */
-enum { HGA_STEP_BWD = 1 };
+/* HGA_STEP_SUMMARIES_READY: summ already holds every block before the
+ * segment; the step skips its summarize. */
+enum { HGA_STEP_BWD = 1, HGA_STEP_SUMMARIES_READY = 2 };
 int hga_segment_step(const hga_config* cfg, int32_t seg, int32_t flags,
                      const void* q, const void* k, const void* v,
                      const void* dO, float* summ, int32_t* sel, void* o,
@@ -210,10 +212,27 @@ int hga_segment_step_exact(const hga_config* cfg, int32_t seg, const void* q, co
                            void* o, float* lse, void* dq, void* dk, void* dv, float* hist_dk,
                            float* hist_dv, void* ws, size_t ws_bytes, void* stream);
 
+/* The whole segmented pass: hga_summarize over every block a later segment
+ * can select (once, on `stream`), then hga_segment_step for seg = 0 ..
+ * S/L-1 without their summarize.  With stream2 non-NULL the segments
+ * alternate between stream and stream2 (stream2 first waits for the
+ * summaries): each segment reads only the inputs and those summaries and
+ * writes rows of its own, so the results equal the in-order steps' bit for
+ * bit, while one segment's kernels fill the CUs the other's leave idle near
+ * their ends.  When the call returns, everything it enqueued is ordered
+ * before later work on `stream`.  Both streams must be at default priority.
+ * flags: HGA_STEP_BWD or 0.  ws: hga_workspace_size(cfg, HGA_OP_PASS) bytes
+ * (one step workspace per stream).  The library keeps two timing-free HIP
+ * events per calling thread for the hand-offs. */
+int hga_segment_pass(const hga_config* cfg, int32_t flags, const void* q, const void* k,
+                     const void* v, const void* dO, float* summ, int32_t* sel, void* o,
+                     float* lse, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                     void* stream, void* stream2);
+
 /* Workspace bytes for an operation (0 if none is needed), or 0 with
  * hga_last_error() set if the config is invalid. */
 enum { HGA_OP_FWD = 0, HGA_OP_BWD = 1, HGA_OP_STEP = 2, HGA_OP_DECODE = 3,
-       HGA_OP_STEP_EXACT = 4 };
+       HGA_OP_STEP_EXACT = 4, HGA_OP_PASS = 5 };
 size_t hga_workspace_size(const hga_config* cfg, int32_t op);
 
 /* Message of the last failure on this thread ("" if none). */

@@ -27,7 +27,8 @@ HGA_ERR_HIP = -4
 HGA_F32 = 0
 HGA_BF16 = 1
 HGA_STEP_BWD = 1
-HGA_OP_FWD, HGA_OP_BWD, HGA_OP_STEP, HGA_OP_DECODE, HGA_OP_STEP_EXACT = 0, 1, 2, 3, 4
+HGA_OP_FWD, HGA_OP_BWD, HGA_OP_STEP, HGA_OP_DECODE, HGA_OP_STEP_EXACT, HGA_OP_PASS = range(6)
+HGA_STEP_SUMMARIES_READY = 2
 KERNEL_CLASSES = ("summarize", "select", "gather", "fwd", "bwd_pre", "bwd_dq", "bwd_dkdv",
                   "decode", "decode_merge", "bwd_hist")
 
@@ -78,6 +79,8 @@ _SIGNATURES = {
                                     _P, _P, ctypes.c_size_t, _P]),
     "hga_segment_step": (ctypes.c_int, [_CP, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P,
                                         _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "hga_segment_pass": (ctypes.c_int, [_CP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "hga_segment_step_exact": (ctypes.c_int, [_CP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
                                               _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                               _P]),
@@ -296,6 +299,26 @@ def profile_end() -> dict:
     return {name: (ms[i], int(cnt[i])) for i, name in enumerate(KERNEL_CLASSES)}
 
 
+def segment_pass(cfg: Config, q, k, v, summ, sel, o, lse=None, do=None, dq=None, dk=None,
+                 dv=None, ws=None, bwd: bool = True, stream2=None) -> None:
+    """hga_segment_pass on the current stream (and stream2, a torch stream at
+    default priority, when given); ws of workspace_size(cfg, HGA_OP_PASS)."""
+    s = Shapes(cfg)
+    torch = _torch()
+    flags = HGA_STEP_BWD if bwd else 0
+    _check(lib().hga_segment_pass(
+        ctypes.byref(cfg), flags, _ptr(q, "q", s.dt, s.q), _ptr(k, "k", s.dt, s.kv),
+        _ptr(v, "v", s.dt, s.kv), _ptr(do, "do", s.dt, s.q, allow_none=not bwd),
+        _ptr(summ, "summ", torch.float32, s.summ), _ptr(sel, "sel", torch.int32, s.sel),
+        _ptr(o, "o", s.dt, s.q), _ptr(lse, "lse", torch.float32, s.lse, allow_none=not bwd),
+        _ptr(dq, "dq", s.dt, s.q, allow_none=not bwd),
+        _ptr(dk, "dk", s.dt, s.kv, allow_none=not bwd),
+        _ptr(dv, "dv", s.dt, s.kv, allow_none=not bwd),
+        _ptr(ws, "ws", allow_none=not bwd),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(),
+        None if stream2 is None else ctypes.c_void_p(stream2.cuda_stream)))
+
+
 class Buffers:
     """Device tensors of one layer's segmented pass (allocated with torch)."""
 
@@ -311,13 +334,23 @@ class Buffers:
             self.dq = torch.zeros(s.q, dtype=s.dt, device=device)
             self.dk = torch.zeros(s.kv, dtype=s.dt, device=device)
             self.dv = torch.zeros(s.kv, dtype=s.dt, device=device)
-            nbytes = max(workspace_size(cfg, HGA_OP_STEP), 256)
+            nbytes = max(workspace_size(cfg, HGA_OP_PASS), 256)
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         else:
             self.dq = self.dk = self.dv = self.ws = None
+        self.stream2 = torch.cuda.Stream(device=device)  # default priority
 
-    def run_pass(self, q, k, v, do=None, bwd: bool = True, segments=None) -> None:
-        """hga_segment_step for every segment in order (one layer's pass)."""
+    def run_pass(self, q, k, v, do=None, bwd: bool = True, segments=None,
+                 two_streams: bool = True, per_step: bool = False) -> None:
+        """One layer's segmented pass: hga_segment_pass (segments alternating
+        over two streams, or on the current stream only with two_streams=False),
+        or, with per_step=True or a segment subset, hga_segment_step for each
+        segment in order."""
+        if segments is None and not per_step:
+            segment_pass(self.cfg, q, k, v, self.summ, self.sel, self.o, self.lse, do,
+                         self.dq, self.dk, self.dv, self.ws, bwd=bwd,
+                         stream2=self.stream2 if two_streams else None)
+            return
         nseg = self.cfg.seq_len // self.cfg.seg_len
         for s in (range(nseg) if segments is None else segments):
             segment_step(self.cfg, s, q, k, v, self.summ, self.sel, self.o, self.lse, do,

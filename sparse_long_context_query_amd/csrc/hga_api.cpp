@@ -170,6 +170,9 @@ size_t hga_workspace_size(const hga_config* cfg, int32_t op) {
     case HGA_OP_STEP_EXACT:
       ok();
       return hga::bwd_exact_workspace_bytes(p);
+    case HGA_OP_PASS:
+      ok();
+      return 2 * ((hga::bwd_workspace_bytes(p) + 255) & ~(size_t)255);
     default:
       fail(HGA_ERR_ARG, "unknown op %d", op);
       return 0;
@@ -268,37 +271,45 @@ int hga_attn_bwd(const hga_config* cfg, const void* q, const void* k, const void
   return ok();
 }
 
-int hga_segment_step(const hga_config* cfg, int32_t seg, int32_t flags, const void* q,
-                     const void* k, const void* v, const void* dO, float* summ, int32_t* sel,
-                     void* o, float* lse, void* dq, void* dk, void* dv, void* ws,
-                     size_t ws_bytes, void* stream) {
-  hga::Prob p;
-  int rc = make_prob(cfg, &p);
-  if (rc) return rc;
-  if ((rc = check_seg(p, seg))) return rc;
-  if (flags & ~HGA_STEP_BWD) return fail(HGA_ERR_ARG, "unknown flags 0x%x", flags);
-  const bool bwd = (flags & HGA_STEP_BWD) != 0;
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the step and the pass (everything but seg).
+int check_step_args(const hga::Prob& p, int32_t flags, const void* q, const void* k,
+                    const void* v, const void* dO, const float* summ, const int32_t* sel,
+                    const void* o, const float* lse, const void* dq, const void* dk,
+                    const void* dv, const void* ws, size_t ws_bytes, size_t ws_need) {
+  if (flags & ~(HGA_STEP_BWD | HGA_STEP_SUMMARIES_READY))
+    return fail(HGA_ERR_ARG, "unknown flags 0x%x", flags);
   HGA_REQUIRE(q);
   HGA_REQUIRE(k);
   HGA_REQUIRE(v);
   HGA_REQUIRE(summ);
   HGA_REQUIRE(sel);
   HGA_REQUIRE(o);
-  if (bwd) {
+  if (flags & HGA_STEP_BWD) {
     HGA_REQUIRE(lse);
     HGA_REQUIRE(dO);
     HGA_REQUIRE(dq);
     HGA_REQUIRE(dk);
     HGA_REQUIRE(dv);
     HGA_REQUIRE(ws);
-    const size_t need = hga::bwd_workspace_bytes(p);
-    if (ws_bytes < need)
+    if (ws_bytes < ws_need)
       return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
-                  ws_bytes, need);
+                  ws_bytes, ws_need);
   }
-  hipStream_t st = (hipStream_t)stream;
+  (void)p;
+  return HGA_OK;
+}
+
+// One validated segment step on stream st.
+int run_step(const hga::Prob& p, int32_t seg, int32_t flags, const void* q, const void* k,
+             const void* v, const void* dO, float* summ, int32_t* sel, void* o, float* lse,
+             void* dq, void* dk, void* dv, void* ws, hipStream_t st) {
+  const bool bwd = (flags & HGA_STEP_BWD) != 0;
   hipError_t e;
-  if (seg > 0) {
+  if (seg > 0 && !(flags & HGA_STEP_SUMMARIES_READY)) {
     // blocks closed by segment seg-1 become history of segment seg
     const int b0 = (seg - 1) * p.L / p.Bh, b1 = seg * p.L / p.Bh;
     e = hga::launch_summarize(p, k, b0, b1, summ, st);
@@ -315,6 +326,88 @@ int hga_segment_step(const hga_config* cfg, int32_t seg, int32_t flags, const vo
   if (bwd) {
     e = hga::launch_bwd(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, (float*)ws, st, fuse);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
+  }
+  return HGA_OK;
+}
+
+// Two events per thread for the pass's stream hand-offs, created on first
+// use and kept (timing disabled: they only order work).
+hipError_t pass_events(hipEvent_t* a, hipEvent_t* b) {
+  thread_local hipEvent_t ev[2] = {nullptr, nullptr};
+  for (int i = 0; i < 2; ++i)
+    if (ev[i] == nullptr) {
+      hipError_t e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+    }
+  *a = ev[0];
+  *b = ev[1];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hga_segment_step(const hga_config* cfg, int32_t seg, int32_t flags, const void* q,
+                     const void* k, const void* v, const void* dO, float* summ, int32_t* sel,
+                     void* o, float* lse, void* dq, void* dk, void* dv, void* ws,
+                     size_t ws_bytes, void* stream) {
+  hga::Prob p;
+  int rc = make_prob(cfg, &p);
+  if (rc) return rc;
+  if ((rc = check_seg(p, seg))) return rc;
+  if ((rc = check_step_args(p, flags, q, k, v, dO, summ, sel, o, lse, dq, dk, dv, ws, ws_bytes,
+                            hga::bwd_workspace_bytes(p))))
+    return rc;
+  if ((rc = run_step(p, seg, flags, q, k, v, dO, summ, sel, o, lse, dq, dk, dv, ws,
+                     (hipStream_t)stream)))
+    return rc;
+  return ok();
+}
+
+int hga_segment_pass(const hga_config* cfg, int32_t flags, const void* q, const void* k,
+                     const void* v, const void* dO, float* summ, int32_t* sel, void* o,
+                     float* lse, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                     void* stream, void* stream2) {
+  hga::Prob p;
+  int rc = make_prob(cfg, &p);
+  if (rc) return rc;
+  if (flags & HGA_STEP_SUMMARIES_READY)
+    return fail(HGA_ERR_ARG, "the pass summarizes the history itself");
+  const size_t one = (hga::bwd_workspace_bytes(p) + 255) & ~(size_t)255;
+  const bool two = stream2 != nullptr;
+  if ((rc = check_step_args(p, flags, q, k, v, dO, summ, sel, o, lse, dq, dk, dv, ws, ws_bytes,
+                            two ? 2 * one : one)))
+    return rc;
+  hipStream_t st[2] = {(hipStream_t)stream, two ? (hipStream_t)stream2 : (hipStream_t)stream};
+  void* wsp[2] = {ws, two && ws ? (void*)((char*)ws + one) : ws};
+  const int nseg = p.S / p.L;
+  hipError_t e;
+  // every block a later segment can select, once
+  if (nseg > 1) {
+    e = hga::launch_summarize(p, k, 0, (p.S - p.L) / p.Bh, summ, st[0]);
+    if (e != hipSuccess) return hip_fail(e, "summarize launch");
+  }
+  hipEvent_t ev_in = nullptr, ev_out = nullptr;
+  if (two) {
+    if ((e = pass_events(&ev_in, &ev_out)) != hipSuccess) return hip_fail(e, "event create");
+    if ((e = hipEventRecord(ev_in, st[0])) != hipSuccess) return hip_fail(e, "event record");
+    if ((e = hipStreamWaitEvent(st[1], ev_in, 0)) != hipSuccess)
+      return hip_fail(e, "stream wait");
+  }
+  // segments alternate between the two streams: each reads only the inputs
+  // and the summaries above and writes rows of its own, so one segment's
+  // kernels can fill the CUs the other's leave idle near their ends
+  for (int seg = 0; seg < nseg; ++seg) {
+    const int i = seg & 1;
+    if ((rc = run_step(p, seg, flags | HGA_STEP_SUMMARIES_READY, q, k, v, dO, summ, sel, o, lse,
+                       dq, dk, dv, wsp[i], st[i])))
+      return rc;
+  }
+  if (two) {
+    if ((e = hipEventRecord(ev_out, st[1])) != hipSuccess) return hip_fail(e, "event record");
+    if ((e = hipStreamWaitEvent(st[0], ev_out, 0)) != hipSuccess)
+      return hip_fail(e, "stream wait");
   }
   return ok();
 }

@@ -191,3 +191,22 @@ def test_exact_step_validation(L):
     assert call(f32) == hga.HGA_ERR_UNSUPPORTED and "bf16" in hga.last_error()
     wide = good_cfg(seg_len=2048, query_block=16)  # 128 query blocks per segment (> 64)
     assert call(wide) == hga.HGA_ERR_UNSUPPORTED and "64" in hga.last_error()
+
+
+def test_segment_pass_validation(L):
+    cfg = good_cfg()
+    one = L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_STEP)
+    two = L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_PASS)
+    assert two >= 2 * one
+
+    def call(flags=hga.HGA_STEP_BWD, ws_bytes=two, stream2=FAKE, dq=FAKE):
+        return L.hga_segment_pass(ctypes.byref(cfg), flags, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, dq, FAKE, FAKE, FAKE, ws_bytes, None, stream2)
+
+    assert call(flags=hga.HGA_STEP_BWD | hga.HGA_STEP_SUMMARIES_READY) == hga.HGA_ERR_ARG
+    assert call(flags=8) == hga.HGA_ERR_ARG and "flags" in hga.last_error()
+    assert call(dq=None) == hga.HGA_ERR_ARG and "dq is NULL" in hga.last_error()
+    assert call(ws_bytes=two - 1) == hga.HGA_ERR_WORKSPACE
+    # one stream needs one step workspace only: the size check passes, the
+    # call then fails on the NULL dq it is given
+    assert call(ws_bytes=one, stream2=None, dq=None) == hga.HGA_ERR_ARG

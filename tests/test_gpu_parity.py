@@ -294,3 +294,30 @@ def test_resume_from_segment_state():
     t = 2 * shape.seg_len
     for key in ("o", "lse", "dq", "dk", "dv"):
         assert torch.equal(getattr(second, key)[:, :, t:], getattr(full, key)[:, :, t:]), key
+
+
+# ------------------------------------------------------- pass vs steps
+@pytest.mark.parametrize("shape", [shp(), shp(dtype="f32", head_dim=64, n_q_heads=4,
+                                                n_kv_heads=2), shp(seq_len=128, seg_len=128)])
+@pytest.mark.parametrize("bwd", [True, False])
+def test_two_stream_pass_equals_in_order_steps(shape, bwd):
+    """hga_segment_pass (segments alternating over two streams, summaries
+    computed once) gives bit for bit the results of hga_segment_step called
+    for each segment in order; so does the pass on one stream."""
+    inp = make_inputs(shape, seed=31, with_do=bwd)
+    dev = upload(inp, shape)
+    cfg = hga.Config.from_shape(shape)
+    a, b = hga.Buffers(cfg, bwd=bwd), hga.Buffers(cfg, bwd=bwd)
+    a.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=bwd, two_streams=True)
+    b.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=bwd, per_step=True)
+    torch.cuda.synchronize()
+    keys = ("sel", "o", "lse") + (("dq", "dk", "dv") if bwd else ())
+    for key in keys:
+        assert torch.equal(getattr(a, key), getattr(b, key)), key
+    c = hga.Buffers(cfg, bwd=bwd)
+    c.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=bwd, two_streams=False)
+    torch.cuda.synchronize()
+    for key in keys:
+        assert torch.equal(getattr(c, key), getattr(b, key)), key
+    if not bwd:
+        compare_all(shape, inp, a)
