@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step timing at the 131,072-token inference shape")
     ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--streams", type=int, choices=(1, 2), default=2,
+                    help="streams the timed passes use (1: every kernel of the pass on one "
+                         "stream, as in the kernel-timing loops; used for kernel traces)")
     ap.add_argument("--no-exact", action="store_true",
                     help="skip the exact-gradient (history not detached) pass timing")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -383,7 +386,8 @@ def main():
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
-        buf.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=bwd)
+        buf.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=bwd,
+                     two_streams=args.streams == 2)
     torch.cuda.synchronize()
 
     # one profiled pass with every kernel bracketed: per-class breakdown and
@@ -398,10 +402,13 @@ def main():
     # streams), nothing profiled.  Kernel times come from one-stream passes:
     # in the two-stream pass neighbouring segments' kernels overlap, so a
     # kernel's start-to-stop time would include time it shares the CUs.
-    log(f"[bench] timing {args.steps} passes (two streams)")
-    ms, _ = timed_passes(buf, dev, bwd, args.steps)
-    log(f"[bench] timing {args.steps} passes (one stream)")
-    ms_one, _ = timed_passes(buf, dev, bwd, args.steps, two_streams=False)
+    log(f"[bench] timing {args.steps} passes ({args.streams} stream(s))")
+    ms, _ = timed_passes(buf, dev, bwd, args.steps, two_streams=args.streams == 2)
+    if args.streams == 2:
+        log(f"[bench] timing {args.steps} passes (one stream)")
+        ms_one, _ = timed_passes(buf, dev, bwd, args.steps, two_streams=False)
+    else:
+        ms_one = ms
     log(f"[bench] timing {args.steps} one-stream passes with {dominant}'s dispatches "
         f"stamping events")
     ms_prof, prof = timed_passes(buf, dev, bwd, args.steps, profile_classes=[dominant],
@@ -486,7 +493,7 @@ def main():
                    "n_q_heads": shape.n_q_heads, "n_kv_heads": shape.n_kv_heads,
                    "head_dim": shape.head_dim, "segments": shape.nseg,
                    "step": ("summarize (once) + select+fwd" + ("+bwd" if bwd else "") +
-                            " over all segments, hga_segment_pass on two streams")},
+                            f" over all segments, hga_segment_pass on {args.streams} stream(s)")},
         "roofline": {
             "kernel": dominant,
             "bound": "mfma",
