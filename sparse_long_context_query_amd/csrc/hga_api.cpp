@@ -147,6 +147,22 @@ bool prof_events(int kclass, hipEvent_t* start, hipEvent_t* stop) {
 }
 }  // namespace hga
 
+namespace {
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace of hga_segment_pass.  bf16: the delta rows of every segment
+// (written by the forward launch), then the dK/dV partial sums of every
+// segment (dkdv launch -> dq launch).  f32: one step workspace per stream.
+size_t pass_workspace_bytes(const hga::Prob& p) {
+  const size_t nseg = (size_t)(p.S / p.L);
+  if (p.dtype == HGA_BF16)
+    return nseg * (hga::bwd_delta_bytes(p) + round256(hga::bwd_partial_bytes(p)));
+  return 2 * round256(hga::bwd_workspace_bytes(p));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* hga_last_error(void) { return g_last_error.c_str(); }
@@ -172,7 +188,7 @@ size_t hga_workspace_size(const hga_config* cfg, int32_t op) {
       return hga::bwd_exact_workspace_bytes(p);
     case HGA_OP_PASS:
       ok();
-      return 2 * ((hga::bwd_workspace_bytes(p) + 255) & ~(size_t)255);
+      return pass_workspace_bytes(p);
     default:
       fail(HGA_ERR_ARG, "unknown op %d", op);
       return 0;
@@ -374,13 +390,12 @@ int hga_segment_pass(const hga_config* cfg, int32_t flags, const void* q, const 
   if (rc) return rc;
   if (flags & HGA_STEP_SUMMARIES_READY)
     return fail(HGA_ERR_ARG, "the pass summarizes the history itself");
-  const size_t one = (hga::bwd_workspace_bytes(p) + 255) & ~(size_t)255;
-  const bool two = stream2 != nullptr;
   if ((rc = check_step_args(p, flags, q, k, v, dO, summ, sel, o, lse, dq, dk, dv, ws, ws_bytes,
-                            two ? 2 * one : one)))
+                            pass_workspace_bytes(p))))
     return rc;
+  const bool bwd = (flags & HGA_STEP_BWD) != 0;
+  const bool two = stream2 != nullptr;
   hipStream_t st[2] = {(hipStream_t)stream, two ? (hipStream_t)stream2 : (hipStream_t)stream};
-  void* wsp[2] = {ws, two && ws ? (void*)((char*)ws + one) : ws};
   const int nseg = p.S / p.L;
   hipError_t e;
   // every block a later segment can select, once
@@ -389,20 +404,55 @@ int hga_segment_pass(const hga_config* cfg, int32_t flags, const void* q, const 
     if (e != hipSuccess) return hip_fail(e, "summarize launch");
   }
   hipEvent_t ev_in = nullptr, ev_out = nullptr;
-  if (two) {
-    if ((e = pass_events(&ev_in, &ev_out)) != hipSuccess) return hip_fail(e, "event create");
-    if ((e = hipEventRecord(ev_in, st[0])) != hipSuccess) return hip_fail(e, "event record");
-    if ((e = hipStreamWaitEvent(st[1], ev_in, 0)) != hipSuccess)
-      return hip_fail(e, "stream wait");
-  }
-  // segments alternate between the two streams: each reads only the inputs
-  // and the summaries above and writes rows of its own, so one segment's
-  // kernels can fill the CUs the other's leave idle near their ends
-  for (int seg = 0; seg < nseg; ++seg) {
-    const int i = seg & 1;
-    if ((rc = run_step(p, seg, flags | HGA_STEP_SUMMARIES_READY, q, k, v, dO, summ, sel, o, lse,
-                       dq, dk, dv, wsp[i], st[i])))
-      return rc;
+  if (two && (e = pass_events(&ev_in, &ev_out)) != hipSuccess) return hip_fail(e, "event create");
+
+  if (p.dtype == HGA_BF16) {
+    // every segment's selection (alternating between the streams: each is a
+    // small grid), then one forward launch over all segments (it also writes
+    // each segment's delta rows), one dK/dV launch and one dQ launch over all
+    // segments, with no per-segment launch tails
+    const size_t dstride = hga::bwd_delta_bytes(p);
+    const size_t pstride = round256(hga::bwd_partial_bytes(p));
+    float* delta = (float*)ws;
+    float* part = ws ? (float*)((char*)ws + (size_t)nseg * dstride) : nullptr;
+    if (two) {
+      if ((e = hipEventRecord(ev_in, st[0])) != hipSuccess) return hip_fail(e, "event record");
+      if ((e = hipStreamWaitEvent(st[1], ev_in, 0)) != hipSuccess)
+        return hip_fail(e, "stream wait");
+    }
+    for (int seg = 0; seg < nseg; ++seg) {
+      e = hga::launch_select(p, q, summ, seg, sel, st[seg & 1]);
+      if (e != hipSuccess) return hip_fail(e, "select launch");
+    }
+    if (two) {
+      if ((e = hipEventRecord(ev_out, st[1])) != hipSuccess) return hip_fail(e, "event record");
+      if ((e = hipStreamWaitEvent(st[0], ev_out, 0)) != hipSuccess)
+        return hip_fail(e, "stream wait");
+    }
+    e = hga::launch_fwd_pass(p, q, k, v, sel, 0, nseg, o, lse, st[0], bwd ? dO : nullptr,
+                             bwd ? delta : nullptr, dstride);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+    if (bwd) {
+      e = hga::launch_bwd_pass(p, q, k, v, lse, dO, sel, 0, nseg, dq, dk, dv, delta, dstride,
+                               part, pstride, st[0]);
+      if (e != hipSuccess) return hip_fail(e, "backward launch");
+    }
+    return ok();
+  } else {
+    // f32: whole steps, alternating between the two streams
+    const size_t one = round256(hga::bwd_workspace_bytes(p));
+    void* wsp[2] = {ws, two && ws ? (void*)((char*)ws + one) : ws};
+    if (two) {
+      if ((e = hipEventRecord(ev_in, st[0])) != hipSuccess) return hip_fail(e, "event record");
+      if ((e = hipStreamWaitEvent(st[1], ev_in, 0)) != hipSuccess)
+        return hip_fail(e, "stream wait");
+    }
+    for (int seg = 0; seg < nseg; ++seg) {
+      const int i = seg & 1;
+      if ((rc = run_step(p, seg, flags | HGA_STEP_SUMMARIES_READY, q, k, v, dO, summ, sel, o,
+                         lse, dq, dk, dv, wsp[i], st[i])))
+        return rc;
+    }
   }
   if (two) {
     if ((e = hipEventRecord(ev_out, st[1])) != hipSuccess) return hip_fail(e, "event record");

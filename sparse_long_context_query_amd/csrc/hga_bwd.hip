@@ -28,6 +28,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdArgs {
   int B, S, L, Bh, Bq, K, Hq, Hkv, G, nqb, nqb_all, seg;
+  // whole-pass launches: segments seg .. seg+nseg-1; segment s's delta rows
+  // and dK/dV partial sums sit (s - seg) * dchunk / pchunk floats further on
+  int nseg;
+  int dchunk;
+  long long pchunk;
   int wpu;      // dq: blocks of threads per (b, g, j) unit
   int nq32;     // 32-row query sub-blocks per query block
   float c2;     // scale * log2(e)
@@ -339,6 +344,192 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// a7, bf16 MFMA, whole segmented pass: dq of segments a.seg .. a.seg+a.nseg-1
+// in one launch.  As fwd_pass_kernel: a block of 4 waves owns up to 4 wave
+// rows of one (segment, b, g, j) unit and walks every key tile of the unit
+// itself (local tiles first, then history), two blocks per CU with no
+// common barrier, no halves to add at the end; same work order (contiguous
+// (b, g) ranges per XCD, last segments and query blocks first).  Per wave
+// and 32-key sub-tile the products are those of dq_bf16_kernel.  Before its
+// tiles every block also does its share of dkdv_finish for every segment of
+// the launch (the dkdv launch before it left the partial sums).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void dq_pass_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, const float* __restrict__ lse,
+    const __bf16* __restrict__ dO, const float* __restrict__ delta,
+    const int32_t* __restrict__ sel, __bf16* __restrict__ dq, const float* __restrict__ part_ws,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, int nph, BwdArgs a) {
+  constexpr int TK = 64;
+  constexpr int NKK = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int TILE_B = TK * 2 * D;
+  constexpr int STAGE_B = 2 * TILE_B;  // K tile + V tile
+
+  __shared__ __attribute__((aligned(1024))) unsigned char s_tiles[2][STAGE_B];
+  __shared__ int s_hlist[kMaxTopK];
+  __shared__ int s_hcount;
+
+  int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int c = w % a.wpu;
+  w /= a.wpu;
+  const int j = a.nqb - 1 - w % a.nqb;
+  w /= a.nqb;
+  const int sg = a.nseg - 1 - w % a.nseg;
+  w /= a.nseg;
+  const int g = w % a.Hkv;
+  const int b = w / a.Hkv;
+  const int seg = a.seg + sg;
+  const int t0 = seg * a.L;
+  const int nb = t0 / a.Bh;
+
+  const int tid = threadIdx.x;
+  const int wr = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
+
+  const int nwr = a.G * a.nq32;
+  const int idx = c * 4 + wr;
+  const bool active = idx < nwr;
+  const int qs = idx / a.G, hh = idx % a.G;
+  const int h = g * a.G + hh;
+  const int qfirst = t0 + j * a.Bq + qs * 32;
+  const int nvalid = active ? min(32, a.Bq - qs * 32) : 0;
+  const int wave_qmax = qfirst + nvalid - 1;
+  int blk_qmax = t0;
+  for (int ww = 0; ww < 4; ++ww) {
+    const int id2 = c * 4 + ww;
+    if (id2 < nwr) {
+      const int q2 = id2 / a.G;
+      blk_qmax = max(blk_qmax, t0 + j * a.Bq + q2 * 32 + min(32, a.Bq - q2 * 32) - 1);
+    }
+  }
+
+  // the first local tile's copies and the query-side rows do not depend on
+  // the selection: request them first, so that their latency overlaps the
+  // partial-sum finish and the compaction
+  const int nloc = (blk_qmax - t0) / TK + 1;
+  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.S * (2 * D));
+  {
+    KeySource<TK> loc;
+    loc.init(s_hlist, 0, a.Bh, t0, t0 + a.L);
+    dma_kv_tile<D, TK>(loc, 0, kr, vr, s_tiles[0], s_tiles[0] + TILE_B, wr, lane);
+  }
+  const int tq = qfirst + lq;
+  const bool row_ok = lq < nvalid;
+  const size_t qrow = (size_t)(b * a.Hq + h) * a.S + tq;
+  bf16x8 qreg[NKK], doreg[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    qreg[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(q + qrow * D + 16 * kk + 8 * hi) : bf16x8{};
+    doreg[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(dO + qrow * D + 16 * kk + 8 * hi) : bf16x8{};
+  }
+  const float lse2 = row_ok ? lse[qrow] * kLog2e : 0.f;
+  const float dlt =
+      row_ok ? delta[(size_t)sg * a.dchunk + (size_t)(b * a.Hq + h) * a.L + (tq - t0)] : 0.f;
+
+  for (int s2 = 0; s2 < a.nseg; ++s2) {
+    BwdArgs as = a;
+    as.seg = a.seg + s2;
+    dkdv_finish<D>(part_ws + (size_t)s2 * a.pchunk, dk, dv, as, nph);
+  }
+
+  const int32_t* srow = sel + ((size_t)(b * a.Hkv + g) * a.nqb_all + (size_t)seg * a.nqb + j) * a.K;
+  const int nsel = compact_selection(srow, a.K, nb, s_hlist, &s_hcount);
+  KeySource<TK> src;
+  src.init(s_hlist, nsel, a.Bh, t0, t0 + a.L);
+  const int nht = src.n_hist_tiles;
+  const int ntiles = nht + nloc;
+
+  floatx16 dqacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dqacc[db] = floatx16{};
+  FragOffsets<D> fo;
+  fo.init(lane);
+  drain_vmem_loads();
+  __syncthreads();
+
+  for (int i = 0; i < ntiles; ++i) {
+    const int it = walk_tile(i, nloc, nht);
+    if (i + 1 < ntiles)
+      dma_kv_tile<D, TK>(src, walk_tile(i + 1, nloc, nht), kr, vr, s_tiles[(i + 1) & 1],
+                         s_tiles[(i + 1) & 1] + TILE_B, wr, lane);
+    const bool is_local = it >= nht;
+    const int local_first = t0 + (it - nht) * TK;
+    const bool work = active && (!is_local || local_first <= wave_qmax);
+    if (work) {
+      const unsigned char* kt = s_tiles[i & 1];
+      const unsigned char* vt = kt + TILE_B;
+      const int base = is_local ? local_first : it * TK;
+      const int lim = is_local ? tq : src.nh - 1;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        if (is_local && local_first + 32 * st > wave_qmax) break;  // sub-tile fully masked
+        bf16x8 kf[NKK], vf[NKK];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          kf[kk] = fo.row(kt, st, kk);
+          vf[kk] = fo.row(vt, st, kk);
+        }
+        floatx16 sacc = floatx16{}, pacc = floatx16{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          sacc = mfma32(kf[kk], qreg[kk], sacc);
+          pacc = mfma32(vf[kk], doreg[kk], pacc);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int u = 0; u < NKK - 4; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        const bool need_mask = is_local ? (local_first + 32 * st + 31 > qfirst)
+                                        : ((it * TK + 32 * st + 32) > src.nh);
+        if (need_mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kr_ = base + 32 * st + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (kr_ > lim) sacc[r] = -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(sacc[r], a.c2, -lse2));
+          sacc[r] = p * (pacc[r] - dlt);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int r0 = 8 * ks;
+          const bf16x8 sb = to_bf16x8(sacc[r0], sacc[r0 + 1], sacc[r0 + 2], sacc[r0 + 3],
+                                      sacc[r0 + 4], sacc[r0 + 5], sacc[r0 + 6], sacc[r0 + 7]);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            dqacc[db] = mfma32(fo.tr(kt, 32 * st + 16 * ks, db), sb, dqacc[db]);
+        }
+      }
+    }
+    drain_vmem_loads();
+    __syncthreads();
+  }
+
+  if (!(active && row_ok)) return;
+  __bf16* op = dq + qrow * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      bf16x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(dqacc[db][4 * r4 + e] * a.scale);
+      *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * r4 + 4 * hi) = pk;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // a8, bf16 MFMA: dk/dv of the local keys.  The work of a 32-key tile kt is
 // its (query head, 32-query tile) pairs: query tiles kt.. of every head of
 // the group, G*(nqt-kt) of them, so causality makes early key tiles up to
@@ -615,10 +806,18 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   const int nkt = (a.L + 31) / 32;
   const int nbk = nkt + (nkt & 1);  // blocks per (b, g)
   const int nph = (nkt + 1) / 2;    // mirror pairs (partial-sum slots)
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  int w = xcd_remap(blockIdx.x, gridDim.x);
   const int n = w % nbk;
-  const int g = (w / nbk) % a.Hkv;
-  const int b = w / (nbk * a.Hkv);
+  w /= nbk;
+  // whole-pass launch: one grid over the segments (a.nseg == 1 otherwise)
+  const int sg = a.nseg - 1 - w % a.nseg;
+  w /= a.nseg;
+  const int g = w % a.Hkv;
+  const int b = w / a.Hkv;
+  BwdArgs as = a;
+  as.seg = a.seg + sg;
+  delta += (size_t)sg * a.dchunk;
+  part_ws += (size_t)sg * a.pchunk;
   // block 2p: pairs [0, split) of tile p; block 2p+1: the rest of tile p,
   // then the mirror tile (scalars only, nothing indexed at run time)
   const int p = n >> 1, part = n & 1;
@@ -633,10 +832,10 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   const bool has2 = rest_first && wl > 0;
   float* pp = part_ws + ((size_t)((b * a.Hkv + g) * nph + p) * 2 + part) * 64 * D;
   if (e1 > b1)
-    dkdv_item<D>(q, k, v, lse, dO, delta, dk, dv, pp, a, s_raw, b, g, kt1, b1, e1,
+    dkdv_item<D>(q, k, v, lse, dO, delta, dk, dv, pp, as, s_raw, b, g, kt1, b1, e1,
                  kt1 == p && tile_split);
   if (has2)
-    dkdv_item<D>(q, k, v, lse, dO, delta, dk, dv, pp, a, s_raw, b, g, nkt - 1 - p, 0, wl, false);
+    dkdv_item<D>(q, k, v, lse, dO, delta, dk, dv, pp, as, s_raw, b, g, nkt - 1 - p, 0, wl, false);
 }
 
 
@@ -905,6 +1104,9 @@ BwdArgs make_args(const Prob& p, int seg) {
   a.c2 = p.scale * kLog2e;
   a.scale = p.scale;
   a.hdk = a.hdv = nullptr;
+  a.nseg = 1;
+  a.dchunk = 0;
+  a.pchunk = 0;
   return a;
 }
 
@@ -949,7 +1151,7 @@ template <int D>
 hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
                     const void* o, const float* lse, const void* dO, const int32_t* sel,
                     int seg, void* dq, void* dk, void* dv, float* delta, hipStream_t st,
-                    bool delta_ready, float* hdk, float* hdv) {
+                    bool delta_ready, float* hdk, float* hdv, float* partials) {
   hipError_t e = delta_ready ? hipSuccess : delta_t<__bf16, D>(p, o, dO, seg, delta, st);
   if (e != hipSuccess) return e;
   BwdArgs a = make_args(p, seg);
@@ -957,7 +1159,7 @@ hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
   a.hdv = hdv;
   const int nkt = (p.L + 31) / 32;
   const int nph = (nkt + 1) / 2;
-  float* part_ws = dkdv_partials(p, delta);
+  float* part_ws = partials != nullptr ? partials : dkdv_partials(p, delta);
   {
     // dk/dv first: the dq kernel finishes the key tiles it left as partial sums
     const int nblocks = p.B * p.Hkv * (nkt + (nkt & 1));
@@ -995,6 +1197,35 @@ hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
   return e;
 }
 
+// Backward of segments seg0 .. seg0+nseg-1 in two launches (dkdv, then dq
+// with the partial-sum finish); delta rows and partial sums per segment at
+// the given strides (bytes).
+template <int D>
+hipError_t bwd_pass_bf16(const Prob& p, const void* q, const void* k, const void* v,
+                         const float* lse, const void* dO, const int32_t* sel, int seg0,
+                         int nseg, void* dq, void* dk, void* dv, const float* delta,
+                         size_t dstride, float* partials, size_t pstride, hipStream_t st) {
+  BwdArgs a = make_args(p, seg0);
+  a.nseg = nseg;
+  a.dchunk = (int)(dstride / sizeof(float));
+  a.pchunk = (long long)(pstride / sizeof(float));
+  const int nkt = (p.L + 31) / 32;
+  const int nph = (nkt + 1) / 2;
+  {
+    const int nblocks = p.B * p.Hkv * nseg * (nkt + (nkt & 1));
+    HGA_LAUNCH(HGA_K_BWD_DKDV, (dkdv_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st,
+               (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dO,
+               delta, (__bf16*)dk, (__bf16*)dv, partials, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int nblocks = p.B * p.Hkv * nseg * p.nqb * a.wpu;
+  HGA_LAUNCH(HGA_K_BWD_DQ, (dq_pass_kernel<D>), dim3(nblocks), dim3(256), 0, st,
+             (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dO, delta,
+             sel, (__bf16*)dq, partials, (__bf16*)dk, (__bf16*)dv, nph, a);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t bwd_f32(const Prob& p, const void* q, const void* k, const void* v,
                    const void* o, const float* lse, const void* dO, const int32_t* sel,
@@ -1027,6 +1258,20 @@ size_t bwd_workspace_bytes(const Prob& p) {
   return delta_bytes(p) + partial_bytes(p);
 }
 
+size_t bwd_delta_bytes(const Prob& p) { return delta_bytes(p); }
+
+hipError_t launch_bwd_pass(const Prob& p, const void* q, const void* k, const void* v,
+                           const float* lse, const void* dO, const int32_t* sel, int seg0,
+                           int nseg, void* dq, void* dk, void* dv, const float* delta,
+                           size_t dstride, float* partials, size_t pstride, hipStream_t st) {
+  if (p.dtype != HGA_BF16) return hipErrorInvalidValue;
+  return p.D == 64 ? bwd_pass_bf16<64>(p, q, k, v, lse, dO, sel, seg0, nseg, dq, dk, dv, delta,
+                                       dstride, partials, pstride, st)
+                   : bwd_pass_bf16<128>(p, q, k, v, lse, dO, sel, seg0, nseg, dq, dk, dv, delta,
+                                        dstride, partials, pstride, st);
+}
+size_t bwd_partial_bytes(const Prob& p) { return partial_bytes(p); }
+
 size_t bwd_exact_workspace_bytes(const Prob& p) {
   return delta_bytes(p) + partial_bytes(p) + hist_list_bytes(p);
 }
@@ -1034,12 +1279,12 @@ size_t bwd_exact_workspace_bytes(const Prob& p) {
 hipError_t launch_bwd(const Prob& p, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, const int32_t* sel,
                       int seg, void* dq, void* dk, void* dv, float* delta_ws, hipStream_t st,
-                      bool delta_ready, float* hist_dk, float* hist_dv) {
+                      bool delta_ready, float* hist_dk, float* hist_dv, float* partials) {
   if (p.dtype == HGA_BF16)
     return p.D == 64 ? bwd_bf16<64>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st,
-                                    delta_ready, hist_dk, hist_dv)
+                                    delta_ready, hist_dk, hist_dv, partials)
                      : bwd_bf16<128>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st,
-                                     delta_ready, hist_dk, hist_dv);
+                                     delta_ready, hist_dk, hist_dv, partials);
   return p.D == 64 ? bwd_f32<64>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st)
                    : bwd_f32<128>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st);
 }

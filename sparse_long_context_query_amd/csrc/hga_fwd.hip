@@ -21,10 +21,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct FwdArgs {
-  int S, L, Bh, Bq, K, Hq, Hkv, G, nqb, nqb_all, seg;
+  int B, S, L, Bh, Bq, K, Hq, Hkv, G, nqb, nqb_all, seg;
+  int nseg;   // segments seg .. seg+nseg-1 in one launch (whole-pass kernel)
   int wpu;    // blocks of threads per (b, g, j) unit
   int nq32;   // 32-row query sub-blocks per query block
   float c2;   // softmax scale * log2(e)
+  int dchunk; // whole-pass kernel: floats between the delta rows of two segments
 };
 
 // ---------------------------------------------------------------------------
@@ -306,6 +308,238 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// bf16 MFMA kernel for a whole segmented pass (segments a.seg .. a.seg +
+// a.nseg - 1 in one launch).  Once the selections of every segment exist the
+// segments are independent, so one grid holds all their query blocks and no
+// key split is needed for parallelism: a block of 4 waves owns up to 4 wave
+// rows of one (segment, b, g, j) unit and walks every key tile of that unit
+// itself.  Two such blocks share a CU (64 KB of tiles each), and since they
+// are not tied by a common barrier, one block's softmax and copies run while
+// the other's MFMAs issue.  Per wave and tile the work is that of
+// fwd_bf16_kernel; the final normalisation needs no merge.
+//
+// Work order: blocks are dealt to XCDs in contiguous ranges (xcd_remap), a
+// range covering the units of one (b, g) so that they share an L2; inside
+// it the segments run from the last to the first and the query blocks from
+// the last to the first, the units with the most keys first, so that the
+// launch ends on short units.
+//
+// delta (with dO): row sums of dO * o, segment s's [B, Hq, L] rows at
+// delta + (s - a.seg) * a.dchunk.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_pass_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, const int32_t* __restrict__ sel,
+    __bf16* __restrict__ o, float* __restrict__ lse, const __bf16* __restrict__ dO,
+    float* __restrict__ delta, FwdArgs a) {
+  constexpr int TK = 64;
+  constexpr int NKK = D / 16;  // MFMA k-steps over the head dim
+  constexpr int NDB = D / 32;  // 32-row blocks of O^T
+  constexpr int TILE_B = TK * 2 * D;
+  constexpr int STAGE_B = 2 * TILE_B;  // K tile + V tile
+
+  __shared__ __attribute__((aligned(1024))) unsigned char s_tiles[2][STAGE_B];
+  __shared__ int s_hlist[kMaxTopK];
+  __shared__ int s_hcount;
+
+  int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int c = w % a.wpu;
+  w /= a.wpu;
+  const int j = a.nqb - 1 - w % a.nqb;
+  w /= a.nqb;
+  const int seg = a.seg + a.nseg - 1 - w % a.nseg;
+  w /= a.nseg;
+  const int g = w % a.Hkv;
+  const int b = w / a.Hkv;
+  const int t0 = seg * a.L;
+  const int nb = t0 / a.Bh;
+
+  const int tid = threadIdx.x;
+  const int wr = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
+
+  const int nwr = a.G * a.nq32;
+  const int idx = c * 4 + wr;
+  const bool active = idx < nwr;
+  const int qs = idx / a.G, hh = idx % a.G;
+  const int h = g * a.G + hh;
+  const int qfirst = t0 + j * a.Bq + qs * 32;
+  const int nvalid = active ? min(32, a.Bq - qs * 32) : 0;
+  const int wave_qmax = qfirst + nvalid - 1;
+  int blk_qmax = t0;
+  for (int ww = 0; ww < 4; ++ww) {
+    const int id2 = c * 4 + ww;
+    if (id2 < nwr) {
+      const int q2 = id2 / a.G;
+      blk_qmax = max(blk_qmax, t0 + j * a.Bq + q2 * 32 + min(32, a.Bq - q2 * 32) - 1);
+    }
+  }
+
+  const int tq = qfirst + lq;
+  const bool row_ok = lq < nvalid;
+  bf16x8 qreg[NKK];
+  {
+    const __bf16* qp = q + ((size_t)(b * a.Hq + h) * a.S + tq) * D + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qreg[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * kk) : bf16x8{};
+  }
+
+  const int32_t* srow = sel + ((size_t)(b * a.Hkv + g) * a.nqb_all + (size_t)seg * a.nqb + j) * a.K;
+  const int nsel = compact_selection(srow, a.K, nb, s_hlist, &s_hcount);
+  KeySource<TK> src;
+  src.init(s_hlist, nsel, a.Bh, t0, t0 + a.L);
+  const int ntiles = src.n_hist_tiles + (blk_qmax - t0) / TK + 1;
+
+  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.S * (2 * D));
+  const __amdgpu_buffer_rsrc_t kr_none = make_rsrc(k + kv_base, 0u);
+  const __amdgpu_buffer_rsrc_t vr_none = make_rsrc(v + kv_base, 0u);
+
+  floatx16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  FragOffsets<D> fo;
+  fo.init(lane);
+
+  dma_kv_tile<D, TK>(src, 0, kr, vr, s_tiles[0], s_tiles[0] + TILE_B, wr, lane);
+  drain_vmem_loads();
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const bool copy_next = it + 1 < ntiles;
+    uint32_t coff[TK / (64 / ((2 * D) / 16)) / 4];
+    kv_tile_offsets<D, TK>(src, copy_next ? it + 1 : it, wr, lane, coff);
+    const __amdgpu_buffer_rsrc_t kr_n = copy_next ? kr : kr_none;
+    const __amdgpu_buffer_rsrc_t vr_n = copy_next ? vr : vr_none;
+    unsigned char* const knext = s_tiles[(it + 1) & 1];
+
+    const bool is_local = it >= src.n_hist_tiles;
+    const int local_first = t0 + (it - src.n_hist_tiles) * TK;
+    const bool work = active && (!is_local || local_first <= wave_qmax);
+    if (!work) kv_tile_issue<D, TK>(kr_n, vr_n, coff, knext, knext + TILE_B, wr);
+    if (work) {
+      const unsigned char* kt = s_tiles[it & 1];
+      const unsigned char* vt = kt + TILE_B;
+      bf16x8 kf[NKK][2];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) kf[kk][st] = fo.row(kt, st, kk);
+      floatx16 sacc[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) sacc[st] = floatx16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) sacc[st] = mfma32(kf[kk][st], qreg[kk], sacc[st]);
+      }
+      kv_tile_issue<D, TK>(kr_n, vr_n, coff, knext, knext + TILE_B, wr);
+      constexpr int NCP = 2 * (TK / (64 / ((2 * D) / 16)) / 4);  // copy instructions
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NKK, 0);
+#pragma unroll
+      for (int u = 0; u < NCP; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NKK / NCP, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      const bool need_mask = is_local ? (local_first + TK - 1 > qfirst)
+                                      : ((it + 1) * TK > src.nh);
+      if (need_mask) {
+        const int base = is_local ? local_first : it * TK;
+        const int lim = is_local ? tq : src.nh - 1;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kr_ = base + 32 * st + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (kr_ > lim) sacc[st][r] = -INFINITY;
+          }
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[st][r]);
+      mt = pair_max(mt) * a.c2;
+      const bool raise = mt > m_run + kRescale;
+      if (__ballot(raise)) {
+        const float m_new = raise ? mt : m_run;
+        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      float rs = 0.f;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(sacc[st][r], a.c2, -m_use));
+          sacc[st][r] = p;
+          rs += p;
+        }
+      }
+      l_run += rs;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int r0 = 8 * ks;
+          const bf16x8 pb = to_bf16x8(sacc[st][r0], sacc[st][r0 + 1], sacc[st][r0 + 2],
+                                      sacc[st][r0 + 3], sacc[st][r0 + 4], sacc[st][r0 + 5],
+                                      sacc[st][r0 + 6], sacc[st][r0 + 7]);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            oacc[db] = mfma32(fo.tr(vt, 32 * st + 16 * ks, db), pb, oacc[db]);
+        }
+      }
+    }
+    drain_vmem_loads();  // the next tile has landed in LDS
+    __syncthreads();
+  }
+
+  if (!(active && row_ok)) return;
+  l_run = pair_sum(l_run);
+  const size_t orow = ((size_t)(b * a.Hq + h) * a.S + tq) * D;
+  const bool want_delta = delta != nullptr;
+  bf16x4 dog[NDB][4];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      dog[db][r4] = want_delta
+                        ? *reinterpret_cast<const bf16x4*>(dO + orow + 32 * db + 8 * r4 + 4 * hi)
+                        : bf16x4{};
+  const float inv = 1.f / l_run;
+  __bf16* op = o + orow;
+  float dsum = 0.f;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      bf16x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(oacc[db][4 * r4 + e] * inv);
+      *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * r4 + 4 * hi) = pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsum += (float)pk[e] * (float)dog[db][r4][e];
+    }
+  }
+  if (lse != nullptr && hi == 0)
+    lse[(size_t)(b * a.Hq + h) * a.S + tq] = (m_run + log2f(l_run)) * kLn2;
+  if (want_delta) {
+    dsum = pair_sum(dsum);
+    if (hi == 0)
+      delta[(size_t)(seg - a.seg) * a.dchunk + (size_t)(b * a.Hq + h) * a.L + (tq - t0)] = dsum;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // float32 kernel (reference-precision path; plain VALU).  One wave per
 // (b, h, 64-query chunk of a query block); one query per lane; key tiles of
 // 32 rows staged in LDS and broadcast to the lanes.  Online softmax per key
@@ -395,10 +629,25 @@ FwdArgs make_args(const Prob& p, int seg) {
   FwdArgs a;
   a.S = p.S; a.L = p.L; a.Bh = p.Bh; a.Bq = p.Bq; a.K = p.K; a.Hq = p.Hq; a.Hkv = p.Hkv;
   a.G = p.G; a.nqb = p.nqb; a.nqb_all = p.nqb_all; a.seg = seg;
+  a.B = p.B; a.nseg = 1; a.dchunk = 0;
   a.nq32 = (p.Bq + 31) / 32;
   a.wpu = (p.G * a.nq32 + 3) / 4;
   a.c2 = p.scale * kLog2e;
   return a;
+}
+
+template <int D>
+hipError_t fwd_pass_bf16(const Prob& p, const void* q, const void* k, const void* v,
+                         const int32_t* sel, int seg0, int nseg, void* o, float* lse,
+                         hipStream_t st, const void* dO, float* delta, size_t delta_stride) {
+  FwdArgs a = make_args(p, seg0);
+  a.nseg = nseg;
+  a.dchunk = (int)(delta_stride / sizeof(float));
+  const int nblocks = p.B * p.Hkv * nseg * p.nqb * a.wpu;
+  HGA_LAUNCH(HGA_K_FWD, (fwd_pass_kernel<D>), dim3(nblocks), dim3(256), 0, st,
+             (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, sel, (__bf16*)o, lse,
+             (const __bf16*)dO, delta, a);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -426,6 +675,17 @@ hipError_t fwd_f32(const Prob& p, const void* q, const void* k, const void* v,
 }  // namespace
 
 bool fused_delta(const Prob& p) { return p.dtype == HGA_BF16; }
+
+hipError_t launch_fwd_pass(const Prob& p, const void* q, const void* k, const void* v,
+                           const int32_t* sel, int seg0, int nseg, void* o, float* lse,
+                           hipStream_t st, const void* dO, float* delta, size_t delta_stride) {
+  if (p.dtype != HGA_BF16) return hipErrorInvalidValue;
+  if (dO == nullptr) delta = nullptr;
+  return p.D == 64 ? fwd_pass_bf16<64>(p, q, k, v, sel, seg0, nseg, o, lse, st, dO, delta,
+                                       delta_stride)
+                   : fwd_pass_bf16<128>(p, q, k, v, sel, seg0, nseg, o, lse, st, dO, delta,
+                                        delta_stride);
+}
 
 hipError_t launch_fwd(const Prob& p, const void* q, const void* k, const void* v,
                       const int32_t* sel, int seg, void* o, float* lse, hipStream_t st,

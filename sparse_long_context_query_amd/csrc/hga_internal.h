@@ -46,6 +46,12 @@ hipError_t launch_fwd(const Prob& p, const void* q, const void* k,
                       const void* v, const int32_t* sel, int seg, void* o,
                       float* lse, hipStream_t st, const void* dO = nullptr,
                       float* delta = nullptr);
+// Forward of segments seg0 .. seg0+nseg-1 in one launch (bf16 only; their
+// selections must exist).  With dO, segment s's delta rows [B, Hq, L] go to
+// delta + (s - seg0) * delta_stride bytes.
+hipError_t launch_fwd_pass(const Prob& p, const void* q, const void* k, const void* v,
+                           const int32_t* sel, int seg0, int nseg, void* o, float* lse,
+                           hipStream_t st, const void* dO, float* delta, size_t delta_stride);
 // hist_dk / hist_dv (exact gradient, bf16 only): fp32 [B, Hkv, S, D] sums
 // of the gradient later segments gave each key; the backward adds them to
 // its own rows and adds its queries' part to the history rows it selected.
@@ -54,8 +60,20 @@ hipError_t launch_bwd(const Prob& p, const void* q, const void* k,
                       const void* dO, const int32_t* sel, int seg, void* dq,
                       void* dk, void* dv, float* delta_ws, hipStream_t st,
                       bool delta_ready = false, float* hist_dk = nullptr,
-                      float* hist_dv = nullptr);
+                      float* hist_dv = nullptr, float* partials = nullptr);
+// Backward of segments seg0 .. seg0+nseg-1 in one dkdv and one dq launch
+// (bf16 only; every segment's forward done, its delta rows [B, Hq, L] at
+// delta + (s - seg0) * dstride bytes; dK/dV partial sums of segment s at
+// partials + (s - seg0) * pstride bytes, pstride >= bwd_partial_bytes).
+hipError_t launch_bwd_pass(const Prob& p, const void* q, const void* k, const void* v,
+                           const float* lse, const void* dO, const int32_t* sel, int seg0,
+                           int nseg, void* dq, void* dk, void* dv, const float* delta,
+                           size_t dstride, float* partials, size_t pstride, hipStream_t st);
 size_t bwd_workspace_bytes(const Prob& p);
+// Workspace parts of the backward: delta rows of one segment, and the dK/dV
+// partial sums (launch_bwd's `partials`, else right after delta_ws).
+size_t bwd_delta_bytes(const Prob& p);
+size_t bwd_partial_bytes(const Prob& p);
 size_t bwd_exact_workspace_bytes(const Prob& p);
 
 // Decode step: selection of the n new tokens of q_new [B, Hq, n, D] (one

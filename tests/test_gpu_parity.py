@@ -283,8 +283,9 @@ def test_resume_from_segment_state():
     shape = WORKLOADS["qwen3_2k"]
     inp = make_inputs(shape, seed=0)
     dev = upload(inp, shape)
-    full = run_pass(shape, dev)
     cfg = hga.Config.from_shape(shape)
+    full = hga.Buffers(cfg)
+    full.run_pass(dev["q"], dev["k"], dev["v"], dev["do"], per_step=True)
     first = hga.Buffers(cfg)
     first.run_pass(dev["q"], dev["k"], dev["v"], dev["do"], segments=range(0, 2))
     second = hga.Buffers(cfg)
@@ -300,24 +301,27 @@ def test_resume_from_segment_state():
 @pytest.mark.parametrize("shape", [shp(), shp(dtype="f32", head_dim=64, n_q_heads=4,
                                                 n_kv_heads=2), shp(seq_len=128, seg_len=128)])
 @pytest.mark.parametrize("bwd", [True, False])
-def test_two_stream_pass_equals_in_order_steps(shape, bwd):
-    """hga_segment_pass (segments alternating over two streams, summaries
-    computed once) gives bit for bit the results of hga_segment_step called
-    for each segment in order; so does the pass on one stream."""
+def test_pass_streams_and_steps(shape, bwd):
+    """hga_segment_pass gives the same results bit for bit on two streams
+    and on one; hga_segment_step called for each segment in order gives the
+    same selections and, within the dtype's tolerance, the same outputs
+    (the bf16 pass runs its forward as one launch over all segments, whose
+    blocks walk all keys of a unit themselves, so its float sums are added
+    in another order); both match the oracle."""
     inp = make_inputs(shape, seed=31, with_do=bwd)
     dev = upload(inp, shape)
     cfg = hga.Config.from_shape(shape)
-    a, b = hga.Buffers(cfg, bwd=bwd), hga.Buffers(cfg, bwd=bwd)
+    a, b, c = (hga.Buffers(cfg, bwd=bwd) for _ in range(3))
     a.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=bwd, two_streams=True)
     b.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=bwd, per_step=True)
+    c.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=bwd, two_streams=False)
     torch.cuda.synchronize()
     keys = ("sel", "o", "lse") + (("dq", "dk", "dv") if bwd else ())
     for key in keys:
-        assert torch.equal(getattr(a, key), getattr(b, key)), key
-    c = hga.Buffers(cfg, bwd=bwd)
-    c.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=bwd, two_streams=False)
-    torch.cuda.synchronize()
-    for key in keys:
-        assert torch.equal(getattr(c, key), getattr(b, key)), key
-    if not bwd:
-        compare_all(shape, inp, a)
+        assert torch.equal(getattr(a, key), getattr(c, key)), key
+    assert torch.equal(a.sel, b.sel)
+    tol = TOL[shape.dtype]
+    for key in keys[1:]:
+        assert_close(key, to_np(getattr(a, key)), to_np(getattr(b, key)).astype(np.float64), tol)
+    compare_all(shape, inp, a)
+    compare_all(shape, inp, b)
