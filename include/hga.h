@@ -216,21 +216,25 @@ int hga_segment_step_exact(const hga_config* cfg, int32_t seg, const void* q, co
  * can select (once, on `stream`), then select, forward and (flags
  * HGA_STEP_BWD) backward of seg = 0 .. S/L-1.  Once the summaries exist the
  * segments are independent: each reads only the inputs and those summaries
- * and writes rows of its own.  bf16: every segment's selection, then ONE
- * forward launch over all segments (no per-segment launch tails; each
- * block of threads walks all keys of its query rows, so the float sums are
- * added in another order than hga_segment_step's: equal within rounding,
- * not bit for bit), then each segment's backward.  f32: hga_segment_step
- * per segment.  With stream2 non-NULL the per-segment work alternates
- * between stream and stream2 (stream2 first waits for the work before it),
- * which fills the CUs one segment's kernels leave idle near their ends;
- * results equal the one-stream pass's bit for bit.  When the call returns,
- * everything it enqueued is ordered before later work on `stream`.  Both
- * streams must be at default priority.  flags: HGA_STEP_BWD or 0.  ws:
- * hga_workspace_size(cfg, HGA_OP_PASS) bytes (needed with HGA_STEP_BWD;
- * bf16: every segment's delta rows and two sets of dK/dV partial sums).
- * The library keeps two timing-free HIP events per calling thread for the
- * hand-offs. */
+ * and writes rows of its own.
+ *   - bf16: one selection launch, one forward launch (which also writes
+ *     every segment's delta rows), one dK/dV launch and one dQ launch, each
+ *     over all segments, so no launch has a per-segment tail.  The forward
+ *     and dQ blocks walk all keys of their query rows themselves, so float
+ *     sums are added in another order than in hga_segment_step: equal within
+ *     rounding, not bit for bit (selections are identical).  stream2 is not
+ *     used.
+ *   - f32: hga_segment_step per segment (without its summarize); with
+ *     stream2 non-NULL the segments alternate between stream and stream2
+ *     (stream2 first waits for the summaries), which fills the CUs one
+ *     segment's kernels leave idle near their ends; results equal the
+ *     one-stream pass's bit for bit.
+ * When the call returns, everything it enqueued is ordered before later work
+ * on `stream`.  Both streams must be at default priority.  flags:
+ * HGA_STEP_BWD or 0.  ws: hga_workspace_size(cfg, HGA_OP_PASS) bytes
+ * (needed with HGA_STEP_BWD; bf16: every segment's delta rows and dK/dV
+ * partial sums).  The library keeps two timing-free HIP events per calling
+ * thread for the f32 hand-offs. */
 int hga_segment_pass(const hga_config* cfg, int32_t flags, const void* q, const void* k,
                      const void* v, const void* dO, float* summ, int32_t* sel, void* o,
                      float* lse, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,

@@ -403,32 +403,17 @@ int hga_segment_pass(const hga_config* cfg, int32_t flags, const void* q, const 
     e = hga::launch_summarize(p, k, 0, (p.S - p.L) / p.Bh, summ, st[0]);
     if (e != hipSuccess) return hip_fail(e, "summarize launch");
   }
-  hipEvent_t ev_in = nullptr, ev_out = nullptr;
-  if (two && (e = pass_events(&ev_in, &ev_out)) != hipSuccess) return hip_fail(e, "event create");
-
   if (p.dtype == HGA_BF16) {
-    // every segment's selection (alternating between the streams: each is a
-    // small grid), then one forward launch over all segments (it also writes
-    // each segment's delta rows), one dK/dV launch and one dQ launch over all
-    // segments, with no per-segment launch tails
+    // one selection launch, one forward launch (it also writes each
+    // segment's delta rows), one dK/dV launch and one dQ launch, each over
+    // all segments: no per-segment launch tails, and the second stream is
+    // not needed
     const size_t dstride = hga::bwd_delta_bytes(p);
     const size_t pstride = round256(hga::bwd_partial_bytes(p));
     float* delta = (float*)ws;
     float* part = ws ? (float*)((char*)ws + (size_t)nseg * dstride) : nullptr;
-    if (two) {
-      if ((e = hipEventRecord(ev_in, st[0])) != hipSuccess) return hip_fail(e, "event record");
-      if ((e = hipStreamWaitEvent(st[1], ev_in, 0)) != hipSuccess)
-        return hip_fail(e, "stream wait");
-    }
-    for (int seg = 0; seg < nseg; ++seg) {
-      e = hga::launch_select(p, q, summ, seg, sel, st[seg & 1]);
-      if (e != hipSuccess) return hip_fail(e, "select launch");
-    }
-    if (two) {
-      if ((e = hipEventRecord(ev_out, st[1])) != hipSuccess) return hip_fail(e, "event record");
-      if ((e = hipStreamWaitEvent(st[0], ev_out, 0)) != hipSuccess)
-        return hip_fail(e, "stream wait");
-    }
+    e = hga::launch_select_pass(p, q, summ, 0, nseg, sel, st[0]);
+    if (e != hipSuccess) return hip_fail(e, "select launch");
     e = hga::launch_fwd_pass(p, q, k, v, sel, 0, nseg, o, lse, st[0], bwd ? dO : nullptr,
                              bwd ? delta : nullptr, dstride);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
@@ -438,26 +423,25 @@ int hga_segment_pass(const hga_config* cfg, int32_t flags, const void* q, const 
       if (e != hipSuccess) return hip_fail(e, "backward launch");
     }
     return ok();
-  } else {
-    // f32: whole steps, alternating between the two streams
-    const size_t one = round256(hga::bwd_workspace_bytes(p));
-    void* wsp[2] = {ws, two && ws ? (void*)((char*)ws + one) : ws};
-    if (two) {
-      if ((e = hipEventRecord(ev_in, st[0])) != hipSuccess) return hip_fail(e, "event record");
-      if ((e = hipStreamWaitEvent(st[1], ev_in, 0)) != hipSuccess)
-        return hip_fail(e, "stream wait");
-    }
-    for (int seg = 0; seg < nseg; ++seg) {
-      const int i = seg & 1;
-      if ((rc = run_step(p, seg, flags | HGA_STEP_SUMMARIES_READY, q, k, v, dO, summ, sel, o,
-                         lse, dq, dk, dv, wsp[i], st[i])))
-        return rc;
-    }
+  }
+  // f32: whole steps, alternating between the two streams
+  const size_t one = round256(hga::bwd_workspace_bytes(p));
+  void* wsp[2] = {ws, two && ws ? (void*)((char*)ws + one) : ws};
+  hipEvent_t ev_in = nullptr, ev_out = nullptr;
+  if (two) {
+    if ((e = pass_events(&ev_in, &ev_out)) != hipSuccess) return hip_fail(e, "event create");
+    if ((e = hipEventRecord(ev_in, st[0])) != hipSuccess) return hip_fail(e, "event record");
+    if ((e = hipStreamWaitEvent(st[1], ev_in, 0)) != hipSuccess) return hip_fail(e, "stream wait");
+  }
+  for (int seg = 0; seg < nseg; ++seg) {
+    const int i = seg & 1;
+    if ((rc = run_step(p, seg, flags | HGA_STEP_SUMMARIES_READY, q, k, v, dO, summ, sel, o, lse,
+                       dq, dk, dv, wsp[i], st[i])))
+      return rc;
   }
   if (two) {
     if ((e = hipEventRecord(ev_out, st[1])) != hipSuccess) return hip_fail(e, "event record");
-    if ((e = hipStreamWaitEvent(st[0], ev_out, 0)) != hipSuccess)
-      return hip_fail(e, "stream wait");
+    if ((e = hipStreamWaitEvent(st[0], ev_out, 0)) != hipSuccess) return hip_fail(e, "stream wait");
   }
   return ok();
 }

@@ -35,6 +35,9 @@ hipError_t launch_summarize(const Prob& p, const void* k, int blk_begin,
                             int blk_end, float* summ, hipStream_t st);
 hipError_t launch_select(const Prob& p, const void* q, const float* summ,
                          int seg, int32_t* sel, hipStream_t st);
+// Selection of segments seg0 .. seg0+nseg-1 in one launch.
+hipError_t launch_select_pass(const Prob& p, const void* q, const float* summ, int seg0,
+                              int nseg, int32_t* sel, hipStream_t st);
 hipError_t launch_gather(const Prob& p, const void* k, const void* v,
                          const int32_t* sel, int seg, void* ko, void* vo,
                          hipStream_t st);

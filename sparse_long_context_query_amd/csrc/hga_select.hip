@@ -25,6 +25,12 @@ struct SelGeom {
   int qS, q0, qstep, nrows;
   int out_units, out_j0;
   int nb;
+  // several segments in one launch (per_seg > 0): unit u is query block
+  // u % per_seg of segment seg0 + u / per_seg, whose rows start at
+  // seg * seg_len and whose candidates are its seg * seg_len / bh closed
+  // blocks; q0, out_j0 and nb above are then per unit, nb giving the most
+  // candidates of any unit
+  int per_seg, seg0, seg_len, bh;
 };
 
 // ---------------------------------------------------------------------------
@@ -241,7 +247,15 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   __shared__ float s_score[kMaxCandidates];
   __shared__ unsigned long long s_thresh;
 
-  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  int j = blockIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z;
+  if (geo.per_seg > 0) {
+    const int seg = geo.seg0 + j / geo.per_seg;
+    j %= geo.per_seg;
+    geo.q0 = seg * geo.seg_len;
+    geo.out_j0 = seg * geo.per_seg;
+    geo.nb = geo.q0 / geo.bh;
+  }
   const int nb = geo.nb;
   int32_t* out = sel + ((size_t)(b * Hkv + g) * geo.out_units + geo.out_j0 + j) * K;
 
@@ -471,15 +485,24 @@ hipError_t launch_select(const Prob& p, const void* q, const float* summ, int se
                          int32_t* sel, hipStream_t st) {
   // unit j = query block j of the segment, rows [t0 + j Bq, t0 + (j+1) Bq)
   const int t0 = seg * p.L;
-  const SelGeom geo{p.S, t0, p.Bq, p.Bq, p.nqb_all, seg * p.nqb, t0 / p.Bh};
+  const SelGeom geo{p.S, t0, p.Bq, p.Bq, p.nqb_all, seg * p.nqb, t0 / p.Bh, 0, 0, 0, 0};
   return select_any(p, q, summ, geo, p.nqb, sel, st);
+}
+
+hipError_t launch_select_pass(const Prob& p, const void* q, const float* summ, int seg0,
+                              int nseg, int32_t* sel, hipStream_t st) {
+  // units: query block j of segment seg0 + s is unit s * nqb + j; the search
+  // is sized for the last segment, which has the most candidates
+  const int last = seg0 + nseg - 1;
+  const SelGeom geo{p.S, 0, p.Bq, p.Bq, p.nqb_all, 0, last * p.L / p.Bh, p.nqb, seg0, p.L, p.Bh};
+  return select_any(p, q, summ, geo, p.nqb * nseg, sel, st);
 }
 
 hipError_t launch_select_decode(const Prob& p, const void* q_new, int n, int t0,
                                 const float* summ, int32_t* sel, float* scores,
                                 hipStream_t st) {
   // one unit: the n new tokens of q_new [B, Hq, n, D]; sel is [B, Hkv, k]
-  const SelGeom geo{n, 0, 0, n, 1, 0, t0 / p.Bh};
+  const SelGeom geo{n, 0, 0, n, 1, 0, t0 / p.Bh, 0, 0, 0, 0};
   const int nb = geo.nb;
   if (nb <= p.K || nb > 1024) return select_any(p, q_new, summ, geo, 1, sel, st);
   const dim3 grid((nb + kThreads - 1) / kThreads, p.Hkv, p.B);
