@@ -404,6 +404,11 @@ __global__ __launch_bounds__(256, 2) void fwd_pass_kernel(
   float m_run = -INFINITY, l_run = 0.f;
   FragOffsets<D> fo;
   fo.init(lane);
+  // when every tile is a run of consecutive rows (tpb > 0), the copies take
+  // loop-invariant lane offsets inside a resource placed at the tile's first
+  // row, built with scalar instructions per tile
+  uint32_t loff[TK / (64 / ((2 * D) / 16)) / 4];
+  contiguous_tile_offsets<D, TK>(wr, lane, loff);
 
   dma_kv_tile<D, TK>(src, 0, kr, vr, s_tiles[0], s_tiles[0] + TILE_B, wr, lane);
   drain_vmem_loads();
@@ -412,9 +417,21 @@ __global__ __launch_bounds__(256, 2) void fwd_pass_kernel(
   for (int it = 0; it < ntiles; ++it) {
     const bool copy_next = it + 1 < ntiles;
     uint32_t coff[TK / (64 / ((2 * D) / 16)) / 4];
-    kv_tile_offsets<D, TK>(src, copy_next ? it + 1 : it, wr, lane, coff);
-    const __amdgpu_buffer_rsrc_t kr_n = copy_next ? kr : kr_none;
-    const __amdgpu_buffer_rsrc_t vr_n = copy_next ? vr : vr_none;
+    __amdgpu_buffer_rsrc_t kr_n, vr_n;
+    if (src.tpb > 0) {
+      // rows past the segment end (last local tile) are read as they are
+      // and masked; past the sequence end the resource returns zeros
+      const int base = src.tile_base(copy_next ? it + 1 : it);
+      const uint32_t nbytes = copy_next ? (uint32_t)(a.S - base) * (2 * D) : 0u;
+      kr_n = make_rsrc(k + kv_base + (size_t)base * D, nbytes);
+      vr_n = make_rsrc(v + kv_base + (size_t)base * D, nbytes);
+#pragma unroll
+      for (int n = 0; n < TK / (64 / ((2 * D) / 16)) / 4; ++n) coff[n] = loff[n];
+    } else {
+      kv_tile_offsets<D, TK>(src, copy_next ? it + 1 : it, wr, lane, coff);
+      kr_n = copy_next ? kr : kr_none;
+      vr_n = copy_next ? vr : vr_none;
+    }
     unsigned char* const knext = s_tiles[(it + 1) & 1];
 
     const bool is_local = it >= src.n_hist_tiles;

@@ -263,6 +263,22 @@ __device__ __forceinline__ void kv_tile_offsets(const KeySource<TK>& src, int it
   }
 }
 
+// Lane byte offsets of kv_tile_offsets for a tile of consecutive rows
+// starting at row 0 (loop-invariant; the tile's first row goes into the
+// buffer resource instead).
+template <int D, int TK>
+__device__ __forceinline__ void contiguous_tile_offsets(int wr, int lane,
+                                                        uint32_t (&off)[TK / (64 / ((2 * D) / 16)) / 4]) {
+  constexpr int CPR = (2 * D) / 16;
+  constexpr int RPI = 64 / CPR;
+  constexpr int NI = TK / RPI;
+#pragma unroll
+  for (int n = 0; n < NI / 4; ++n) {
+    const int row = (wr + 4 * n) * RPI + lane / CPR;
+    off[n] = (uint32_t)row * (2 * D) + ((lane % CPR) ^ swz<D>(row)) * 16;
+  }
+}
+
 template <int D, int TK>
 __device__ __forceinline__ void kv_tile_issue(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                               const uint32_t (&off)[TK / (64 / ((2 * D) / 16)) / 4],
