@@ -302,7 +302,7 @@ def profile_end() -> dict:
 def segment_pass(cfg: Config, q, k, v, summ, sel, o, lse=None, do=None, dq=None, dk=None,
                  dv=None, ws=None, bwd: bool = True, stream2=None) -> None:
     """hga_segment_pass on the current stream (and stream2, a torch stream at
-    default priority, when given); ws of workspace_size(cfg, HGA_OP_PASS)."""
+    default priority, when given); ws of workspace_size(cfg, HGA_OP_PASS) bytes."""
     s = Shapes(cfg)
     torch = _torch()
     flags = HGA_STEP_BWD if bwd else 0
@@ -334,7 +334,8 @@ class Buffers:
             self.dq = torch.zeros(s.q, dtype=s.dt, device=device)
             self.dk = torch.zeros(s.kv, dtype=s.dt, device=device)
             self.dv = torch.zeros(s.kv, dtype=s.dt, device=device)
-            nbytes = max(workspace_size(cfg, HGA_OP_PASS), 256)
+            # one workspace for the whole pass and for per-segment steps
+            nbytes = max(workspace_size(cfg, HGA_OP_PASS), workspace_size(cfg, HGA_OP_STEP), 256)
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         else:
             self.dq = self.dk = self.dv = self.ws = None

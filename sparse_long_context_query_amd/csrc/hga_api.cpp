@@ -152,12 +152,10 @@ namespace {
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Workspace of hga_segment_pass.  bf16: the delta rows of every segment
-// (written by the forward launch), then the dK/dV partial sums of every
-// segment (dkdv launch -> dq launch).  f32: one step workspace per stream.
+// (written by the forward launch, read by the backward launches).  f32: one
+// step workspace per stream.
 size_t pass_workspace_bytes(const hga::Prob& p) {
-  const size_t nseg = (size_t)(p.S / p.L);
-  if (p.dtype == HGA_BF16)
-    return nseg * (hga::bwd_delta_bytes(p) + round256(hga::bwd_partial_bytes(p)));
+  if (p.dtype == HGA_BF16) return (size_t)(p.S / p.L) * hga::bwd_delta_bytes(p);
   return 2 * round256(hga::bwd_workspace_bytes(p));
 }
 
@@ -409,9 +407,7 @@ int hga_segment_pass(const hga_config* cfg, int32_t flags, const void* q, const 
     // all segments: no per-segment launch tails, and the second stream is
     // not needed
     const size_t dstride = hga::bwd_delta_bytes(p);
-    const size_t pstride = round256(hga::bwd_partial_bytes(p));
     float* delta = (float*)ws;
-    float* part = ws ? (float*)((char*)ws + (size_t)nseg * dstride) : nullptr;
     e = hga::launch_select_pass(p, q, summ, 0, nseg, sel, st[0]);
     if (e != hipSuccess) return hip_fail(e, "select launch");
     e = hga::launch_fwd_pass(p, q, k, v, sel, 0, nseg, o, lse, st[0], bwd ? dO : nullptr,
@@ -419,7 +415,7 @@ int hga_segment_pass(const hga_config* cfg, int32_t flags, const void* q, const 
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     if (bwd) {
       e = hga::launch_bwd_pass(p, q, k, v, lse, dO, sel, 0, nseg, dq, dk, dv, delta, dstride,
-                               part, pstride, st[0]);
+                               st[0]);
       if (e != hipSuccess) return hip_fail(e, "backward launch");
     }
     return ok();

@@ -29,10 +29,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct BwdArgs {
   int B, S, L, Bh, Bq, K, Hq, Hkv, G, nqb, nqb_all, seg;
   // whole-pass launches: segments seg .. seg+nseg-1; segment s's delta rows
-  // and dK/dV partial sums sit (s - seg) * dchunk / pchunk floats further on
+  // sit (s - seg) * dchunk floats further on
   int nseg;
   int dchunk;
-  long long pchunk;
   int wpu;      // dq: blocks of threads per (b, g, j) unit
   int nq32;     // 32-row query sub-blocks per query block
   float c2;     // scale * log2(e)
@@ -350,17 +349,14 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
 // itself (local tiles first, then history), two blocks per CU with no
 // common barrier, no halves to add at the end; same work order (contiguous
 // (b, g) ranges per XCD, last segments and query blocks first).  Per wave
-// and 32-key sub-tile the products are those of dq_bf16_kernel.  Before its
-// tiles every block also does its share of dkdv_finish for every segment of
-// the launch (the dkdv launch before it left the partial sums).
+// and 32-key sub-tile the products are those of dq_bf16_kernel.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void dq_pass_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, const float* __restrict__ lse,
     const __bf16* __restrict__ dO, const float* __restrict__ delta,
-    const int32_t* __restrict__ sel, __bf16* __restrict__ dq, const float* __restrict__ part_ws,
-    __bf16* __restrict__ dk, __bf16* __restrict__ dv, int nph, BwdArgs a) {
+    const int32_t* __restrict__ sel, __bf16* __restrict__ dq, BwdArgs a) {
   constexpr int TK = 64;
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
@@ -407,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void dq_pass_kernel(
 
   // the first local tile's copies and the query-side rows do not depend on
   // the selection: request them first, so that their latency overlaps the
-  // partial-sum finish and the compaction
+  // compaction
   const int nloc = (blk_qmax - t0) / TK + 1;
   const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
@@ -429,12 +425,6 @@ __global__ __launch_bounds__(256, 2) void dq_pass_kernel(
   const float lse2 = row_ok ? lse[qrow] * kLog2e : 0.f;
   const float dlt =
       row_ok ? delta[(size_t)sg * a.dchunk + (size_t)(b * a.Hq + h) * a.L + (tq - t0)] : 0.f;
-
-  for (int s2 = 0; s2 < a.nseg; ++s2) {
-    BwdArgs as = a;
-    as.seg = a.seg + s2;
-    dkdv_finish<D>(part_ws + (size_t)s2 * a.pchunk, dk, dv, as, nph);
-  }
 
   const int32_t* srow = sel + ((size_t)(b * a.Hkv + g) * a.nqb_all + (size_t)seg * a.nqb + j) * a.K;
   const int nsel = compact_selection(srow, a.K, nb, s_hlist, &s_hcount);
@@ -806,18 +796,10 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   const int nkt = (a.L + 31) / 32;
   const int nbk = nkt + (nkt & 1);  // blocks per (b, g)
   const int nph = (nkt + 1) / 2;    // mirror pairs (partial-sum slots)
-  int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int n = w % nbk;
-  w /= nbk;
-  // whole-pass launch: one grid over the segments (a.nseg == 1 otherwise)
-  const int sg = a.nseg - 1 - w % a.nseg;
-  w /= a.nseg;
-  const int g = w % a.Hkv;
-  const int b = w / a.Hkv;
-  BwdArgs as = a;
-  as.seg = a.seg + sg;
-  delta += (size_t)sg * a.dchunk;
-  part_ws += (size_t)sg * a.pchunk;
+  const int g = (w / nbk) % a.Hkv;
+  const int b = w / (nbk * a.Hkv);
   // block 2p: pairs [0, split) of tile p; block 2p+1: the rest of tile p,
   // then the mirror tile (scalars only, nothing indexed at run time)
   const int p = n >> 1, part = n & 1;
@@ -832,13 +814,221 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   const bool has2 = rest_first && wl > 0;
   float* pp = part_ws + ((size_t)((b * a.Hkv + g) * nph + p) * 2 + part) * 64 * D;
   if (e1 > b1)
-    dkdv_item<D>(q, k, v, lse, dO, delta, dk, dv, pp, as, s_raw, b, g, kt1, b1, e1,
+    dkdv_item<D>(q, k, v, lse, dO, delta, dk, dv, pp, a, s_raw, b, g, kt1, b1, e1,
                  kt1 == p && tile_split);
   if (has2)
-    dkdv_item<D>(q, k, v, lse, dO, delta, dk, dv, pp, as, s_raw, b, g, nkt - 1 - p, 0, wl, false);
+    dkdv_item<D>(q, k, v, lse, dO, delta, dk, dv, pp, a, s_raw, b, g, nkt - 1 - p, 0, wl, false);
 }
 
 
+
+// ---------------------------------------------------------------------------
+// a8, bf16 MFMA, whole segmented pass: dk/dv of the local keys of segments
+// a.seg .. a.seg+a.nseg-1 in one launch.  A block of 4 waves owns 128
+// consecutive keys of one (segment, b, g); wave w owns keys k0+32w .. +31,
+// holds their K rows in registers (B operand of S = Q.K^T), their V rows in
+// LDS (B operand of dP = dO.V^T) and their dK^T, dV^T accumulators.  The
+// block walks the (32-query tile, head) pairs that can see its keys --
+// query tiles from the block's first key on, every head of the group -- and
+// copies each pair's Q and dO tiles (with lse and delta) into LDS once for
+// its 4 waves, double-buffered so that the next pair's copies land while
+// the current one is computed.  Per wave and pair, with the products of
+// dkdv_item:
+//   S = Q.K^T, dP = dO.V^T,  P = exp2(S c2 - lse2), dS = P (dP - delta)
+//   dV^T += dO^T.P,  dK^T += Q^T.dS      (transposed reads of the Q, dO tiles)
+// Each key has one owner, so its dK, dV rows are written directly.  Key
+// block kb sees about nqt - 4kb query tiles; blocks run from the first key
+// block to the last (the most pairs first), segments innermost, so the
+// launch ends on short blocks.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void dkdv_pass_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, const float* __restrict__ lse,
+    const __bf16* __restrict__ dO, const float* __restrict__ delta,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, BwdArgs a) {
+  constexpr int TQ = 32;                 // queries per tile
+  constexpr int KB = 128;                // keys per block
+  constexpr int NKK = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int TILE_B = TQ * 2 * D;     // bytes of one 32-row tile
+  constexpr int STAGE_B = 2 * TILE_B + 512;  // Q tile, dO tile, lse (64), delta (64)
+  constexpr int CPR = (2 * D) / 16;
+  constexpr int RPI = 64 / CPR;          // rows per 1 KB copy instruction
+  __shared__ __attribute__((aligned(1024))) unsigned char s_v[KB * 2 * D];
+  __shared__ __attribute__((aligned(1024))) unsigned char s_stage[2][STAGE_B];
+
+  const int nkb = (a.L + KB - 1) / KB;
+  int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int sg = a.nseg - 1 - w % a.nseg;
+  w /= a.nseg;
+  const int kb = w % nkb;
+  w /= nkb;
+  const int g = w % a.Hkv;
+  const int b = w / a.Hkv;
+  const int seg = a.seg + sg;
+  const int t0 = seg * a.L, tend = t0 + a.L;
+  const int k0 = t0 + kb * KB;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
+  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
+  const float* dlt = delta + (size_t)sg * a.dchunk;
+
+  // keys of this wave; rows past the segment end read the last row (masked)
+  const int kfirst = k0 + 32 * wave;
+  const int nkey = max(0, min(32, tend - kfirst));
+  const int tk = kfirst + lq;
+  const bool key_ok = lq < nkey;
+  const int nkey_blk = min(KB, tend - k0);
+  // V rows of the block's keys into LDS (4 waves x 8 instructions)
+  {
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(v + kv_base + (size_t)k0 * D, (uint32_t)nkey_blk * (2 * D));
+#pragma unroll
+    for (int n = 0; n < KB / RPI / 4; ++n) {
+      const int i = wave + 4 * n;
+      const int row = i * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz<D>(row);
+      const int rr = row < nkey_blk ? row : nkey_blk - 1;
+      buffer_to_lds16(r, (uint32_t)rr * (2 * D) + c * 16, s_v + i * 1024);
+    }
+  }
+  // K rows of this wave's keys as B operands: lane (key lq, hi) holds
+  // K[key][16kk + 8hi .. +7]
+  bf16x8 kreg[NKK];
+  {
+    const int krow = key_ok ? tk : (nkey > 0 ? kfirst : tend - 1);
+    const __bf16* kp = k + kv_base + (size_t)krow * D + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) kreg[kk] = *reinterpret_cast<const bf16x8*>(kp + 16 * kk);
+  }
+
+  const int nqt = (a.L + TQ - 1) / TQ;
+  const int qt0 = (kb * KB) / TQ;        // first query tile that sees any key
+  const int npairs = (nqt - qt0) * a.G;
+  // copies of pair pi's tiles (every wave a quarter of Q and dO; waves 0 / 1
+  // the lse / delta of its 32 queries) into stage buffer `st`
+  auto stage_pair = [&](int pi, int st) __attribute__((always_inline)) {
+    const bool ok = pi < npairs;
+    const int pc = ok ? pi : 0;
+    const int qt = qt0 + pc / a.G, h = g * a.G + pc % a.G;
+    const int tq0 = t0 + qt * TQ;
+    const int nval = min(TQ, tend - tq0);
+    const size_t hrow = (size_t)(b * a.Hq + h) * a.S;
+    const uint32_t nb = ok ? (uint32_t)nval * (2 * D) : 0u;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + (hrow + tq0) * D, nb);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dO + (hrow + tq0) * D, nb);
+    unsigned char* sq = s_stage[st];
+    unsigned char* sd = sq + TILE_B;
+#pragma unroll
+    for (int n = 0; n < TQ / RPI / 4; ++n) {
+      const int i = wave + 4 * n;
+      const int row = i * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz<D>(row);
+      const int rr = row < nval ? row : nval - 1;
+      buffer_to_lds16(rq, (uint32_t)rr * (2 * D) + c * 16, sq + i * 1024);
+      buffer_to_lds16(rd, (uint32_t)rr * (2 * D) + c * 16, sd + i * 1024);
+    }
+    if (wave < 2) {
+      const float* base = wave == 0 ? lse + hrow + tq0
+                                    : dlt + (size_t)(b * a.Hq + h) * a.L + (tq0 - t0);
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(base, ok ? (uint32_t)nval * 4u : 0u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, to_lds(sq + 2 * TILE_B + wave * 256), 4,
+                                               (int)((lane & 31) * 4), 0, 0, 0);
+    }
+  };
+
+  floatx16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) { dkacc[db] = floatx16{}; dvacc[db] = floatx16{}; }
+  FragOffsets<D> fo;
+  fo.init(lane);
+  const unsigned char* vt = s_v + wave * 32 * (2 * D);
+
+  stage_pair(0, 0);
+  drain_vmem_loads();
+  __syncthreads();
+
+  for (int pi = 0; pi < npairs; ++pi) {
+    stage_pair(pi + 1, (pi + 1) & 1);
+    const int qt = qt0 + pi / a.G;
+    const int tq0 = t0 + qt * TQ;
+    const int nval = min(TQ, tend - tq0);
+    // a wave whose keys all come after the tile's queries has nothing to do
+    if (nkey > 0 && tq0 + TQ - 1 >= kfirst) {
+      const unsigned char* sq = s_stage[pi & 1];
+      const unsigned char* sd = sq + TILE_B;
+      const float* sl = reinterpret_cast<const float*>(sq + 2 * TILE_B);
+      floatx16 sacc = floatx16{}, pacc = floatx16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        sacc = mfma32(fo.row(sq, 0, kk), kreg[kk], sacc);
+        pacc = mfma32(fo.row(sd, 0, kk), fo.row(vt, 0, kk), pacc);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int u = 0; u < 2 * NKK - 2; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      // C layout: lane = key lq, item r = query row 8(r/4)+4hi+(r%4) of the tile
+      const bool need_mask = (tq0 < kfirst + 31) || (nval < TQ) || (nkey < 32);
+      float pv[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 l4 = *reinterpret_cast<const float4*>(&sl[8 * r4 + 4 * hi]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&sl[64 + 8 * r4 + 4 * hi]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv_[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          float p = fast_exp2(fmaf(sacc[r], a.c2, -lv[e] * kLog2e));
+          if (need_mask) {
+            const int row = 8 * r4 + 4 * hi + e;
+            p = (key_ok && row < nval && tk <= tq0 + row) ? p : 0.f;
+          }
+          pv[r] = p;
+          sacc[r] = p * (pacc[r] - dv_[e]);  // dS
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int r0 = 8 * ks;
+        const bf16x8 pb = to_bf16x8(pv[r0], pv[r0 + 1], pv[r0 + 2], pv[r0 + 3], pv[r0 + 4],
+                                    pv[r0 + 5], pv[r0 + 6], pv[r0 + 7]);
+        const bf16x8 sb = to_bf16x8(sacc[r0], sacc[r0 + 1], sacc[r0 + 2], sacc[r0 + 3],
+                                    sacc[r0 + 4], sacc[r0 + 5], sacc[r0 + 6], sacc[r0 + 7]);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dvacc[db] = mfma32(fo.tr(sd, 16 * ks, db), pb, dvacc[db]);
+          dkacc[db] = mfma32(fo.tr(sq, 16 * ks, db), sb, dkacc[db]);
+        }
+      }
+    }
+    drain_vmem_loads();  // the next pair's tiles have landed
+    __syncthreads();
+  }
+
+  if (!key_ok) return;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * db + 8 * r4 + 4 * hi;
+      const bf16x4 ko = {(__bf16)(dkacc[db][4 * r4] * a.scale),
+                         (__bf16)(dkacc[db][4 * r4 + 1] * a.scale),
+                         (__bf16)(dkacc[db][4 * r4 + 2] * a.scale),
+                         (__bf16)(dkacc[db][4 * r4 + 3] * a.scale)};
+      const bf16x4 vo = {(__bf16)dvacc[db][4 * r4], (__bf16)dvacc[db][4 * r4 + 1],
+                         (__bf16)dvacc[db][4 * r4 + 2], (__bf16)dvacc[db][4 * r4 + 3]};
+      *reinterpret_cast<bf16x4*>(dk + kv_base + (size_t)tk * D + d) = ko;
+      *reinterpret_cast<bf16x4*>(dv + kv_base + (size_t)tk * D + d) = vo;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Exact-gradient backward ([SeCO] 提案手法: the chunks are visited from the
@@ -1106,7 +1296,6 @@ BwdArgs make_args(const Prob& p, int seg) {
   a.hdk = a.hdv = nullptr;
   a.nseg = 1;
   a.dchunk = 0;
-  a.pchunk = 0;
   return a;
 }
 
@@ -1197,32 +1386,29 @@ hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
   return e;
 }
 
-// Backward of segments seg0 .. seg0+nseg-1 in two launches (dkdv, then dq
-// with the partial-sum finish); delta rows and partial sums per segment at
-// the given strides (bytes).
+// Backward of segments seg0 .. seg0+nseg-1 in two launches, dkdv then dq;
+// each segment's delta rows at the given stride (bytes).
 template <int D>
 hipError_t bwd_pass_bf16(const Prob& p, const void* q, const void* k, const void* v,
                          const float* lse, const void* dO, const int32_t* sel, int seg0,
                          int nseg, void* dq, void* dk, void* dv, const float* delta,
-                         size_t dstride, float* partials, size_t pstride, hipStream_t st) {
+                         size_t dstride, hipStream_t st) {
   BwdArgs a = make_args(p, seg0);
   a.nseg = nseg;
   a.dchunk = (int)(dstride / sizeof(float));
-  a.pchunk = (long long)(pstride / sizeof(float));
-  const int nkt = (p.L + 31) / 32;
-  const int nph = (nkt + 1) / 2;
   {
-    const int nblocks = p.B * p.Hkv * nseg * (nkt + (nkt & 1));
-    HGA_LAUNCH(HGA_K_BWD_DKDV, (dkdv_bf16_kernel<D>), dim3(nblocks), dim3(512), 0, st,
+    const int nkb = (p.L + 127) / 128;
+    const int nblocks = p.B * p.Hkv * nkb * nseg;
+    HGA_LAUNCH(HGA_K_BWD_DKDV, (dkdv_pass_kernel<D>), dim3(nblocks), dim3(256), 0, st,
                (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dO,
-               delta, (__bf16*)dk, (__bf16*)dv, partials, a);
+               delta, (__bf16*)dk, (__bf16*)dv, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int nblocks = p.B * p.Hkv * nseg * p.nqb * a.wpu;
   HGA_LAUNCH(HGA_K_BWD_DQ, (dq_pass_kernel<D>), dim3(nblocks), dim3(256), 0, st,
              (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dO, delta,
-             sel, (__bf16*)dq, partials, (__bf16*)dk, (__bf16*)dv, nph, a);
+             sel, (__bf16*)dq, a);
   return hipGetLastError();
 }
 
@@ -1263,12 +1449,12 @@ size_t bwd_delta_bytes(const Prob& p) { return delta_bytes(p); }
 hipError_t launch_bwd_pass(const Prob& p, const void* q, const void* k, const void* v,
                            const float* lse, const void* dO, const int32_t* sel, int seg0,
                            int nseg, void* dq, void* dk, void* dv, const float* delta,
-                           size_t dstride, float* partials, size_t pstride, hipStream_t st) {
+                           size_t dstride, hipStream_t st) {
   if (p.dtype != HGA_BF16) return hipErrorInvalidValue;
   return p.D == 64 ? bwd_pass_bf16<64>(p, q, k, v, lse, dO, sel, seg0, nseg, dq, dk, dv, delta,
-                                       dstride, partials, pstride, st)
+                                       dstride, st)
                    : bwd_pass_bf16<128>(p, q, k, v, lse, dO, sel, seg0, nseg, dq, dk, dv, delta,
-                                        dstride, partials, pstride, st);
+                                        dstride, st);
 }
 size_t bwd_partial_bytes(const Prob& p) { return partial_bytes(p); }
 

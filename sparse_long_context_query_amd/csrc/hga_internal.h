@@ -66,12 +66,11 @@ hipError_t launch_bwd(const Prob& p, const void* q, const void* k,
                       float* hist_dv = nullptr, float* partials = nullptr);
 // Backward of segments seg0 .. seg0+nseg-1 in one dkdv and one dq launch
 // (bf16 only; every segment's forward done, its delta rows [B, Hq, L] at
-// delta + (s - seg0) * dstride bytes; dK/dV partial sums of segment s at
-// partials + (s - seg0) * pstride bytes, pstride >= bwd_partial_bytes).
+// delta + (s - seg0) * dstride bytes).
 hipError_t launch_bwd_pass(const Prob& p, const void* q, const void* k, const void* v,
                            const float* lse, const void* dO, const int32_t* sel, int seg0,
                            int nseg, void* dq, void* dk, void* dv, const float* delta,
-                           size_t dstride, float* partials, size_t pstride, hipStream_t st);
+                           size_t dstride, hipStream_t st);
 size_t bwd_workspace_bytes(const Prob& p);
 // Workspace parts of the backward: delta rows of one segment, and the dK/dV
 // partial sums (launch_bwd's `partials`, else right after delta_ws).

@@ -195,9 +195,12 @@ def test_exact_step_validation(L):
 
 def test_segment_pass_validation(L):
     cfg = good_cfg()
-    one = L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_STEP)
     two = L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_PASS)
-    assert two >= one
+    # bf16: the fp32 delta rows of every segment
+    assert two == (cfg.seq_len // cfg.seg_len) * cfg.batch * cfg.n_q_heads * cfg.seg_len * 4
+    f32 = good_cfg(dtype=hga.HGA_F32)
+    step32 = L.hga_workspace_size(ctypes.byref(f32), hga.HGA_OP_STEP)
+    assert L.hga_workspace_size(ctypes.byref(f32), hga.HGA_OP_PASS) >= 2 * step32
 
     def call(flags=hga.HGA_STEP_BWD, ws_bytes=two, stream2=FAKE, dq=FAKE):
         return L.hga_segment_pass(ctypes.byref(cfg), flags, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
