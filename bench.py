@@ -66,9 +66,11 @@ def parse():
 
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_CLASS_OF = {"fwd_bf16_kernel": "fwd", "dq_bf16_kernel": "bwd_dq",
-                   "dkdv_bf16_kernel": "bwd_dkdv", "delta_kernel": "bwd_pre",
-                   "select_kernel": "select", "summarize_kernel": "summarize"}
+KERNEL_CLASS_OF = {"fwd_pass_kernel": "fwd", "dq_pass_kernel": "bwd_dq",
+                   "dkdv_pass_kernel": "bwd_dkdv", "fwd_bf16_kernel": "fwd",
+                   "dq_bf16_kernel": "bwd_dq", "dkdv_bf16_kernel": "bwd_dkdv",
+                   "delta_kernel": "bwd_pre", "select_kernel": "select",
+                   "summarize_kernel": "summarize"}
 
 
 def sources_sha256() -> str:
@@ -109,8 +111,7 @@ def pmc_summary(fetch_csv, write_csv, workload):
     f_scale, w_scale = copy_kib / cf[0], copy_kib / cw[0]
     classes = {}
     for name in fetch:
-        m = re.search(r"(fwd_bf16_kernel|dq_bf16_kernel|dkdv_bf16_kernel|delta_kernel|"
-                      r"select_kernel|summarize_kernel)", name)
+        m = re.search("(" + "|".join(KERNEL_CLASS_OF) + ")", name)
         if not m:
             continue
         c = classes.setdefault(KERNEL_CLASS_OF[m.group(1)], {"fetch": [], "write": []})
