@@ -171,10 +171,12 @@ def timed_passes(buf, dev, bwd, n, profile_classes=None, two_streams=True):
 
 
 def exact_bench(shape, dev, steps, warmup):
-    """The exact-gradient form of the pass (hga_segment_step_exact): all
-    block summaries, then every segment from the last to the first, each
-    giving its queries' dK/dV to the history blocks it selected.  Same
-    inputs as the headline pass."""
+    """The exact-gradient pass (hga_segment_pass_exact): summaries, selection
+    and forward of every segment, then every segment's queries (last
+    segment first) give their dK/dV to the history blocks they selected,
+    then local dK/dV plus those sums, and dQ.  Same inputs as the headline
+    pass.  `steps_ms_per_step` times the same gradient through
+    hga_segment_step_exact per segment."""
     import torch
     import sparse_long_context_query_amd as hga
     cfg = hga.Config.from_shape(shape)
@@ -183,36 +185,47 @@ def exact_bench(shape, dev, steps, warmup):
     summ, sel = z(s.summ, torch.float32), z(s.sel, torch.int32)
     o, lse, dq = z(s.q, s.dt), z(s.lse, torch.float32), z(s.q, s.dt)
     dk, dv = z(s.kv, s.dt), z(s.kv, s.dt)
-    hdk, hdv = z(s.kv, torch.float32), z(s.kv, torch.float32)
-    ws = torch.empty(hga.workspace_size(cfg, hga.HGA_OP_STEP_EXACT), dtype=torch.uint8,
+    ws = torch.empty(hga.workspace_size(cfg, hga.HGA_OP_PASS_EXACT), dtype=torch.uint8,
                      device="cuda")
+    hdk, hdv = z(s.kv, torch.float32), z(s.kv, torch.float32)
+    ws_step = torch.empty(hga.workspace_size(cfg, hga.HGA_OP_STEP_EXACT), dtype=torch.uint8,
+                          device="cuda")
 
     def one_pass():
+        hga.segment_pass_exact(cfg, dev["q"], dev["k"], dev["v"], dev["do"], summ, sel, o, lse,
+                               dq, dk, dv, ws)
+
+    def one_step_pass():
         hdk.zero_()
         hdv.zero_()
         hga.summarize(cfg, dev["k"], 0, shape.seq_len // shape.hist_block, summ)
         for seg in reversed(range(shape.nseg)):
             hga.segment_step_exact(cfg, seg, dev["q"], dev["k"], dev["v"], dev["do"], summ, sel,
-                                   o, lse, dq, dk, dv, hdk, hdv, ws)
+                                   o, lse, dq, dk, dv, hdk, hdv, ws_step)
 
-    for _ in range(warmup):
-        one_pass()
-    torch.cuda.synchronize()
-    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    st.record()
-    for _ in range(steps):
-        one_pass()
-    en.record()
-    torch.cuda.synchronize()
-    ms = st.elapsed_time(en) / steps
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        for _ in range(steps):
+            fn()
+        en.record()
+        torch.cuda.synchronize()
+        return st.elapsed_time(en) / steps
+
+    ms = timed(one_pass)
+    ms_steps = timed(one_step_pass)
     hga.profile_begin()
     one_pass()
     prof = hga.profile_end()
     return {"ms_per_step": round(ms, 4),
             "tokens_per_s": round(shape.batch * shape.seq_len / (ms * 1e-3), 1),
             "kernels_ms_per_pass": {c: round(v[0], 4) for c, v in prof.items() if v[1]},
+            "steps_ms_per_step": round(ms_steps, 4),
             "note": "history not detached: later segments' queries also give dK/dV to the "
-                    "blocks they selected; segments visited last to first"}
+                    "blocks they selected (hga_segment_pass_exact)"}
 
 
 def decode_bench(n_steps, news=(1, 16)):

@@ -239,10 +239,32 @@ int hga_segment_pass(const hga_config* cfg, int32_t flags, const void* q, const 
                      float* lse, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
                      void* stream, void* stream2);
 
+/* The whole exact-gradient pass ([SeCO] 提案手法: the backward visits the
+ * chunks from the last one and the gradient is exact; here the history
+ * keys are not detached): hga_summarize over every block a later segment
+ * can select, the selection and forward of every segment (one launch
+ * each), then the backward: each segment's queries, from the last segment
+ * to the first, add their dK/dV for the history blocks they selected into
+ * fp32 sums kept in ws; then one dK/dV launch writes every segment's local
+ * part plus its rows' sums, and one launch writes dQ.  The same results as
+ * hga_segment_step_exact called for seg = S/L-1 .. 0 after hga_summarize,
+ * within rounding (float sums in another order).  dq, dk, dv: the complete
+ * gradient of the layer's attention with respect to q, k, v.
+ * Requirements: bf16 (else HGA_ERR_UNSUPPORTED); L/Bq <= 64 and
+ * (L/Bq)*k <= 8192 (else HGA_ERR_UNSUPPORTED).  ws:
+ * hga_workspace_size(cfg, HGA_OP_PASS_EXACT) bytes (every segment's delta
+ * rows, the fp32 history sums of dK and dV, the history block list).
+ * Results are deterministic (every sum has one writer at a time; no
+ * atomics on floats). */
+int hga_segment_pass_exact(const hga_config* cfg, const void* q, const void* k, const void* v,
+                           const void* dO, float* summ, int32_t* sel, void* o, float* lse,
+                           void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                           void* stream);
+
 /* Workspace bytes for an operation (0 if none is needed), or 0 with
  * hga_last_error() set if the config is invalid. */
 enum { HGA_OP_FWD = 0, HGA_OP_BWD = 1, HGA_OP_STEP = 2, HGA_OP_DECODE = 3,
-       HGA_OP_STEP_EXACT = 4, HGA_OP_PASS = 5 };
+       HGA_OP_STEP_EXACT = 4, HGA_OP_PASS = 5, HGA_OP_PASS_EXACT = 6 };
 size_t hga_workspace_size(const hga_config* cfg, int32_t op);
 
 /* Message of the last failure on this thread ("" if none). */

@@ -27,7 +27,8 @@ HGA_ERR_HIP = -4
 HGA_F32 = 0
 HGA_BF16 = 1
 HGA_STEP_BWD = 1
-HGA_OP_FWD, HGA_OP_BWD, HGA_OP_STEP, HGA_OP_DECODE, HGA_OP_STEP_EXACT, HGA_OP_PASS = range(6)
+(HGA_OP_FWD, HGA_OP_BWD, HGA_OP_STEP, HGA_OP_DECODE, HGA_OP_STEP_EXACT, HGA_OP_PASS,
+ HGA_OP_PASS_EXACT) = range(7)
 HGA_STEP_SUMMARIES_READY = 2
 KERNEL_CLASSES = ("summarize", "select", "gather", "fwd", "bwd_pre", "bwd_dq", "bwd_dkdv",
                   "decode", "decode_merge", "bwd_hist")
@@ -84,6 +85,8 @@ _SIGNATURES = {
     "hga_segment_step_exact": (ctypes.c_int, [_CP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
                                               _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                               _P]),
+    "hga_segment_pass_exact": (ctypes.c_int, [_CP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                              _P, ctypes.c_size_t, _P]),
     "hga_decode_step": (ctypes.c_int, [_CP, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P,
                                        _P, _P, _P, ctypes.c_size_t, _P]),
     "hga_workspace_size": (ctypes.c_size_t, [_CP, ctypes.c_int32]),
@@ -254,6 +257,24 @@ def segment_step_exact(cfg: Config, seg: int, q, k, v, do, summ, sel, o, lse, dq
         _ptr(dq, "dq", s.dt, s.q), _ptr(dk, "dk", s.dt, s.kv), _ptr(dv, "dv", s.dt, s.kv),
         _ptr(hist_dk, "hist_dk", torch.float32, s.kv),
         _ptr(hist_dv, "hist_dv", torch.float32, s.kv),
+        _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream()))
+
+
+def segment_pass_exact(cfg: Config, q, k, v, do, summ, sel, o, lse, dq, dk, dv, ws=None) -> None:
+    """The whole exact-gradient pass (history not detached); see
+    hga_segment_pass_exact.  ws defaults to a fresh buffer of
+    workspace_size(cfg, HGA_OP_PASS_EXACT) bytes."""
+    s = Shapes(cfg)
+    torch = _torch()
+    if ws is None:
+        ws = torch.empty(max(workspace_size(cfg, HGA_OP_PASS_EXACT), 256), dtype=torch.uint8,
+                         device=q.device)
+    _check(lib().hga_segment_pass_exact(
+        ctypes.byref(cfg), _ptr(q, "q", s.dt, s.q), _ptr(k, "k", s.dt, s.kv),
+        _ptr(v, "v", s.dt, s.kv), _ptr(do, "do", s.dt, s.q),
+        _ptr(summ, "summ", torch.float32, s.summ), _ptr(sel, "sel", torch.int32, s.sel),
+        _ptr(o, "o", s.dt, s.q), _ptr(lse, "lse", torch.float32, s.lse),
+        _ptr(dq, "dq", s.dt, s.q), _ptr(dk, "dk", s.dt, s.kv), _ptr(dv, "dv", s.dt, s.kv),
         _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream()))
 
 

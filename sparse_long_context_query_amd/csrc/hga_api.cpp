@@ -154,9 +154,18 @@ size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 // Workspace of hga_segment_pass.  bf16: the delta rows of every segment
 // (written by the forward launch, read by the backward launches).  f32: one
 // step workspace per stream.
+size_t pass_exact_workspace_bytes(const hga::Prob& p);
+
 size_t pass_workspace_bytes(const hga::Prob& p) {
   if (p.dtype == HGA_BF16) return (size_t)(p.S / p.L) * hga::bwd_delta_bytes(p);
   return 2 * round256(hga::bwd_workspace_bytes(p));
+}
+
+// Workspace of hga_segment_pass_exact: every segment's delta rows, the fp32
+// history sums of dK and dV ([B, Hkv, S, D] each), the history block list.
+size_t pass_exact_workspace_bytes(const hga::Prob& p) {
+  const size_t sums = round256((size_t)p.B * p.Hkv * p.S * p.D * sizeof(float));
+  return (size_t)(p.S / p.L) * hga::bwd_delta_bytes(p) + 2 * sums + hga::hist_ws_bytes(p);
 }
 
 }  // namespace
@@ -187,6 +196,9 @@ size_t hga_workspace_size(const hga_config* cfg, int32_t op) {
     case HGA_OP_PASS:
       ok();
       return pass_workspace_bytes(p);
+    case HGA_OP_PASS_EXACT:
+      ok();
+      return pass_exact_workspace_bytes(p);
     default:
       fail(HGA_ERR_ARG, "unknown op %d", op);
       return 0;
@@ -483,6 +495,69 @@ int hga_segment_step_exact(const hga_config* cfg, int32_t seg, const void* q, co
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   e = hga::launch_bwd(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, (float*)ws, st, fuse,
                       hist_dk, hist_dv);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return ok();
+}
+
+int hga_segment_pass_exact(const hga_config* cfg, const void* q, const void* k, const void* v,
+                           const void* dO, float* summ, int32_t* sel, void* o, float* lse,
+                           void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                           void* stream) {
+  hga::Prob p;
+  int rc = make_prob(cfg, &p);
+  if (rc) return rc;
+  if (p.dtype != HGA_BF16)
+    return fail(HGA_ERR_UNSUPPORTED, "the exact-gradient pass needs bf16");
+  if (p.nqb > 64 || p.nqb * p.K > hga::kHistMaxEntries)
+    return fail(HGA_ERR_UNSUPPORTED,
+                "the exact-gradient pass needs seg_len/query_block <= 64 and "
+                "(seg_len/query_block)*top_k <= %d", hga::kHistMaxEntries);
+  HGA_REQUIRE(q);
+  HGA_REQUIRE(k);
+  HGA_REQUIRE(v);
+  HGA_REQUIRE(dO);
+  HGA_REQUIRE(summ);
+  HGA_REQUIRE(sel);
+  HGA_REQUIRE(o);
+  HGA_REQUIRE(lse);
+  HGA_REQUIRE(dq);
+  HGA_REQUIRE(dk);
+  HGA_REQUIRE(dv);
+  HGA_REQUIRE(ws);
+  const size_t need = pass_exact_workspace_bytes(p);
+  if (ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  const int nseg = p.S / p.L;
+  const size_t dstride = hga::bwd_delta_bytes(p);
+  const size_t nsum = (size_t)p.B * p.Hkv * p.S * p.D;
+  float* delta = (float*)ws;
+  float* hist_dk = (float*)((char*)ws + (size_t)nseg * dstride);
+  float* hist_dv = (float*)((char*)hist_dk + round256(nsum * sizeof(float)));
+  void* list_ws = (char*)hist_dv + round256(nsum * sizeof(float));
+  hipError_t e;
+  if (nseg > 1) {
+    e = hga::launch_summarize(p, k, 0, (p.S - p.L) / p.Bh, summ, st);
+    if (e != hipSuccess) return hip_fail(e, "summarize launch");
+  }
+  e = hga::launch_select_pass(p, q, summ, 0, nseg, sel, st);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  e = hga::launch_fwd_pass(p, q, k, v, sel, 0, nseg, o, lse, st, dO, delta, dstride);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  // history sums: each segment's queries add their part to the rows of the
+  // blocks they selected, from the last segment to the first (a fixed order)
+  if ((e = hga::launch_zero(hist_dk, nsum, st)) != hipSuccess) return hip_fail(e, "zero launch");
+  if ((e = hga::launch_zero(hist_dv, nsum, st)) != hipSuccess) return hip_fail(e, "zero launch");
+  for (int seg = nseg - 1; seg >= 1; --seg) {
+    e = hga::launch_hist_exact(p, q, k, v, lse, dO, sel, seg,
+                               (const float*)((const char*)delta + (size_t)seg * dstride),
+                               hist_dk, hist_dv, list_ws, st);
+    if (e != hipSuccess) return hip_fail(e, "history backward launch");
+  }
+  // local dK/dV of every segment plus its rows' history sums, and dQ
+  e = hga::launch_bwd_pass(p, q, k, v, lse, dO, sel, 0, nseg, dq, dk, dv, delta, dstride, st,
+                           hist_dk, hist_dv);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();
 }

@@ -18,6 +18,8 @@
 // floating-point atomics, so results are bitwise reproducible.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "hga_internal.h"
 #include "hga_tiles.h"
 
@@ -836,8 +838,9 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
 // dkdv_item:
 //   S = Q.K^T, dP = dO.V^T,  P = exp2(S c2 - lse2), dS = P (dP - delta)
 //   dV^T += dO^T.P,  dK^T += Q^T.dS      (transposed reads of the Q, dO tiles)
-// Each key has one owner, so its dK, dV rows are written directly.  Key
-// block kb sees about nqt - 4kb query tiles; blocks run from the first key
+// Each key has one owner, so its dK, dV rows are written directly (plus,
+// for the exact gradient, the fp32 sums a.hdk / a.hdv that later segments'
+// queries left in those rows).  Key block kb sees about nqt - 4kb query tiles; blocks run from the first key
 // block to the last (the most pairs first), segments innermost, so the
 // launch ends on short blocks.
 // ---------------------------------------------------------------------------
@@ -1019,14 +1022,21 @@ __global__ __launch_bounds__(256, 2) void dkdv_pass_kernel(
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int d = 32 * db + 8 * r4 + 4 * hi;
-      const bf16x4 ko = {(__bf16)(dkacc[db][4 * r4] * a.scale),
-                         (__bf16)(dkacc[db][4 * r4 + 1] * a.scale),
-                         (__bf16)(dkacc[db][4 * r4 + 2] * a.scale),
-                         (__bf16)(dkacc[db][4 * r4 + 3] * a.scale)};
-      const bf16x4 vo = {(__bf16)dvacc[db][4 * r4], (__bf16)dvacc[db][4 * r4 + 1],
-                         (__bf16)dvacc[db][4 * r4 + 2], (__bf16)dvacc[db][4 * r4 + 3]};
-      *reinterpret_cast<bf16x4*>(dk + kv_base + (size_t)tk * D + d) = ko;
-      *reinterpret_cast<bf16x4*>(dv + kv_base + (size_t)tk * D + d) = vo;
+      const size_t off = kv_base + (size_t)tk * D + d;
+      float4 hk = make_float4(0.f, 0.f, 0.f, 0.f), hv = hk;
+      if (a.hdk != nullptr) {
+        hk = *reinterpret_cast<const float4*>(a.hdk + off);
+        hv = *reinterpret_cast<const float4*>(a.hdv + off);
+      }
+      const bf16x4 ko = {(__bf16)(dkacc[db][4 * r4] * a.scale + hk.x),
+                         (__bf16)(dkacc[db][4 * r4 + 1] * a.scale + hk.y),
+                         (__bf16)(dkacc[db][4 * r4 + 2] * a.scale + hk.z),
+                         (__bf16)(dkacc[db][4 * r4 + 3] * a.scale + hk.w)};
+      const bf16x4 vo = {(__bf16)(dvacc[db][4 * r4] + hv.x), (__bf16)(dvacc[db][4 * r4 + 1] + hv.y),
+                         (__bf16)(dvacc[db][4 * r4 + 2] + hv.z),
+                         (__bf16)(dvacc[db][4 * r4 + 3] + hv.w)};
+      *reinterpret_cast<bf16x4*>(dk + off) = ko;
+      *reinterpret_cast<bf16x4*>(dv + off) = vo;
     }
 }
 
@@ -1134,6 +1144,13 @@ __global__ __launch_bounds__(512) void dkdv_hist_kernel(
                        bg / a.Hkv, bg % a.Hkv, kt, 0, pairs, false, s_j,
                        ent.blk * a.Bh + 32 * kt, min(32, a.Bh - 32 * kt));
   }
+}
+
+// Clears n floats (n a multiple of 4, 16-byte aligned): a plain store kernel,
+// so that it may sit in a captured graph.
+__global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, size_t n4) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -1392,10 +1409,12 @@ template <int D>
 hipError_t bwd_pass_bf16(const Prob& p, const void* q, const void* k, const void* v,
                          const float* lse, const void* dO, const int32_t* sel, int seg0,
                          int nseg, void* dq, void* dk, void* dv, const float* delta,
-                         size_t dstride, hipStream_t st) {
+                         size_t dstride, hipStream_t st, const float* hdk, const float* hdv) {
   BwdArgs a = make_args(p, seg0);
   a.nseg = nseg;
   a.dchunk = (int)(dstride / sizeof(float));
+  a.hdk = const_cast<float*>(hdk);
+  a.hdv = const_cast<float*>(hdv);
   {
     const int nkb = (p.L + 127) / 128;
     const int nblocks = p.B * p.Hkv * nkb * nseg;
@@ -1449,12 +1468,53 @@ size_t bwd_delta_bytes(const Prob& p) { return delta_bytes(p); }
 hipError_t launch_bwd_pass(const Prob& p, const void* q, const void* k, const void* v,
                            const float* lse, const void* dO, const int32_t* sel, int seg0,
                            int nseg, void* dq, void* dk, void* dv, const float* delta,
-                           size_t dstride, hipStream_t st) {
+                           size_t dstride, hipStream_t st, const float* hist_dk,
+                           const float* hist_dv) {
   if (p.dtype != HGA_BF16) return hipErrorInvalidValue;
   return p.D == 64 ? bwd_pass_bf16<64>(p, q, k, v, lse, dO, sel, seg0, nseg, dq, dk, dv, delta,
-                                       dstride, st)
+                                       dstride, st, hist_dk, hist_dv)
                    : bwd_pass_bf16<128>(p, q, k, v, lse, dO, sel, seg0, nseg, dq, dk, dv, delta,
-                                        dstride, st);
+                                        dstride, st, hist_dk, hist_dv);
+}
+
+hipError_t launch_zero(float* p, size_t n, hipStream_t st) {
+  const size_t n4 = n / 4;
+  const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 4096);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, st, (float4*)p, n4);
+  return hipGetLastError();
+}
+
+size_t hist_ws_bytes(const Prob& p) { return hist_list_bytes(p); }
+
+hipError_t launch_hist_exact(const Prob& p, const void* q, const void* k, const void* v,
+                             const float* lse, const void* dO, const int32_t* sel, int seg,
+                             const float* delta_seg, float* hist_dk, float* hist_dv, void* list_ws,
+                             hipStream_t st) {
+  if (p.dtype != HGA_BF16) return hipErrorInvalidValue;
+  const int maxd = hist_max_entries(p);
+  if (seg <= 0 || maxd <= 0) return hipSuccess;
+  BwdArgs a = make_args(p, seg);
+  a.hdk = hist_dk;
+  a.hdv = hist_dv;
+  char* base = reinterpret_cast<char*>(list_ws);
+  int* counts = reinterpret_cast<int*>(base);
+  HistEntry* list =
+      reinterpret_cast<HistEntry*>(base + round256((size_t)p.B * p.Hkv * sizeof(int)));
+  HGA_LAUNCH(HGA_K_BWD_HIST, hist_blocks_kernel, dim3(p.B * p.Hkv), dim3(256), 0, st, sel, list,
+             counts, a, maxd);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int ntpb = (p.Bh + 31) / 32;
+  if (p.D == 64)
+    HGA_LAUNCH(HGA_K_BWD_HIST, (dkdv_hist_kernel<64>), dim3(256), dim3(512), 0, st,
+               (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dO,
+               delta_seg, (const HistEntry*)list, (const int*)counts, a, maxd, ntpb);
+  else
+    HGA_LAUNCH(HGA_K_BWD_HIST, (dkdv_hist_kernel<128>), dim3(256), dim3(512), 0, st,
+               (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dO,
+               delta_seg, (const HistEntry*)list, (const int*)counts, a, maxd, ntpb);
+  return hipGetLastError();
 }
 size_t bwd_partial_bytes(const Prob& p) { return partial_bytes(p); }
 

@@ -67,10 +67,23 @@ hipError_t launch_bwd(const Prob& p, const void* q, const void* k,
 // Backward of segments seg0 .. seg0+nseg-1 in one dkdv and one dq launch
 // (bf16 only; every segment's forward done, its delta rows [B, Hq, L] at
 // delta + (s - seg0) * dstride bytes).
+// With hist_dk / hist_dv (exact gradient): the fp32 sums later segments'
+// queries left in the keys' rows are added to dk / dv.
 hipError_t launch_bwd_pass(const Prob& p, const void* q, const void* k, const void* v,
                            const float* lse, const void* dO, const int32_t* sel, int seg0,
                            int nseg, void* dq, void* dk, void* dv, const float* delta,
-                           size_t dstride, hipStream_t st);
+                           size_t dstride, hipStream_t st, const float* hist_dk = nullptr,
+                           const float* hist_dv = nullptr);
+// Exact gradient, segment seg: its queries' dK/dV for the history blocks
+// they selected, added into the fp32 sums hist_dk / hist_dv (segment seg's
+// delta rows at delta_seg; list_ws: hist_ws_bytes of scratch).
+hipError_t launch_hist_exact(const Prob& p, const void* q, const void* k, const void* v,
+                             const float* lse, const void* dO, const int32_t* sel, int seg,
+                             const float* delta_seg, float* hist_dk, float* hist_dv, void* list_ws,
+                             hipStream_t st);
+size_t hist_ws_bytes(const Prob& p);
+// Stores zeros into n floats (n % 4 == 0, 16-byte aligned).
+hipError_t launch_zero(float* p, size_t n, hipStream_t st);
 size_t bwd_workspace_bytes(const Prob& p);
 // Workspace parts of the backward: delta rows of one segment, and the dK/dV
 // partial sums (launch_bwd's `partials`, else right after delta_ws).

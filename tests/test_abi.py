@@ -193,6 +193,25 @@ def test_exact_step_validation(L):
     assert call(wide) == hga.HGA_ERR_UNSUPPORTED and "64" in hga.last_error()
 
 
+def test_exact_pass_validation(L):
+    cfg = good_cfg()
+    need = L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_PASS_EXACT)
+    # every segment's delta rows, the fp32 history sums of dK and dV, the list
+    sums = 2 * cfg.batch * cfg.n_kv_heads * cfg.seq_len * cfg.head_dim * 4
+    assert need >= (cfg.seq_len // cfg.seg_len) * cfg.batch * cfg.n_q_heads * cfg.seg_len * 4 + sums
+
+    def call(c, ws_bytes=need, dk=FAKE):
+        return L.hga_segment_pass_exact(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, dk, FAKE, FAKE, ws_bytes, None)
+
+    assert call(cfg, dk=None) == hga.HGA_ERR_ARG and "dk is NULL" in hga.last_error()
+    assert call(cfg, ws_bytes=need - 1) == hga.HGA_ERR_WORKSPACE
+    f32 = good_cfg(dtype=hga.HGA_F32)
+    assert call(f32) == hga.HGA_ERR_UNSUPPORTED and "bf16" in hga.last_error()
+    wide = good_cfg(seg_len=2048, query_block=16)  # 128 query blocks per segment (> 64)
+    assert call(wide) == hga.HGA_ERR_UNSUPPORTED and "64" in hga.last_error()
+
+
 def test_segment_pass_validation(L):
     cfg = good_cfg()
     two = L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_PASS)

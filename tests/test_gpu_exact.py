@@ -52,7 +52,21 @@ def run_exact(shape, dev):
     return {k: to_np(v) for k, v in out.items()}
 
 
-@pytest.mark.parametrize("shape", [
+def run_exact_pass(shape, dev):
+    """hga_segment_pass_exact; returns the output tensors on the host."""
+    cfg = hga.Config.from_shape(shape)
+    s = hga.Shapes(cfg)
+    z = lambda shp_, dt: torch.zeros(shp_, dtype=dt, device="cuda")  # noqa: E731
+    out = {"summ": z(s.summ, torch.float32), "sel": z(s.sel, torch.int32), "o": z(s.q, s.dt),
+           "lse": z(s.lse, torch.float32), "dq": z(s.q, s.dt), "dk": z(s.kv, s.dt),
+           "dv": z(s.kv, s.dt)}
+    hga.segment_pass_exact(cfg, dev["q"], dev["k"], dev["v"], dev["do"], out["summ"],
+                           out["sel"], out["o"], out["lse"], out["dq"], out["dk"], out["dv"])
+    torch.cuda.synchronize()
+    return {k: to_np(v) for k, v in out.items()}
+
+
+EXACT_SHAPES = [
     shp(),                                                      # G = 4, D = 128
     shp(top_k=40),                                              # k covers all history
     shp(hist_block=16, query_block=16, top_k=5),                # 16-row blocks (half tiles)
@@ -60,7 +74,10 @@ def run_exact(shape, dev):
     shp(head_dim=64, seq_len=384, seg_len=96, hist_block=48, query_block=48, top_k=2),
     shp(batch=2, seq_len=256, n_q_heads=2, n_kv_heads=2, top_k=2),  # G = 1, batch 2
     shp(seq_len=128, seg_len=128),                              # one segment: no history
-])
+]
+
+
+@pytest.mark.parametrize("shape", EXACT_SHAPES)
 def test_exact_backward_parity(shape):
     inp = make_inputs(shape, seed=23)
     got = run_exact(shape, upload(inp, shape))
@@ -110,3 +127,29 @@ def test_exact_backward_full_size_16k():
     assert_close("dq", got["dq"][0, hs], dQ[0, hs], tol)
     assert_close("dk", got["dk"][0, g], dK[0, g], tol)
     assert_close("dv", got["dv"][0, g], dV[0, g], tol)
+
+
+@pytest.mark.parametrize("shape", EXACT_SHAPES + [
+    shp(seq_len=1024, seg_len=256, hist_block=64, query_block=64, top_k=3),  # 2 key blocks
+    shp(seq_len=480, seg_len=160, hist_block=32, query_block=32, top_k=4),   # ragged key block
+])
+def test_exact_pass_parity(shape):
+    """hga_segment_pass_exact against the oracle's backward_exact, and
+    against the exact steps (selection bit for bit; outputs within the
+    dtype's tolerance: the pass adds float sums in another order)."""
+    inp = make_inputs(shape, seed=29)
+    dev = upload(inp, shape)
+    got = run_exact_pass(shape, dev)
+    ref = orc.run(inp, shape, bwd=False)
+    np.testing.assert_array_equal(got["sel"], ref["sel"])
+    dQ, dK, dV = orc.backward_exact(inp["q"], inp["k"], inp["v"], inp["do"], ref["sel"], shape,
+                                    ref["o"], ref["lse"])
+    tol = TOL[shape.dtype]
+    errs = {}
+    for key, want in (("o", ref["o"]), ("lse", ref["lse"]), ("dq", dQ), ("dk", dK), ("dv", dV)):
+        errs[key] = assert_close(key, got[key], want, tol)
+    steps = run_exact(shape, dev)
+    np.testing.assert_array_equal(got["sel"], steps["sel"])
+    for key in ("o", "lse", "dq", "dk", "dv"):
+        assert_close(key, got[key], steps[key].astype(np.float64), tol)
+    print({k: f"{v:.2e}" for k, v in errs.items()})
