@@ -410,10 +410,13 @@ __global__ __launch_bounds__(256, 2) void dq_pass_kernel(
   const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.S * (2 * D));
+  uint32_t loff[TK / (64 / ((2 * D) / 16)) / 4];
+  contiguous_tile_offsets<D, TK>(wr, lane, loff);
   {
     KeySource<TK> loc;
     loc.init(s_hlist, 0, a.Bh, t0, t0 + a.L);
-    dma_kv_tile<D, TK>(loc, 0, kr, vr, s_tiles[0], s_tiles[0] + TILE_B, wr, lane);
+    dma_kv_tile_fast<D, TK>(loc, 0, k + kv_base, v + kv_base, a.S, kr, vr, loff, s_tiles[0],
+                            s_tiles[0] + TILE_B, wr, lane);
   }
   const int tq = qfirst + lq;
   const bool row_ok = lq < nvalid;
@@ -446,8 +449,9 @@ __global__ __launch_bounds__(256, 2) void dq_pass_kernel(
   for (int i = 0; i < ntiles; ++i) {
     const int it = walk_tile(i, nloc, nht);
     if (i + 1 < ntiles)
-      dma_kv_tile<D, TK>(src, walk_tile(i + 1, nloc, nht), kr, vr, s_tiles[(i + 1) & 1],
-                         s_tiles[(i + 1) & 1] + TILE_B, wr, lane);
+      dma_kv_tile_fast<D, TK>(src, walk_tile(i + 1, nloc, nht), k + kv_base, v + kv_base, a.S,
+                              kr, vr, loff, s_tiles[(i + 1) & 1], s_tiles[(i + 1) & 1] + TILE_B,
+                              wr, lane);
     const bool is_local = it >= nht;
     const int local_first = t0 + (it - nht) * TK;
     const bool work = active && (!is_local || local_first <= wave_qmax);

@@ -282,6 +282,33 @@ __device__ __forceinline__ void contiguous_tile_offsets(int wr, int lane,
 template <int D, int TK>
 __device__ __forceinline__ void kv_tile_issue(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                               const uint32_t (&off)[TK / (64 / ((2 * D) / 16)) / 4],
+                                              unsigned char* kdst, unsigned char* vdst, int wr);
+
+// dma_kv_tile with the scalar fast path: when every tile is a run of
+// consecutive rows (tpb > 0) the lanes keep the fixed offsets `loff`
+// (contiguous_tile_offsets) and the resource is placed at the tile's first
+// row, over the rows up to the sequence end (rows past the segment end are
+// read as they are; the kernels mask them).  k_rows / v_rows: row 0 of the
+// (sequence, KV head), S rows.
+template <int D, int TK>
+__device__ __forceinline__ void dma_kv_tile_fast(
+    const KeySource<TK>& src, int it, const __bf16* k_rows, const __bf16* v_rows, int S,
+    __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+    const uint32_t (&loff)[TK / (64 / ((2 * D) / 16)) / 4], unsigned char* kdst,
+    unsigned char* vdst, int wr, int lane) {
+  if (src.tpb > 0) {
+    const int base = src.tile_base(it);
+    const uint32_t nbytes = (uint32_t)(S - base) * (2 * D);
+    kv_tile_issue<D, TK>(make_rsrc(k_rows + (size_t)base * D, nbytes),
+                         make_rsrc(v_rows + (size_t)base * D, nbytes), loff, kdst, vdst, wr);
+  } else {
+    dma_kv_tile<D, TK>(src, it, kr, vr, kdst, vdst, wr, lane);
+  }
+}
+
+template <int D, int TK>
+__device__ __forceinline__ void kv_tile_issue(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                              const uint32_t (&off)[TK / (64 / ((2 * D) / 16)) / 4],
                                               unsigned char* kdst, unsigned char* vdst, int wr) {
   constexpr int NI = TK / (64 / ((2 * D) / 16));
 #pragma unroll
