@@ -19,12 +19,15 @@
 // takes the query rows r = w, w+4, ... of the R = G*n rows of the group and
 // writes the chunk's max, sum of exponentials and unnormalised P.V (fp32)
 // to the workspace.  A merge kernel then combines the chunks of every row in
-// chunk order (deterministic) into o and lse.  With a handful of query rows
-// against thousands of keys the step is bound by HBM, not by arithmetic, so
-// it runs on the vector ALU; MFMA tiles would sit mostly empty.
+// chunk order (deterministic) into o and lse.  bf16 runs the chunk products
+// on the matrix cores (decode_mfma_kernel: S^T = K.Q^T and O^T = V^T.P^T per
+// 32-row tile of the G*n rows), f32 on the vector ALU (decode_attn_kernel).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "hga_internal.h"
+#include "hga_tiles.h"
 
 namespace hga {
 namespace {
@@ -203,6 +206,138 @@ __global__ __launch_bounds__(64 * kWaves) void decode_attn_kernel(
   }
 }
 
+// bf16, MFMA form of decode_attn_kernel (same chunks, same partial sums).
+// The chunk's K and V rows are copied straight into swizzled row-major LDS
+// tiles; wave w takes query rows 32w .. 32w+31 of the R = G*n rows (row r =
+// head r / n, token r % n) and, with Q^T in registers as the B operand:
+//   S^T = K.Q^T (two 32-key halves),  per row: chunk max m, P = exp2(S c2 - m)
+//   on the visible keys, l = sum P,  O^T = V^T.P^T (V^T read transposed)
+// then writes m, l and the unnormalised O rows like decode_attn_kernel.
+template <int D>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const int32_t* __restrict__ sel, float* __restrict__ part_o, float* __restrict__ part_ml,
+    DecArgs a) {
+  constexpr int NKK = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int TILE_B = kCK * 2 * D;
+  constexpr int CPR = (2 * D) / 16;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;         // rows per 1 KB copy instruction
+  __shared__ __attribute__((aligned(1024))) unsigned char s_k[TILE_B];
+  __shared__ __attribute__((aligned(1024))) unsigned char s_v[TILE_B];
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int R = a.G * a.n;
+
+  // token of key `key` of this chunk; rows that hold no key read a valid row
+  auto token_of = [&](int key, bool& valid, bool& local) {
+    if (c < a.nch_h) {
+      const int hp = c * kCK + key;
+      valid = hp < a.nht;
+      local = false;
+      return valid ? sel[(size_t)(b * a.Hkv + g) * a.K + hp / a.Bh] * a.Bh + hp % a.Bh : 0;
+    }
+    const int t = a.t0 + (c - a.nch_h) * kCK + key;
+    valid = t < a.pos + a.n;
+    local = true;
+    return valid ? t : a.t0;
+  };
+  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
+  {
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.S * (2 * D));
+#pragma unroll
+    for (int n = 0; n < kCK / RPI / 4; ++n) {
+      const int i = wave + 4 * n;
+      const int row = i * RPI + lane / CPR;
+      bool vld, loc;
+      const int tok = token_of(row, vld, loc);
+      const uint32_t off = (uint32_t)tok * (2 * D) + (((lane % CPR) ^ swz<D>(row)) << 4);
+      buffer_to_lds16(kr, off, s_k + i * 1024);
+      buffer_to_lds16(vr, off, s_v + i * 1024);
+    }
+  }
+  // this wave's query rows as B operands: lane (row lq, hi) holds
+  // Q[row][16kk + 8hi .. +7]
+  const int r = 32 * wave + lq;
+  const bool row_ok = r < R;
+  const int hh = row_ok ? r / a.n : 0, ti = row_ok ? r % a.n : 0;
+  bf16x8 qreg[NKK];
+  {
+    const __bf16* qp = q + ((size_t)(b * a.Hq + g * a.G + hh) * a.n + ti) * D + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qreg[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * kk) : bf16x8{};
+  }
+  drain_vmem_loads();
+  __syncthreads();
+  if (32 * wave >= R) return;
+
+  FragOffsets<D> fo;
+  fo.init(lane);
+  floatx16 sacc[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) sacc[st] = floatx16{};
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+    for (int st = 0; st < 2; ++st) sacc[st] = mfma32(fo.row(s_k, st, kk), qreg[kk], sacc[st]);
+  // C layout: lane = query row lq, item rr of half st = key 32st + 8(rr/4) + 4hi + rr%4
+  float mt = -INFINITY;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int key = 32 * st + 8 * (rr >> 2) + 4 * hi + (rr & 3);
+      // history keys: every selected token; local keys: up to this row's token
+      const int tl = a.t0 + (c - a.nch_h) * kCK + key;
+      const bool vis = c < a.nch_h ? c * kCK + key < a.nht : tl <= a.pos + ti;
+      sacc[st][rr] = vis ? sacc[st][rr] * a.c2 : -INFINITY;
+      mt = fmaxf(mt, sacc[st][rr]);
+    }
+  mt = pair_max(mt);
+  float lsum = 0.f;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const float p = mt == -INFINITY ? 0.f : exp2f(sacc[st][rr] - mt);
+      sacc[st][rr] = p;
+      lsum += p;
+    }
+  lsum = pair_sum(lsum);
+  floatx16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int r0 = 8 * ks;
+      const bf16x8 pb = to_bf16x8(sacc[st][r0], sacc[st][r0 + 1], sacc[st][r0 + 2],
+                                  sacc[st][r0 + 3], sacc[st][r0 + 4], sacc[st][r0 + 5],
+                                  sacc[st][r0 + 6], sacc[st][r0 + 7]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = mfma32(fo.tr(s_v, 32 * st + 16 * ks, db), pb, oacc[db]);
+    }
+  if (!row_ok) return;
+  float* ml = part_ml + ((size_t)(b * a.Hkv + g) * a.nc + c) * kMaxRows * 2;
+  if (hi == 0) {
+    ml[2 * r] = mt;
+    ml[2 * r + 1] = lsum;
+  }
+  float* po = part_o + (((size_t)(b * a.Hkv + g) * a.nc + c) * kMaxRows + r) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      *reinterpret_cast<float4*>(po + 32 * db + 8 * r4 + 4 * hi) =
+          make_float4(oacc[db][4 * r4], oacc[db][4 * r4 + 1], oacc[db][4 * r4 + 2],
+                      oacc[db][4 * r4 + 3]);
+}
+
 // One wave per (query row, KV head, sequence): combines the chunks in
 // order.  With M = max_c m_c: l = sum_c l_c 2^(m_c - M),
 // o = sum_c O_c 2^(m_c - M) / l, lse = (M + log2 l) ln 2.
@@ -301,6 +436,16 @@ hipError_t decode_t(const Prob& p, int pos, int n, const void* q_new, const void
   const DecPlan d = plan(p, pos, n);
   float* part_o = ws;
   float* part_ml = ws + (size_t)p.B * p.Hkv * max_chunks(p) * kMaxRows * p.D;
+  if constexpr (std::is_same<T, __bf16>::value) {
+    HGA_LAUNCH(HGA_K_DECODE, (decode_mfma_kernel<D>), dim3(d.a.nc, p.Hkv, p.B), dim3(256), 0, st,
+               (const __bf16*)q_new, (const __bf16*)k, (const __bf16*)v, sel, part_o, part_ml,
+               d.a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    HGA_LAUNCH(HGA_K_DECODE_MERGE, (decode_merge_kernel<T, D>), dim3(d.R, p.Hkv, p.B), dim3(64),
+               0, st, (const float*)part_o, (const float*)part_ml, (T*)o, lse, d.a);
+    return hipGetLastError();
+  }
   const size_t shm = DecLds<T, D>::bytes(d.R);
   if (shm > 32768) {
     hipError_t e = hipFuncSetAttribute((const void*)decode_attn_kernel<T, D>,
