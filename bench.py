@@ -37,7 +37,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="train_16k")
     ap.add_argument("--mode", default="planted", choices=["planted", "diverse"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -404,24 +404,22 @@ def main():
                      two_streams=args.streams == 2)
     torch.cuda.synchronize()
 
-    # one profiled pass with every kernel bracketed: per-class breakdown and
-    # the dominant kernel
-    _, prof_all = timed_passes(buf, dev, bwd, 1, profile_classes=hga.KERNEL_CLASSES,
-                               two_streams=False)
-    dominant = max(prof_all, key=lambda c: prof_all[c][0])
-    log(f"[bench] per-kernel ms (one pass): "
-        + ", ".join(f"{c}={v[0]:.3f}/{v[1]}" for c, v in prof_all.items() if v[1]))
-
-    # value: K passes (hga_segment_pass), nothing profiled.  Kernel times
-    # come from a second loop of one-stream passes: with the f32 pass on two
-    # streams neighbouring segments' kernels overlap, and a kernel's
-    # start-to-stop time would include time it shares the CUs.
+    # value: K passes (hga_segment_pass), nothing profiled
     log(f"[bench] timing {args.steps} passes ({args.streams} stream(s))")
     ms, _ = timed_passes(buf, dev, bwd, args.steps, two_streams=args.streams == 2)
-    log(f"[bench] timing {args.steps} one-stream passes with {dominant}'s dispatches "
+    # kernel times: a second loop of K one-stream passes in which every
+    # kernel's own dispatch stamps HIP start / stop events (the stamps add a
+    # little idle time between kernels, so the pass time above never comes
+    # from this loop; with the f32 pass on two streams neighbouring
+    # segments' kernels would overlap and share the CUs)
+    log(f"[bench] timing {args.steps} one-stream passes with every kernel's dispatches "
         f"stamping events")
-    ms_prof, prof = timed_passes(buf, dev, bwd, args.steps, profile_classes=[dominant],
+    ms_prof, prof = timed_passes(buf, dev, bwd, args.steps, profile_classes=hga.KERNEL_CLASSES,
                                  two_streams=False)
+    prof_all = {c: (v[0] / args.steps, v[1] // args.steps) for c, v in prof.items()}
+    dominant = max(prof_all, key=lambda c: prof_all[c][0])
+    log(f"[bench] per-kernel ms per pass: "
+        + ", ".join(f"{c}={v[0]:.3f}/{v[1]}" for c, v in prof_all.items() if v[1]))
     dom_ms, dom_n = prof[dominant]
 
     fl = work.flops(shape)
@@ -513,10 +511,10 @@ def main():
             "avg_launch_us": round(avg_launch_ms * 1e3, 2),
             "launches": dom_n,
             "algorithmic_flop_per_launch": per_launch_flop,
-            "timing": (f"HIP start/stop events stamped by the kernel's own dispatches "
-                       f"(hipExtLaunchKernel) on its launch stream over a timed loop of "
+            "timing": (f"HIP start/stop events stamped by every kernel's own dispatches "
+                       f"(hipExtLaunchKernel) on its launch stream over a loop of "
                        f"{args.steps} one-stream passes ({ms_prof:.4f} ms per pass with the "
-                       f"stamps)"),
+                       f"stamps); kernels_ms_per_pass averages the same loop"),
         },
     }
     out.update(extras)

@@ -1,5 +1,5 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (hga_segment_step over every segment).  Selection and
+benchmark times (hga_segment_pass: one launch per kernel over all segments).  Selection and
 summaries are compared in full; O, LSE and gradients on sampled (segment,
 sequence, KV head) groups that the fp64 oracle recomputes one by one."""
 
