@@ -325,3 +325,83 @@ def test_pass_streams_and_steps(shape, bwd):
         assert_close(key, to_np(getattr(a, key)), to_np(getattr(b, key)).astype(np.float64), tol)
     compare_all(shape, inp, a)
     compare_all(shape, inp, b)
+
+# ------------------------------------------------------- limits of the sizes
+def exact_score_inputs(shape, seed, nvalues):
+    """Inputs whose selection scores are exact small integers: every key of
+    block x is v_x * e_0 (so its summary is exactly v_x e_0), every query is
+    e_0 (so every query-block mean is exactly e_0), hence score_x = v_x with
+    no rounding on either side.  v_x in [0, nvalues) with many blocks per
+    value, so the k-th boundary falls inside a group of ties and the
+    lower-index rule decides."""
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, S, D = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.seq_len, shape.head_dim
+    nblk = S // shape.hist_block
+    vals = rng.integers(0, nvalues, size=(B, Hkv, nblk)).astype(np.float32)
+    k = np.zeros((B, Hkv, S, D), np.float32)
+    k[..., 0] = np.repeat(vals, shape.hist_block, axis=2)
+    q = np.zeros((B, Hq, S, D), np.float32)
+    q[..., 0] = 1.0
+    return {"q": q, "k": k, "v": np.zeros_like(k)}
+
+
+@pytest.mark.parametrize("dtype,nvalues", [("bf16", 200), ("f32", 2000)])
+def test_selection_at_the_size_limits(dtype, nvalues):
+    """The largest selection the library takes: 8,192 history blocks in the
+    sequence (8,128 candidates for the last segment, the LDS-sort path) and
+    top-k 1,024, with exact integer scores and ties at the k-th boundary;
+    bit-exact against the oracle for the last and a middle segment."""
+    shape = shp(seq_len=131072, seg_len=1024, hist_block=16, query_block=256, top_k=1024,
+                n_q_heads=2, n_kv_heads=1, head_dim=64, dtype=dtype)
+    assert shape.seq_len // shape.hist_block == 8192
+    inp = exact_score_inputs(shape, 3, nvalues)
+    dev = upload(inp, shape)
+    cfg = hga.Config.from_shape(shape)
+    buf = hga.Buffers(cfg, bwd=False)
+    nblk = shape.seq_len // shape.hist_block
+    hga.summarize(cfg, dev["k"], 0, nblk, buf.summ)
+    nqb = shape.n_qblocks
+    kbar = orc.block_summaries(inp["k"], shape.hist_block)
+    for s in (shape.nseg - 1, shape.nseg // 2):
+        hga.select(cfg, dev["q"], buf.summ, s, buf.sel)
+        torch.cuda.synchronize()
+        want = orc.select_segment(inp["q"], inp["k"], shape, s, kbar=kbar)
+        got = to_np(buf.sel)[:, :, s * nqb:(s + 1) * nqb]
+        np.testing.assert_array_equal(got, want, err_msg=f"segment {s}")
+        # the k-th score is shared by blocks on both sides of the cut
+        nb = s * shape.seg_len // shape.hist_block
+        sc = kbar[0, 0, :nb, 0]
+        kth = np.sort(sc)[::-1][shape.top_k - 1]
+        assert (sc == kth).sum() > (sc[want[0, 0, 0]] == kth).sum()
+
+
+def test_attention_with_top_k_1024():
+    """Forward and backward of one segment whose query blocks each attend to
+    1,024 history blocks (the top-k limit; 16,384 history keys) plus their
+    local keys, against the oracle."""
+    shape = shp(seq_len=24576, seg_len=2048, hist_block=16, query_block=128, top_k=1024,
+                n_q_heads=2, n_kv_heads=1, head_dim=64, dtype="bf16")
+    inp = make_inputs(shape, seed=21)
+    dev = upload(inp, shape)
+    cfg = hga.Config.from_shape(shape)
+    buf = hga.Buffers(cfg)
+    s = shape.nseg - 1
+    t0, L = s * shape.seg_len, shape.seg_len
+    hga.summarize(cfg, dev["k"], 0, t0 // shape.hist_block, buf.summ)
+    hga.select(cfg, dev["q"], buf.summ, s, buf.sel)
+    hga.attn_fwd(cfg, dev["q"], dev["k"], dev["v"], buf.sel, s, buf.o, buf.lse)
+    hga.attn_bwd(cfg, dev["q"], dev["k"], dev["v"], buf.o, buf.lse, dev["do"], buf.sel, s,
+                 buf.dq, buf.dk, buf.dv, buf.ws)
+    torch.cuda.synchronize()
+    nqb = shape.n_qblocks
+    sel = to_np(buf.sel)[:, :, s * nqb:(s + 1) * nqb]
+    assert (sel >= 0).sum(axis=-1).min() == 1024
+    O, LSE = orc.segment_forward(inp["q"], inp["k"], inp["v"], sel, shape, s)
+    dQ, dK, dV = orc.segment_backward(inp["q"], inp["k"], inp["v"], inp["do"], sel, shape, s,
+                                      O, LSE)
+    tol = TOL["bf16"]
+    assert_close("o", to_np(buf.o)[:, :, t0:t0 + L], O, tol)
+    assert_close("lse", to_np(buf.lse)[:, :, t0:t0 + L], LSE, tol)
+    assert_close("dq", to_np(buf.dq)[:, :, t0:t0 + L], dQ, tol)
+    assert_close("dk", to_np(buf.dk)[:, :, t0:t0 + L], dK, tol)
+    assert_close("dv", to_np(buf.dv)[:, :, t0:t0 + L], dV, tol)
