@@ -485,6 +485,9 @@ __global__ __launch_bounds__(256, 2) void dq_pass_kernel(
         const bool need_mask = is_local ? (local_first + 32 * st + 31 > qfirst)
                                         : ((it * TK + 32 * st + 32) > src.nh);
         if (need_mask) {
+          // a fence with side effects keeps this a branch: if-converted, the
+          // selects would run on every tile
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kr_ = base + 32 * st + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -987,20 +990,28 @@ __global__ __launch_bounds__(256, 2) void dkdv_pass_kernel(
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const float4 l4 = *reinterpret_cast<const float4*>(&sl[8 * r4 + 4 * hi]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&sl[64 + 8 * r4 + 4 * hi]);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pv[4 * r4 + e] = fast_exp2(fmaf(sacc[4 * r4 + e], a.c2, -lv[e] * kLog2e));
+      }
+      if (need_mask) {
+        // kept a branch (a fence with side effects): only diagonal and
+        // ragged pairs need it
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + 4 * hi + (r & 3);
+          pv[r] = (key_ok && row < nval && tk <= tq0 + row) ? pv[r] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {  // dS
+        const float4 d4 = *reinterpret_cast<const float4*>(&sl[64 + 8 * r4 + 4 * hi]);
         const float dv_[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          float p = fast_exp2(fmaf(sacc[r], a.c2, -lv[e] * kLog2e));
-          if (need_mask) {
-            const int row = 8 * r4 + 4 * hi + e;
-            p = (key_ok && row < nval && tk <= tq0 + row) ? p : 0.f;
-          }
-          pv[r] = p;
-          sacc[r] = p * (pacc[r] - dv_[e]);  // dS
-        }
+        for (int e = 0; e < 4; ++e)
+          sacc[4 * r4 + e] = pv[4 * r4 + e] * (pacc[4 * r4 + e] - dv_[e]);
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
