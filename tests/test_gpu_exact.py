@@ -127,6 +127,15 @@ def test_exact_backward_full_size_16k():
     assert_close("dq", got["dq"][0, hs], dQ[0, hs], tol)
     assert_close("dk", got["dk"][0, g], dK[0, g], tol)
     assert_close("dv", got["dv"][0, g], dV[0, g], tol)
+    # the exact pass (whole-pass kernels) on the same inputs: the same
+    # selections, the same gradient within the tolerance, for every head
+    print("[exact 16k] exact pass", flush=True)
+    dev = upload(inp, shape)
+    pas = run_exact_pass(shape, dev)
+    np.testing.assert_array_equal(pas["sel"], got["sel"])
+    for key in ("o", "lse", "dq", "dk", "dv"):
+        assert_close(f"pass {key}", pas[key], got[key].astype(np.float64), tol)
+    assert_close("pass dk (oracle head)", pas["dk"][0, g], dK[0, g], tol)
 
 
 @pytest.mark.parametrize("shape", EXACT_SHAPES + [
