@@ -261,10 +261,55 @@ int hga_segment_pass_exact(const hga_config* cfg, const void* q, const void* k, 
                            void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
                            void* stream);
 
+/* Host-RAM history tier ([JA] 背景と概要 and [FR] Contexte: the history KV
+ * is moved off the GPU to system RAM, and only the active segment's state
+ * stays in GPU memory; [JA] 深掘り分析: the block summaries stay resident,
+ * so the limit becomes host capacity; [JA] 今後の展望 and [FR]
+ * Perspectives: the transfers between GPU and host memory are the part to
+ * optimise).  hga_segment_step with the keys and values in host memory:
+ *   - k_host, v_host: [B, Hkv, S, D] bf16 in pinned host memory (hipHostMalloc,
+ *     or a pinned torch tensor), read by the GPU directly; rows 0 .. t0+L-1
+ *     must hold the keys / values (t0 = seg*L).  Never written.
+ *   - per step, on the GPU: the summaries of segment seg-1's blocks are read
+ *     from the host copy (unless HGA_STEP_SUMMARIES_READY), the selection is
+ *     made as in hga_segment_step, then the union of the blocks the
+ *     segment's query blocks chose (per (b, g), at most
+ *     C = min((L/Bq)*k, (S-L)/Bh) blocks) and the segment's own L rows are
+ *     copied from host memory into a window in ws of C*Bh + L rows per
+ *     (b, g), and forward and backward read the window.  The host never
+ *     waits for the selection.
+ *   - every other argument, and every result, is that of hga_segment_step:
+ *     o, lse, dq, dk, dv, summ and sel equal its results bit for bit (the
+ *     window keeps the chosen blocks in ascending order).
+ * HBM use per step is bounded by the window, whatever S is; the tier needs
+ * host memory for K and V only.  Requirements: bf16 (else
+ * HGA_ERR_UNSUPPORTED); k_host and v_host pinned host memory (else
+ * HGA_ERR_ARG).  ws: hga_workspace_size(cfg, HGA_OP_STEP_HOST) bytes (also
+ * without HGA_STEP_BWD); calls sharing a workspace must not overlap. */
+int hga_segment_step_host(const hga_config* cfg, int32_t seg, int32_t flags, const void* q,
+                          const void* k_host, const void* v_host, const void* dO, float* summ,
+                          int32_t* sel, void* o, float* lse, void* dq, void* dk, void* dv,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* The whole segmented pass with the host tier: hga_segment_step_host for
+ * seg = 0 .. S/L-1, with two windows in ws so that the summaries,
+ * selection and fetch of segment seg+1 run on stream2 while the attention
+ * of segment seg runs on stream (stream2 NULL: everything on stream, in
+ * order).  Results equal the steps' bit for bit.  When the call returns,
+ * everything it enqueued is ordered before later work on `stream`; both
+ * streams at default priority.  flags: HGA_STEP_BWD or 0.  ws:
+ * hga_workspace_size(cfg, HGA_OP_PASS_HOST) bytes.  The library keeps five
+ * timing-free HIP events per calling thread for the hand-offs. */
+int hga_segment_pass_host(const hga_config* cfg, int32_t flags, const void* q,
+                          const void* k_host, const void* v_host, const void* dO, float* summ,
+                          int32_t* sel, void* o, float* lse, void* dq, void* dk, void* dv,
+                          void* ws, size_t ws_bytes, void* stream, void* stream2);
+
 /* Workspace bytes for an operation (0 if none is needed), or 0 with
  * hga_last_error() set if the config is invalid. */
 enum { HGA_OP_FWD = 0, HGA_OP_BWD = 1, HGA_OP_STEP = 2, HGA_OP_DECODE = 3,
-       HGA_OP_STEP_EXACT = 4, HGA_OP_PASS = 5, HGA_OP_PASS_EXACT = 6 };
+       HGA_OP_STEP_EXACT = 4, HGA_OP_PASS = 5, HGA_OP_PASS_EXACT = 6,
+       HGA_OP_STEP_HOST = 7, HGA_OP_PASS_HOST = 8 };
 size_t hga_workspace_size(const hga_config* cfg, int32_t op);
 
 /* Message of the last failure on this thread ("" if none). */
@@ -292,7 +337,9 @@ enum {
   HGA_K_DECODE = 7,
   HGA_K_DECODE_MERGE = 8,
   HGA_K_BWD_HIST = 9,
-  HGA_KCLASS_COUNT = 10
+  HGA_K_TIER_PLAN = 10,
+  HGA_K_TIER_FETCH = 11,
+  HGA_KCLASS_COUNT = 12
 };
 int hga_profile_begin(uint32_t mask);
 int hga_profile_end(double* ms, int64_t* count);

@@ -28,10 +28,10 @@ HGA_F32 = 0
 HGA_BF16 = 1
 HGA_STEP_BWD = 1
 (HGA_OP_FWD, HGA_OP_BWD, HGA_OP_STEP, HGA_OP_DECODE, HGA_OP_STEP_EXACT, HGA_OP_PASS,
- HGA_OP_PASS_EXACT) = range(7)
+ HGA_OP_PASS_EXACT, HGA_OP_STEP_HOST, HGA_OP_PASS_HOST) = range(9)
 HGA_STEP_SUMMARIES_READY = 2
 KERNEL_CLASSES = ("summarize", "select", "gather", "fwd", "bwd_pre", "bwd_dq", "bwd_dkdv",
-                  "decode", "decode_merge", "bwd_hist")
+                  "decode", "decode_merge", "bwd_hist", "tier_plan", "tier_fetch")
 
 
 class HGAError(RuntimeError):
@@ -82,6 +82,11 @@ _SIGNATURES = {
                                         _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "hga_segment_pass": (ctypes.c_int, [_CP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P,
                                         _P, _P, _P, _P, ctypes.c_size_t, _P, _P]),
+    "hga_segment_step_host": (ctypes.c_int, [_CP, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
+                                             _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             ctypes.c_size_t, _P]),
+    "hga_segment_pass_host": (ctypes.c_int, [_CP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
+                                             _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "hga_segment_step_exact": (ctypes.c_int, [_CP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
                                               _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                               _P]),
@@ -149,6 +154,22 @@ def _ptr(t, name, dtype=None, shape=None, allow_none=False):
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
     if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _host_ptr(t, name, dtype, shape):
+    """A pinned host tensor (the host tier's K / V)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cpu" or not t.is_pinned():
+        raise ValueError(f"{name} must be a pinned host tensor (pin_memory=True)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
     return ctypes.c_void_p(t.data_ptr())
 
@@ -338,6 +359,55 @@ def segment_pass(cfg: Config, q, k, v, summ, sel, o, lse=None, do=None, dq=None,
         _ptr(ws, "ws", allow_none=not bwd),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(),
         None if stream2 is None else ctypes.c_void_p(stream2.cuda_stream)))
+
+
+def _host_args(cfg: Config, q, k_host, v_host, summ, sel, o, lse, do, dq, dk, dv, ws, bwd):
+    s = Shapes(cfg)
+    torch = _torch()
+    return [_ptr(q, "q", s.dt, s.q), _host_ptr(k_host, "k_host", s.dt, s.kv),
+            _host_ptr(v_host, "v_host", s.dt, s.kv),
+            _ptr(do, "do", s.dt, s.q, allow_none=not bwd),
+            _ptr(summ, "summ", torch.float32, s.summ), _ptr(sel, "sel", torch.int32, s.sel),
+            _ptr(o, "o", s.dt, s.q),
+            _ptr(lse, "lse", torch.float32, s.lse, allow_none=not bwd),
+            _ptr(dq, "dq", s.dt, s.q, allow_none=not bwd),
+            _ptr(dk, "dk", s.dt, s.kv, allow_none=not bwd),
+            _ptr(dv, "dv", s.dt, s.kv, allow_none=not bwd),
+            _ptr(ws, "ws"), ws.numel() * ws.element_size()]
+
+
+def host_workspace(cfg: Config, op: int = HGA_OP_PASS_HOST):
+    """A device workspace for hga_segment_step_host / hga_segment_pass_host."""
+    torch = _torch()
+    return torch.empty(max(workspace_size(cfg, op), 256), dtype=torch.uint8, device="cuda")
+
+
+def segment_step_host(cfg: Config, seg: int, q, k_host, v_host, summ, sel, o, lse=None,
+                      do=None, dq=None, dk=None, dv=None, ws=None, bwd: bool = True,
+                      summaries_ready: bool = False) -> None:
+    """hga_segment_step_host: k_host / v_host pinned host tensors [B, Hkv, S, D];
+    ws of workspace_size(cfg, HGA_OP_STEP_HOST) bytes."""
+    if ws is None:
+        ws = host_workspace(cfg, HGA_OP_STEP_HOST)
+    flags = (HGA_STEP_BWD if bwd else 0) | (HGA_STEP_SUMMARIES_READY if summaries_ready else 0)
+    _check(lib().hga_segment_step_host(
+        ctypes.byref(cfg), seg, flags,
+        *_host_args(cfg, q, k_host, v_host, summ, sel, o, lse, do, dq, dk, dv, ws, bwd),
+        _stream()))
+
+
+def segment_pass_host(cfg: Config, q, k_host, v_host, summ, sel, o, lse=None, do=None,
+                      dq=None, dk=None, dv=None, ws=None, bwd: bool = True,
+                      stream2=None) -> None:
+    """hga_segment_pass_host on the current stream, the fetches on stream2 (a torch
+    stream at default priority) when given; ws of workspace_size(cfg,
+    HGA_OP_PASS_HOST) bytes."""
+    if ws is None:
+        ws = host_workspace(cfg, HGA_OP_PASS_HOST)
+    _check(lib().hga_segment_pass_host(
+        ctypes.byref(cfg), HGA_STEP_BWD if bwd else 0,
+        *_host_args(cfg, q, k_host, v_host, summ, sel, o, lse, do, dq, dk, dv, ws, bwd),
+        _stream(), None if stream2 is None else ctypes.c_void_p(stream2.cuda_stream)))
 
 
 class Buffers:

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhga.so")
-SOURCES = ["hga_api.cpp", "hga_select.hip", "hga_fwd.hip", "hga_bwd.hip", "hga_decode.hip"]
+SOURCES = ["hga_api.cpp", "hga_select.hip", "hga_fwd.hip", "hga_bwd.hip", "hga_decode.hip",
+           "hga_tier.hip"]
 
 
 def hipcc() -> str:

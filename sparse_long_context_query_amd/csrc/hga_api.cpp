@@ -3,6 +3,7 @@
 // before anything is enqueued; no C++ exception leaves this file.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -94,6 +95,8 @@ int make_prob(const hga_config* c, hga::Prob* p) {
   p->nqb = p->L / p->Bq;
   p->nqb_all = p->S / p->Bq;
   p->nblk = p->S / p->Bh;
+  p->kv_rows = p->S;
+  p->kv_local = -1;
   return HGA_OK;
 }
 
@@ -155,6 +158,8 @@ size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 // (written by the forward launch, read by the backward launches).  f32: one
 // step workspace per stream.
 size_t pass_exact_workspace_bytes(const hga::Prob& p);
+size_t tier_workspace_bytes(const hga::Prob& p, int nwin);
+int check_tier(const hga::Prob& p);
 
 size_t pass_workspace_bytes(const hga::Prob& p) {
   if (p.dtype == HGA_BF16) return (size_t)(p.S / p.L) * hga::bwd_delta_bytes(p);
@@ -199,6 +204,11 @@ size_t hga_workspace_size(const hga_config* cfg, int32_t op) {
     case HGA_OP_PASS_EXACT:
       ok();
       return pass_exact_workspace_bytes(p);
+    case HGA_OP_STEP_HOST:
+    case HGA_OP_PASS_HOST:
+      if (check_tier(p)) return 0;
+      ok();
+      return tier_workspace_bytes(p, op == HGA_OP_STEP_HOST ? 1 : 2);
     default:
       fail(HGA_ERR_ARG, "unknown op %d", op);
       return 0;
@@ -370,6 +380,126 @@ hipError_t pass_events(hipEvent_t* a, hipEvent_t* b) {
   return hipSuccess;
 }
 
+// ---- host-RAM history tier -------------------------------------------------
+// Workspace: the backward's scratch, the selection in window slots (wsel,
+// the layout of sel), then one or two windows, each the K and V rows
+// [B, Hkv, C*Bh + L, D] (C = tier_slots), the slot list [B, Hkv, C] and the
+// union sizes [B, Hkv].
+struct TierWs {
+  void* bws;
+  int32_t* wsel;
+  void* kw[2];
+  void* vw[2];
+  int32_t* list[2];
+  int32_t* count[2];
+};
+
+size_t tier_kv_bytes(const hga::Prob& p) {
+  return round256((size_t)p.B * p.Hkv * hga::tier_rows(p) * p.D * 2);
+}
+size_t tier_list_bytes(const hga::Prob& p) {
+  return round256((size_t)p.B * p.Hkv * std::max(hga::tier_slots(p), 1) * sizeof(int32_t));
+}
+size_t tier_count_bytes(const hga::Prob& p) {
+  return round256((size_t)p.B * p.Hkv * sizeof(int32_t));
+}
+size_t tier_wsel_bytes(const hga::Prob& p) {
+  return round256((size_t)p.B * p.Hkv * p.nqb_all * p.K * sizeof(int32_t));
+}
+size_t tier_workspace_bytes(const hga::Prob& p, int nwin) {
+  const size_t win = 2 * tier_kv_bytes(p) + tier_list_bytes(p) + tier_count_bytes(p);
+  return round256(hga::bwd_workspace_bytes(p)) + tier_wsel_bytes(p) + nwin * win;
+}
+TierWs tier_carve(const hga::Prob& p, void* ws, int nwin) {
+  TierWs t;
+  char* c = (char*)ws;
+  t.bws = c;
+  c += round256(hga::bwd_workspace_bytes(p));
+  t.wsel = (int32_t*)c;
+  c += tier_wsel_bytes(p);
+  for (int w = 0; w < 2; ++w) {
+    if (w < nwin) {
+      t.kw[w] = c; c += tier_kv_bytes(p);
+      t.vw[w] = c; c += tier_kv_bytes(p);
+      t.list[w] = (int32_t*)c; c += tier_list_bytes(p);
+      t.count[w] = (int32_t*)c; c += tier_count_bytes(p);
+    } else {
+      t.kw[w] = t.kw[0]; t.vw[w] = t.vw[0]; t.list[w] = t.list[0]; t.count[w] = t.count[0];
+    }
+  }
+  return t;
+}
+
+// The device address of pinned host memory (the kernels read it directly).
+int host_pointer(const void* h, const char* name, const void** dptr) {
+  hipPointerAttribute_t at;
+  const hipError_t e = hipPointerGetAttributes(&at, h);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(HGA_ERR_ARG, "%s is not pinned host memory (%s)", name, hipGetErrorString(e));
+  }
+  if (at.type != hipMemoryTypeHost || at.devicePointer == nullptr)
+    return fail(HGA_ERR_ARG, "%s is not pinned host memory", name);
+  *dptr = at.devicePointer;
+  return HGA_OK;
+}
+
+int check_tier(const hga::Prob& p) {
+  if (p.dtype != HGA_BF16)
+    return fail(HGA_ERR_UNSUPPORTED, "the host tier runs the bf16 kernels only");
+  return HGA_OK;
+}
+
+// The selection of segment seg, then the fetch of what it chose, on st.
+int tier_fetch_step(const hga::Prob& p, int32_t seg, bool summarize, const void* q,
+                    const void* kh, const void* vh, float* summ, int32_t* sel, const TierWs& t,
+                    int w, hipStream_t st) {
+  hipError_t e;
+  if (seg > 0 && summarize) {
+    // blocks closed by segment seg-1, read from the host copy
+    e = hga::launch_summarize(p, kh, (seg - 1) * p.L / p.Bh, seg * p.L / p.Bh, summ, st);
+    if (e != hipSuccess) return hip_fail(e, "summarize launch");
+  }
+  e = hga::launch_select(p, q, summ, seg, sel, st);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  e = hga::launch_tier_plan(p, sel, seg, t.wsel, t.list[w], t.count[w], st);
+  if (e != hipSuccess) return hip_fail(e, "tier plan launch");
+  e = hga::launch_tier_fetch(p, kh, vh, t.list[w], t.count[w], seg, t.kw[w], t.vw[w], st);
+  if (e != hipSuccess) return hip_fail(e, "tier fetch launch");
+  return HGA_OK;
+}
+
+// The attention of segment seg over window w, on st.
+int tier_attn_step(const hga::Prob& p, int32_t seg, bool bwd, const void* q, const void* dO,
+                   void* o, float* lse, void* dq, void* dk, void* dv, const TierWs& t, int w,
+                   hipStream_t st) {
+  hga::Prob pw = p;
+  pw.kv_rows = hga::tier_rows(p);
+  pw.kv_local = hga::tier_slots(p) * p.Bh;
+  hipError_t e = hga::launch_fwd(pw, q, t.kw[w], t.vw[w], t.wsel, seg, o, lse, st,
+                                 bwd ? dO : nullptr, bwd ? (float*)t.bws : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  if (bwd) {
+    e = hga::launch_bwd(pw, q, t.kw[w], t.vw[w], o, lse, dO, t.wsel, seg, dq, dk, dv,
+                        (float*)t.bws, st, true);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+  }
+  return HGA_OK;
+}
+
+// Events for the host-tier pass: [0, 2) fetch of window w done, [2, 4)
+// attention over window w done, [4] inputs ready (created on first use).
+hipError_t tier_events(hipEvent_t** out) {
+  thread_local hipEvent_t ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  for (int i = 0; i < 5; ++i)
+    if (ev[i] == nullptr) {
+      hipError_t e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+    }
+  *out = ev;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -388,6 +518,90 @@ int hga_segment_step(const hga_config* cfg, int32_t seg, int32_t flags, const vo
   if ((rc = run_step(p, seg, flags, q, k, v, dO, summ, sel, o, lse, dq, dk, dv, ws,
                      (hipStream_t)stream)))
     return rc;
+  return ok();
+}
+
+int hga_segment_step_host(const hga_config* cfg, int32_t seg, int32_t flags, const void* q,
+                          const void* k_host, const void* v_host, const void* dO, float* summ,
+                          int32_t* sel, void* o, float* lse, void* dq, void* dk, void* dv,
+                          void* ws, size_t ws_bytes, void* stream) {
+  hga::Prob p;
+  int rc = make_prob(cfg, &p);
+  if (rc) return rc;
+  if ((rc = check_tier(p))) return rc;
+  if ((rc = check_seg(p, seg))) return rc;
+  const size_t need = tier_workspace_bytes(p, 1);
+  if ((rc = check_step_args(p, flags, q, k_host, v_host, dO, summ, sel, o, lse, dq, dk, dv, ws,
+                            ws_bytes, need)))
+    return rc;
+  HGA_REQUIRE(ws);
+  if (ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, need);
+  const void *kh, *vh;
+  if ((rc = host_pointer(k_host, "k_host", &kh))) return rc;
+  if ((rc = host_pointer(v_host, "v_host", &vh))) return rc;
+  const TierWs t = tier_carve(p, ws, 1);
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = tier_fetch_step(p, seg, !(flags & HGA_STEP_SUMMARIES_READY), q, kh, vh, summ, sel, t,
+                            0, st)))
+    return rc;
+  if ((rc = tier_attn_step(p, seg, (flags & HGA_STEP_BWD) != 0, q, dO, o, lse, dq, dk, dv, t, 0,
+                           st)))
+    return rc;
+  return ok();
+}
+
+int hga_segment_pass_host(const hga_config* cfg, int32_t flags, const void* q,
+                          const void* k_host, const void* v_host, const void* dO, float* summ,
+                          int32_t* sel, void* o, float* lse, void* dq, void* dk, void* dv,
+                          void* ws, size_t ws_bytes, void* stream, void* stream2) {
+  hga::Prob p;
+  int rc = make_prob(cfg, &p);
+  if (rc) return rc;
+  if ((rc = check_tier(p))) return rc;
+  if (flags & HGA_STEP_SUMMARIES_READY)
+    return fail(HGA_ERR_ARG, "the pass summarizes the history itself");
+  const size_t need = tier_workspace_bytes(p, 2);
+  if ((rc = check_step_args(p, flags, q, k_host, v_host, dO, summ, sel, o, lse, dq, dk, dv, ws,
+                            ws_bytes, need)))
+    return rc;
+  HGA_REQUIRE(ws);
+  if (ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, need);
+  const void *kh, *vh;
+  if ((rc = host_pointer(k_host, "k_host", &kh))) return rc;
+  if ((rc = host_pointer(v_host, "v_host", &vh))) return rc;
+  const TierWs t = tier_carve(p, ws, 2);
+  const bool bwd = (flags & HGA_STEP_BWD) != 0;
+  // attention on stream, the next segment's selection and fetch on stream2
+  hipStream_t sa = (hipStream_t)stream;
+  hipStream_t sf = stream2 != nullptr ? (hipStream_t)stream2 : sa;
+  const bool two = sf != sa;
+  hipEvent_t* ev = nullptr;
+  hipError_t e;
+  if (two) {
+    if ((e = tier_events(&ev)) != hipSuccess) return hip_fail(e, "event create");
+    if ((e = hipEventRecord(ev[4], sa)) != hipSuccess) return hip_fail(e, "event record");
+    if ((e = hipStreamWaitEvent(sf, ev[4], 0)) != hipSuccess) return hip_fail(e, "stream wait");
+  }
+  const int nseg = p.S / p.L;
+  for (int seg = 0; seg < nseg; ++seg) {
+    const int w = seg & 1;
+    // window w was last read by the attention of segment seg-2
+    if (two && seg >= 2 && (e = hipStreamWaitEvent(sf, ev[2 + w], 0)) != hipSuccess)
+      return hip_fail(e, "stream wait");
+    if ((rc = tier_fetch_step(p, seg, true, q, kh, vh, summ, sel, t, w, sf))) return rc;
+    if (two) {
+      if ((e = hipEventRecord(ev[w], sf)) != hipSuccess) return hip_fail(e, "event record");
+      if ((e = hipStreamWaitEvent(sa, ev[w], 0)) != hipSuccess) return hip_fail(e, "stream wait");
+    }
+    if ((rc = tier_attn_step(p, seg, bwd, q, dO, o, lse, dq, dk, dv, t, w, sa))) return rc;
+    if (two && (e = hipEventRecord(ev[2 + w], sa)) != hipSuccess)
+      return hip_fail(e, "event record");
+  }
+  // stream waited for every fetch-stream launch (the last fetch's event)
   return ok();
 }
 

@@ -42,6 +42,8 @@ struct BwdArgs {
   // the gradient that later segments' queries gave each key (dK scaled)
   float* hdk;
   float* hdv;
+  int Skv;    // step kernels: K/V rows per (b, g)
+  int kv_t0;  // step kernels: K/V row of the segment's first key
 };
 
 // ---------------------------------------------------------------------------
@@ -203,12 +205,12 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
   // partial-sum finish and the compaction (local tiles come first in the
   // walk order)
   const int nloc = (blk_qmax - t0) / TK + 1;  // local tiles any wave of the block sees
-  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.S * (2 * D));
+  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.Skv * D;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.Skv * (2 * D));
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.Skv * (2 * D));
   if (half < nloc) {
     KeySource<TK> loc;
-    loc.init(s_hlist, 0, a.Bh, t0, t0 + a.L);
+    loc.init(s_hlist, 0, a.Bh, a.kv_t0, a.kv_t0 + a.L);  // K/V rows, not tokens
     dma_kv_tile<D, TK>(loc, half, kr, vr, s_tiles[half][0], s_tiles[half][0] + TILE_B, wr, lane);
   }
   const int tq = qfirst + lq;
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
   const int32_t* srow = sel + ((size_t)(b * a.Hkv + g) * a.nqb_all + (size_t)a.seg * a.nqb + j) * a.K;
   const int nsel = compact_selection(srow, a.K, nb, s_hlist, &s_hcount);
   KeySource<TK> src;
-  src.init(s_hlist, nsel, a.Bh, t0, t0 + a.L);
+  src.init(s_hlist, nsel, a.Bh, a.kv_t0, a.kv_t0 + a.L);
   const int ntiles = src.n_hist_tiles + nloc;
   const int n0 = (ntiles + 1) / 2;  // walk positions of half 0; half 1 has ntiles - n0
   const int nht = src.n_hist_tiles;
@@ -627,7 +629,7 @@ __device__ __forceinline__ void dkdv_item(
   unsigned char* s_q = s_raw + 2 * TILE_B + wave * SLICE_B;
   unsigned char* s_do = s_q + TILE_B;
   float* s_ld = reinterpret_cast<float*>(s_do + TILE_B);  // [0,32) lse, [32,64) delta
-  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
+  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;  // dK / dV rows (tokens)
   // K and V rows of this key tile, shared by the 8 waves (lane (key lq, hi)
   // reads K[key][16kk + 8hi .. +7]); the barrier also retires the previous
   // item's reads of the fold buffer that overlaps these tiles
@@ -635,9 +637,12 @@ __device__ __forceinline__ void dkdv_item(
   const int nkey = HIST ? kvalid : min(32, tend - kfirst);  // key rows that exist
   const int tk = kfirst + lq;
   const bool key_ok = lq < nkey;
+  // the tile's first row in the K / V storage (its token in full-sequence
+  // storage)
+  const size_t kin = (size_t)(b * a.Hkv + g) * a.Skv * D + (size_t)(kfirst - t0 + a.kv_t0) * D;
   __syncthreads();
-  if (wave == 0) dma_rows<D>(k + kv_base + (size_t)kfirst * D, 32, nkey, s_k, lane);
-  if (wave == 1) dma_rows<D>(v + kv_base + (size_t)kfirst * D, 32, nkey, s_v, lane);
+  if (wave == 0) dma_rows<D>(k + kin, 32, nkey, s_k, lane);
+  if (wave == 1) dma_rows<D>(v + kin, 32, nkey, s_v, lane);
   drain_vmem_loads();
   __syncthreads();
 
@@ -1328,6 +1333,8 @@ BwdArgs make_args(const Prob& p, int seg) {
   a.hdk = a.hdv = nullptr;
   a.nseg = 1;
   a.dchunk = 0;
+  a.Skv = p.kv_rows;
+  a.kv_t0 = p.kv_local >= 0 ? p.kv_local : seg * p.L;
   return a;
 }
 
@@ -1485,7 +1492,7 @@ hipError_t launch_bwd_pass(const Prob& p, const void* q, const void* k, const vo
                            int nseg, void* dq, void* dk, void* dv, const float* delta,
                            size_t dstride, hipStream_t st, const float* hist_dk,
                            const float* hist_dv) {
-  if (p.dtype != HGA_BF16) return hipErrorInvalidValue;
+  if (p.dtype != HGA_BF16 || p.kv_rows != p.S) return hipErrorInvalidValue;
   return p.D == 64 ? bwd_pass_bf16<64>(p, q, k, v, lse, dO, sel, seg0, nseg, dq, dk, dv, delta,
                                        dstride, st, hist_dk, hist_dv)
                    : bwd_pass_bf16<128>(p, q, k, v, lse, dO, sel, seg0, nseg, dq, dk, dv, delta,
@@ -1506,7 +1513,7 @@ hipError_t launch_hist_exact(const Prob& p, const void* q, const void* k, const 
                              const float* lse, const void* dO, const int32_t* sel, int seg,
                              const float* delta_seg, float* hist_dk, float* hist_dv, void* list_ws,
                              hipStream_t st) {
-  if (p.dtype != HGA_BF16) return hipErrorInvalidValue;
+  if (p.dtype != HGA_BF16 || p.kv_rows != p.S) return hipErrorInvalidValue;
   const int maxd = hist_max_entries(p);
   if (seg <= 0 || maxd <= 0) return hipSuccess;
   BwdArgs a = make_args(p, seg);
@@ -1541,6 +1548,9 @@ hipError_t launch_bwd(const Prob& p, const void* q, const void* k, const void* v
                       const void* o, const float* lse, const void* dO, const int32_t* sel,
                       int seg, void* dq, void* dk, void* dv, float* delta_ws, hipStream_t st,
                       bool delta_ready, float* hist_dk, float* hist_dv, float* partials) {
+  // the f32 kernels and the exact gradient read full-sequence K / V only
+  if ((p.dtype != HGA_BF16 || hist_dk != nullptr) && p.kv_rows != p.S)
+    return hipErrorInvalidValue;
   if (p.dtype == HGA_BF16)
     return p.D == 64 ? bwd_bf16<64>(p, q, k, v, o, lse, dO, sel, seg, dq, dk, dv, delta_ws, st,
                                     delta_ready, hist_dk, hist_dv, partials)

@@ -27,6 +27,8 @@ struct FwdArgs {
   int nq32;   // 32-row query sub-blocks per query block
   float c2;   // softmax scale * log2(e)
   int dchunk; // whole-pass kernel: floats between the delta rows of two segments
+  int Skv;    // step kernel: K/V rows per (b, g)
+  int kv_t0;  // step kernel: K/V row of the segment's first key
 };
 
 // ---------------------------------------------------------------------------
@@ -111,15 +113,15 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(
   const int32_t* srow = sel + ((size_t)(b * a.Hkv + g) * a.nqb_all + (size_t)a.seg * a.nqb + j) * a.K;
   const int nsel = compact_selection(srow, a.K, nb, s_hlist, &s_hcount);
   KeySource<TK> src;
-  src.init(s_hlist, nsel, a.Bh, t0, t0 + a.L);
+  src.init(s_hlist, nsel, a.Bh, a.kv_t0, a.kv_t0 + a.L);  // K/V rows, not tokens
   const int ntiles = src.n_hist_tiles + (blk_qmax - t0) / TK + 1;
   const int n0 = (ntiles + 1) / 2;              // tiles of half 0
   const int my_first = half ? n0 : 0;
   const int my_count = half ? ntiles - n0 : n0;
 
-  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.S * (2 * D));
+  const size_t kv_base = (size_t)(b * a.Hkv + g) * a.Skv * D;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.Skv * (2 * D));
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.Skv * (2 * D));
   const __amdgpu_buffer_rsrc_t kr_none = make_rsrc(k + kv_base, 0u);
   const __amdgpu_buffer_rsrc_t vr_none = make_rsrc(v + kv_base, 0u);
 
@@ -647,6 +649,8 @@ FwdArgs make_args(const Prob& p, int seg) {
   a.S = p.S; a.L = p.L; a.Bh = p.Bh; a.Bq = p.Bq; a.K = p.K; a.Hq = p.Hq; a.Hkv = p.Hkv;
   a.G = p.G; a.nqb = p.nqb; a.nqb_all = p.nqb_all; a.seg = seg;
   a.B = p.B; a.nseg = 1; a.dchunk = 0;
+  a.Skv = p.kv_rows;
+  a.kv_t0 = p.kv_local >= 0 ? p.kv_local : seg * p.L;
   a.nq32 = (p.Bq + 31) / 32;
   a.wpu = (p.G * a.nq32 + 3) / 4;
   a.c2 = p.scale * kLog2e;
@@ -696,7 +700,7 @@ bool fused_delta(const Prob& p) { return p.dtype == HGA_BF16; }
 hipError_t launch_fwd_pass(const Prob& p, const void* q, const void* k, const void* v,
                            const int32_t* sel, int seg0, int nseg, void* o, float* lse,
                            hipStream_t st, const void* dO, float* delta, size_t delta_stride) {
-  if (p.dtype != HGA_BF16) return hipErrorInvalidValue;
+  if (p.dtype != HGA_BF16 || p.kv_rows != p.S) return hipErrorInvalidValue;
   if (dO == nullptr) delta = nullptr;
   return p.D == 64 ? fwd_pass_bf16<64>(p, q, k, v, sel, seg0, nseg, o, lse, st, dO, delta,
                                        delta_stride)
@@ -708,6 +712,7 @@ hipError_t launch_fwd(const Prob& p, const void* q, const void* k, const void* v
                       const int32_t* sel, int seg, void* o, float* lse, hipStream_t st,
                       const void* dO, float* delta) {
   if (dO == nullptr || !fused_delta(p)) delta = nullptr;
+  if (p.dtype != HGA_BF16 && p.kv_rows != p.S) return hipErrorInvalidValue;
   if (p.dtype == HGA_BF16)
     return p.D == 64 ? fwd_bf16<64>(p, q, k, v, sel, seg, o, lse, st, dO, delta)
                      : fwd_bf16<128>(p, q, k, v, sel, seg, o, lse, st, dO, delta);

@@ -24,6 +24,13 @@ struct Prob {
   int nqb;        // query blocks per segment  = L / Bq
   int nqb_all;    // query blocks per sequence = S / Bq
   int nblk;       // history blocks per sequence = S / Bh
+  // K/V storage the step kernels read (bf16 only): rows per (b, g) and the
+  // row of the segment's first key.  Full-sequence storage: kv_rows = S and
+  // kv_local = -1 (a key's row is its token index).  The host tier's window
+  // holds the chosen history blocks at rows slot * Bh and the segment's own
+  // keys from row kv_local on.
+  int kv_rows;
+  int kv_local;
 };
 
 constexpr int kMaxCandidates = 8192;   // S / Bh limit of the selection sort
@@ -104,6 +111,23 @@ hipError_t launch_decode(const Prob& p, int pos, int n, const void* q_new, const
 size_t decode_workspace_bytes(const Prob& p);
 float* decode_score_ws(const Prob& p, void* ws);
 int decode_max_rows();  // limit of G * n
+
+// ---- host-RAM history tier (bf16) -----------------------------------------
+// Window slots per (b, g): C = min(nqb * K, (S - L) / Bh) history blocks, the
+// most one segment's query blocks can select together; window rows C*Bh + L.
+int tier_slots(const Prob& p);
+int tier_rows(const Prob& p);
+// Segment seg: the union of the blocks its query blocks chose (sel), per
+// (b, g) in ascending order -> list [B, Hkv, C] and count [B, Hkv]; wsel
+// (the layout of sel) gets each entry's slot in that union, -1 kept.
+hipError_t launch_tier_plan(const Prob& p, const int32_t* sel, int seg, int32_t* wsel,
+                            int32_t* list, int32_t* count, hipStream_t st);
+// Copies the listed blocks of the host K / V [B, Hkv, S, D] (device-mapped
+// pinned memory) into window rows slot * Bh, and the segment's rows into
+// window rows C * Bh .. C * Bh + L - 1 (window [B, Hkv, C*Bh + L, D]).
+hipError_t launch_tier_fetch(const Prob& p, const void* k_host, const void* v_host,
+                             const int32_t* list, const int32_t* count, int seg, void* kw,
+                             void* vw, hipStream_t st);
 
 // ---- profiling hooks (no-ops unless hga_profile_begin() was called) -----
 // While kernel class kclass is profiled, returns true with a start / stop

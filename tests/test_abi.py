@@ -212,6 +212,54 @@ def test_exact_pass_validation(L):
     assert call(wide) == hga.HGA_ERR_UNSUPPORTED and "64" in hga.last_error()
 
 
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
+def test_host_tier_validation(L):
+    cfg = good_cfg()
+    B, Hkv, D, Bh, Lseg = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.hist_block, cfg.seg_len
+    # window slots: the most one segment's query blocks can choose together
+    C = min((Lseg // cfg.query_block) * cfg.top_k, (cfg.seq_len - Lseg) // Bh)
+    assert C == 240
+    window = 2 * _r256(B * Hkv * (C * Bh + Lseg) * D * 2) + _r256(B * Hkv * C * 4) + _r256(B * Hkv * 4)
+    wsel = _r256(B * Hkv * (cfg.seq_len // cfg.query_block) * cfg.top_k * 4)
+    step = L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_STEP_HOST)
+    two = L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_PASS_HOST)
+    bwd = _r256(L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_STEP))
+    assert step == bwd + wsel + window and two == step + window
+    # the window does not grow with the sequence once the selection bounds it
+    long = good_cfg(seq_len=131072, hist_block=128, query_block=128, top_k=16)
+    C2 = min(8 * 16, (131072 - 1024) // 128)
+    assert C2 == 128
+    win2 = 2 * _r256(B * Hkv * (C2 * 128 + 1024) * D * 2)
+    need_long = L.hga_workspace_size(ctypes.byref(long), hga.HGA_OP_STEP_HOST)
+    assert win2 < need_long < win2 + (12 << 20)  # + the backward's scratch and wsel
+    assert need_long < (2 * B * Hkv * 131072 * D * 2) // 6  # vs K and V resident: 512 MiB
+    f32 = good_cfg(dtype=hga.HGA_F32)
+    assert L.hga_workspace_size(ctypes.byref(f32), hga.HGA_OP_STEP_HOST) == 0
+    assert "bf16" in hga.last_error()
+
+    def step_call(c, flags=hga.HGA_STEP_BWD, ws_bytes=step, seg=1, dq=FAKE):
+        return L.hga_segment_step_host(ctypes.byref(c), seg, flags, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, FAKE, dq, FAKE, FAKE, FAKE, ws_bytes, None)
+
+    def pass_call(c, flags=hga.HGA_STEP_BWD, ws_bytes=two, dq=FAKE):
+        return L.hga_segment_pass_host(ctypes.byref(c), flags, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, dq, FAKE, FAKE, FAKE, ws_bytes, None, FAKE)
+
+    assert step_call(f32) == hga.HGA_ERR_UNSUPPORTED and "bf16" in hga.last_error()
+    assert pass_call(f32) == hga.HGA_ERR_UNSUPPORTED
+    assert step_call(cfg, seg=16) == hga.HGA_ERR_ARG
+    assert step_call(cfg, dq=None) == hga.HGA_ERR_ARG and "dq is NULL" in hga.last_error()
+    assert step_call(cfg, ws_bytes=step - 1) == hga.HGA_ERR_WORKSPACE
+    # the forward alone needs the window too
+    assert step_call(cfg, flags=0, ws_bytes=step - 1) == hga.HGA_ERR_WORKSPACE
+    assert pass_call(cfg, ws_bytes=two - 1) == hga.HGA_ERR_WORKSPACE
+    assert pass_call(cfg, flags=hga.HGA_STEP_BWD | hga.HGA_STEP_SUMMARIES_READY) == hga.HGA_ERR_ARG
+    assert pass_call(cfg, flags=8) == hga.HGA_ERR_ARG and "flags" in hga.last_error()
+
+
 def test_segment_pass_validation(L):
     cfg = good_cfg()
     two = L.hga_workspace_size(ctypes.byref(cfg), hga.HGA_OP_PASS)

@@ -1,0 +1,214 @@
+"""Host-RAM history tier on the GPU: K and V in pinned host memory, each
+segment's chosen history blocks and its own rows fetched into a bounded HBM
+window.  The window keeps the chosen blocks in ascending order, so every
+result must equal the resident steps' (hga_segment_step) bit for bit; the
+resident steps are checked against the fp64 oracle in the parity tests, and
+the tier is also checked against the oracle directly on two workloads here."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from oracle import hga_oracle as orc
+from synth import HGAShape, WORKLOADS, make_inputs
+
+from gpu_util import TOL, assert_close, to_np, upload
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import sparse_long_context_query_amd as hga  # noqa: E402
+
+OUTPUTS = ("summ", "sel", "o", "lse", "dq", "dk", "dv")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hga.lib()
+
+
+def shp(**kw):
+    base = dict(name="t", batch=1, seq_len=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                seg_len=128, hist_block=32, query_block=32, top_k=3, dtype="bf16")
+    base.update(kw)
+    return HGAShape(**base)
+
+
+def host_kv(dev):
+    return dev["k"].cpu().pin_memory(), dev["v"].cpu().pin_memory()
+
+
+def resident_steps(shape, dev, bwd):
+    cfg = hga.Config.from_shape(shape)
+    buf = hga.Buffers(cfg, bwd=bwd)
+    buf.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do") if bwd else None, bwd=bwd,
+                 per_step=True)
+    torch.cuda.synchronize()
+    return buf
+
+
+def host_run(shape, dev, bwd, mode, kv=None):
+    """mode: "steps" (hga_segment_step_host per segment), "pass1" (the pass on
+    one stream) or "pass2" (fetches on a second stream)."""
+    cfg = hga.Config.from_shape(shape)
+    buf = hga.Buffers(cfg, bwd=bwd)
+    kh, vh = kv if kv is not None else host_kv(dev)
+    do = dev.get("do") if bwd else None
+    if mode == "steps":
+        ws = hga.host_workspace(cfg, hga.HGA_OP_STEP_HOST)
+        for s in range(shape.nseg):
+            print(f"[tier] {shape.name} step {s}", flush=True)
+            hga.segment_step_host(cfg, s, dev["q"], kh, vh, buf.summ, buf.sel, buf.o, buf.lse,
+                                  do, buf.dq, buf.dk, buf.dv, ws=ws, bwd=bwd)
+    else:
+        print(f"[tier] {shape.name} {mode}", flush=True)
+        hga.segment_pass_host(cfg, dev["q"], kh, vh, buf.summ, buf.sel, buf.o, buf.lse, do,
+                              buf.dq, buf.dk, buf.dv, bwd=bwd,
+                              stream2=buf.stream2 if mode == "pass2" else None)
+    torch.cuda.synchronize()
+    return buf
+
+
+def assert_identical(got, ref, label):
+    for key in OUTPUTS:
+        x, y = getattr(got, key), getattr(ref, key)
+        if x is None or y is None:
+            continue
+        if not torch.equal(x, y):
+            diff = (x.float() - y.float()).abs().max().item()
+            raise AssertionError(f"{label}: {key} differs from the resident steps (max {diff})")
+
+
+def union_sizes(shape, sel):
+    """Per (b, g, segment): the number of distinct history blocks chosen."""
+    s = sel.cpu().numpy()
+    nqb = shape.seg_len // shape.query_block
+    out = []
+    for seg in range(shape.nseg):
+        rows = s[:, :, seg * nqb:(seg + 1) * nqb, :]
+        for b in range(rows.shape[0]):
+            for g in range(rows.shape[1]):
+                u = rows[b, g]
+                out.append(len(np.unique(u[u >= 0])))
+    return out
+
+
+def window_slots(shape):
+    nqb = shape.seg_len // shape.query_block
+    return min(nqb * shape.top_k, (shape.seq_len - shape.seg_len) // shape.hist_block)
+
+
+@pytest.mark.parametrize("shape,mode", [
+    (shp(), "planted"),                                               # several tiles, G=4
+    (shp(query_block=16, hist_block=16, top_k=5), "planted"),         # 16-row blocks
+    (shp(head_dim=64, query_block=64, hist_block=64, seg_len=128, top_k=2), "planted"),  # D=64
+    (shp(batch=2, seq_len=256, top_k=2), "planted"),                  # batch 2
+    (shp(seq_len=128, seg_len=128), "planted"),                       # one segment, no window slots
+    (shp(top_k=40), "planted"),                                       # k covers all history
+    (shp(seq_len=480, seg_len=160, top_k=4), "planted"),              # odd number of key tiles
+    (shp(seq_len=2048, seg_len=512, top_k=8, n_q_heads=8, n_kv_heads=2), "diverse"),  # unions near C
+    (shp(seq_len=1024, seg_len=256, hist_block=16, query_block=64, top_k=24), "diverse"),
+])
+def test_tier_equals_resident_steps(shape, mode):
+    inp = make_inputs(shape, seed=5, mode=mode)
+    dev = upload(inp, shape)
+    ref = resident_steps(shape, dev, bwd=True)
+    kv = host_kv(dev)
+    for run in ("steps", "pass1", "pass2"):
+        got = host_run(shape, dev, True, run, kv)
+        assert_identical(got, ref, f"{shape.name}/{run}")
+    sizes = union_sizes(shape, ref.sel)
+    C = window_slots(shape)
+    assert max(sizes) <= C
+    if mode == "diverse":
+        # the query blocks chose different blocks: many window slots in use
+        assert max(sizes) > shape.top_k
+
+
+def test_tier_forward_only():
+    shape = shp(seq_len=384)
+    inp = make_inputs(shape, seed=2, with_do=False)
+    dev = upload(inp, shape)
+    ref = resident_steps(shape, dev, bwd=False)
+    for run in ("steps", "pass2"):
+        assert_identical(host_run(shape, dev, False, run), ref, f"fwd/{run}")
+    out = orc.run(inp, shape, bwd=False)
+    np.testing.assert_array_equal(to_np(ref.sel), out["sel"])
+    assert_close("o", to_np(ref.o), out["o"], TOL["bf16"])
+
+
+@pytest.mark.parametrize("mode", ["planted", "diverse"])
+def test_tier_against_oracle(mode):
+    """The 2K workload through the host-tier pass against the oracle.  Planted
+    inputs: the whole pass.  Diverse inputs (one direction per query block,
+    so the window holds many more blocks): the directions cannot all be
+    orthogonal, so the selection is compared where the oracle's k-th gap is
+    clear, and the attention against the oracle run on the GPU's selection."""
+    shape = WORKLOADS["qwen3_2k"]
+    inp = make_inputs(shape, seed=0, mode=mode)
+    dev = upload(inp, shape)
+    got = host_run(shape, dev, True, "pass2")
+    if mode == "planted":
+        ref = orc.run(inp, shape, bwd=True)
+        np.testing.assert_array_equal(to_np(got.sel), ref["sel"])
+        for key in ("o", "lse", "dq", "dk", "dv"):
+            assert_close(key, to_np(getattr(got, key)), ref[key], TOL["bf16"])
+        return
+    L, nqb = shape.seg_len, shape.seg_len // shape.query_block
+    sel_gpu = to_np(got.sel)
+    for s in range(shape.nseg):
+        rows = sel_gpu[:, :, s * nqb:(s + 1) * nqb]
+        if orc.selection_gap(inp["q"], inp["k"], shape, s) >= 1e-3:
+            np.testing.assert_array_equal(rows, orc.select_segment(inp["q"], inp["k"], shape, s))
+        O, LSE = orc.segment_forward(inp["q"], inp["k"], inp["v"], rows, shape, s)
+        dQ, dK, dV = orc.segment_backward(inp["q"], inp["k"], inp["v"], inp["do"], rows, shape,
+                                          s, O, LSE)
+        sl = slice(s * L, (s + 1) * L)
+        tol = TOL["bf16"]
+        assert_close(f"o seg {s}", to_np(got.o)[:, :, sl], O, tol)
+        assert_close(f"lse seg {s}", to_np(got.lse)[:, :, sl], LSE, tol)
+        assert_close(f"dq seg {s}", to_np(got.dq)[:, :, sl], dQ, tol)
+        assert_close(f"dk seg {s}", to_np(got.dk)[:, :, sl], dK, tol)
+        assert_close(f"dv seg {s}", to_np(got.dv)[:, :, sl], dV, tol)
+    assert max(union_sizes(shape, got.sel)) > shape.top_k
+
+
+def test_tier_rejects_memory_that_is_not_pinned_host_memory():
+    shape = shp(seq_len=256)
+    inp = make_inputs(shape, seed=1)
+    dev = upload(inp, shape)
+    cfg = hga.Config.from_shape(shape)
+    buf = hga.Buffers(cfg, bwd=True)
+    ws = hga.host_workspace(cfg, hga.HGA_OP_STEP_HOST)
+    pageable = dev["k"].cpu()
+    with pytest.raises(ValueError, match="pinned"):
+        hga.segment_step_host(cfg, 1, dev["q"], pageable, pageable, buf.summ, buf.sel, buf.o,
+                              buf.lse, dev["do"], buf.dq, buf.dk, buf.dv, ws=ws)
+    L = hga.lib()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    for bad in (pageable, dev["k"]):  # pageable host memory, device memory
+        rc = L.hga_segment_step_host(
+            ctypes.byref(cfg), 1, hga.HGA_STEP_BWD, P(dev["q"]), P(bad), P(bad), P(dev["do"]),
+            P(buf.summ), P(buf.sel), P(buf.o), P(buf.lse), P(buf.dq), P(buf.dk), P(buf.dv),
+            P(ws), ws.numel(), None)
+        assert rc == hga.HGA_ERR_ARG and "pinned host memory" in hga.last_error()
+    torch.cuda.synchronize()
+    # nothing was enqueued: a valid call afterwards still works
+    kh, vh = host_kv(dev)
+    hga.segment_step_host(cfg, 0, dev["q"], kh, vh, buf.summ, buf.sel, buf.o, buf.lse,
+                          dev["do"], buf.dq, buf.dk, buf.dv, ws=ws)
+    torch.cuda.synchronize()
+
+
+def test_tier_full_size_16k():
+    """The 16K training workload: the host-tier pass (fetches on a second
+    stream) equals the resident steps bit for bit."""
+    shape = WORKLOADS["train_16k"]
+    inp = make_inputs(shape, seed=0)
+    dev = upload(inp, shape)
+    ref = resident_steps(shape, dev, bwd=True)
+    got = host_run(shape, dev, True, "pass2")
+    assert_identical(got, ref, "train_16k/pass2")
