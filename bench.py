@@ -55,6 +55,8 @@ def parse():
                          "stream, as in the kernel-timing loops; used for kernel traces)")
     ap.add_argument("--no-exact", action="store_true",
                     help="skip the exact-gradient (history not detached) pass timing")
+    ap.add_argument("--no-host-tier", action="store_true",
+                    help="skip the pass with K and V in pinned host memory")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size "
                          "reference for HBM byte counters)")
@@ -66,7 +68,8 @@ def parse():
 
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_CLASS_OF = {"fwd_pass_kernel": "fwd", "dq_pass_kernel": "bwd_dq",
+KERNEL_CLASS_OF = {"tier_fetch_kernel": "tier_fetch", "tier_plan_kernel": "tier_plan",
+                   "fwd_pass_kernel": "fwd", "dq_pass_kernel": "bwd_dq",
                    "dkdv_pass_kernel": "bwd_dkdv", "fwd_bf16_kernel": "fwd",
                    "dq_bf16_kernel": "bwd_dq", "dkdv_bf16_kernel": "bwd_dkdv",
                    "delta_kernel": "bwd_pre", "select_kernel": "select",
@@ -226,6 +229,99 @@ def exact_bench(shape, dev, steps, warmup):
             "steps_ms_per_step": round(ms_steps, 4),
             "note": "history not detached: later segments' queries also give dK/dV to the "
                     "blocks they selected (hga_segment_pass_exact)"}
+
+
+PCIE5_X16_GBPS = 64.0  # host link of the MI355X: PCIe 5.0 x16, per direction
+
+
+def host_tier_bench(shape, dev, steps, warmup):
+    """The pass with K and V in pinned host memory (hga_segment_pass_host):
+    per segment the summaries of the previous segment's blocks are read from
+    the host, the selection is made, the union of the chosen blocks and the
+    segment's own rows are fetched into an HBM window, and the attention
+    reads the window; the next segment's fetch runs on a second stream
+    meanwhile.  The fetch kernel reads host memory over the PCIe link: its
+    roofline is the link's bandwidth, not HBM."""
+    import numpy as np
+    import torch
+    import sparse_long_context_query_amd as hga
+    cfg = hga.Config.from_shape(shape)
+    buf = hga.Buffers(cfg, bwd=True)
+    kh, vh = dev["k"].cpu().pin_memory(), dev["v"].cpu().pin_memory()
+    ws2 = hga.host_workspace(cfg, hga.HGA_OP_PASS_HOST)
+    ws1 = hga.host_workspace(cfg, hga.HGA_OP_STEP_HOST)
+
+    def run_pass(stream2):
+        hga.segment_pass_host(cfg, dev["q"], kh, vh, buf.summ, buf.sel, buf.o, buf.lse,
+                              dev["do"], buf.dq, buf.dk, buf.dv, ws=ws2, stream2=stream2)
+
+    def run_steps():
+        for seg in range(shape.nseg):
+            hga.segment_step_host(cfg, seg, dev["q"], kh, vh, buf.summ, buf.sel, buf.o, buf.lse,
+                                  dev["do"], buf.dq, buf.dk, buf.dv, ws=ws1)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        for _ in range(steps):
+            fn()
+        en.record()
+        torch.cuda.synchronize()
+        return st.elapsed_time(en) / steps
+
+    ms2 = timed(lambda: run_pass(buf.stream2))
+    ms1 = timed(lambda: run_pass(None))
+    ms_steps = timed(run_steps)
+    torch.cuda.synchronize()
+    hga.profile_begin()
+    for _ in range(steps):
+        run_pass(None)
+    prof = {c: (v[0] / steps, v[1] // steps) for c, v in hga.profile_end().items()}
+    # bytes the fetches move per pass: each segment's union of chosen blocks
+    # and its own rows, K and V (the summaries are taken from the window)
+    sel = buf.sel.cpu().numpy()
+    nqb = shape.seg_len // shape.query_block
+    rows = 0
+    for seg in range(shape.nseg):
+        part = sel[:, :, seg * nqb:(seg + 1) * nqb, :]
+        for b in range(part.shape[0]):
+            for g in range(part.shape[1]):
+                u = part[b, g]
+                rows += len(np.unique(u[u >= 0])) * shape.hist_block + shape.seg_len
+    esz = 2
+    fetch_bytes = rows * shape.head_dim * esz * 2
+    fetch_ms, fetch_n = prof["tier_fetch"]
+    achieved = fetch_bytes / (fetch_ms * 1e-3) / 1e9
+    # a plain host-to-device copy of the whole K (copy engine) for comparison
+    dst = torch.empty_like(dev["k"])
+    for _ in range(2):
+        dst.copy_(kh, non_blocking=True)
+    torch.cuda.synchronize()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    for _ in range(5):
+        dst.copy_(kh, non_blocking=True)
+    en.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * kh.numel() * esz / (st.elapsed_time(en) * 1e-3) / 1e9
+    kv_bytes = 2 * kh.numel() * esz
+    return {"ms_per_step": round(ms2, 4),
+            "tokens_per_s": round(shape.batch * shape.seq_len / (ms2 * 1e-3), 1),
+            "one_stream_ms_per_step": round(ms1, 4),
+            "steps_ms_per_step": round(ms_steps, 4),
+            "kernels_ms_per_pass": {c: round(v[0], 4) for c, v in prof.items() if v[1]},
+            "fetch": {"bound": "pcie", "bytes_per_pass": fetch_bytes,
+                      "kernel_ms_per_pass": round(fetch_ms, 4), "launches": fetch_n,
+                      "achieved": round(achieved, 1), "peak": PCIE5_X16_GBPS, "unit": "GB/s",
+                      "frac": round(achieved / PCIE5_X16_GBPS, 4),
+                      "h2d_copy_engine_GBps": round(copy_gbps, 1)},
+            "hbm_workspace_bytes": int(ws2.numel()),
+            "kv_bytes_in_host_memory": kv_bytes,
+            "note": "K and V in pinned host memory; per segment only the chosen blocks "
+                    "and the segment's rows are fetched into HBM (hga_segment_pass_host)"}
 
 
 def decode_bench(n_steps, news=(1, 16)):
@@ -475,6 +571,9 @@ def main():
     if not args.no_exact and bwd and shape.dtype == "bf16":
         log("[bench] exact-gradient pass")
         extras["exact_gradient"] = exact_bench(shape, dev, max(3, args.steps // 4), 1)
+    if not args.no_host_tier and bwd and shape.dtype == "bf16":
+        log("[bench] host-RAM history tier pass")
+        extras["host_tier"] = host_tier_bench(shape, dev, max(3, args.steps // 4), 2)
     if not args.no_decode:
         log("[bench] decode steps at 131K")
         del buf

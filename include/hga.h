@@ -270,17 +270,19 @@ int hga_segment_pass_exact(const hga_config* cfg, const void* q, const void* k, 
  *   - k_host, v_host: [B, Hkv, S, D] bf16 in pinned host memory (hipHostMalloc,
  *     or a pinned torch tensor), read by the GPU directly; rows 0 .. t0+L-1
  *     must hold the keys / values (t0 = seg*L).  Never written.
- *   - per step, on the GPU: the summaries of segment seg-1's blocks are read
- *     from the host copy (unless HGA_STEP_SUMMARIES_READY), the selection is
- *     made as in hga_segment_step, then the union of the blocks the
+ *   - per step, on the GPU: the selection is made as in hga_segment_step
+ *     (summ must hold the blocks before t0), then the union of the blocks the
  *     segment's query blocks chose (per (b, g), at most
  *     C = min((L/Bq)*k, (S-L)/Bh) blocks) and the segment's own L rows are
  *     copied from host memory into a window in ws of C*Bh + L rows per
- *     (b, g), and forward and backward read the window.  The host never
- *     waits for the selection.
+ *     (b, g); forward and backward read the window, and the summaries of
+ *     the segment's own blocks (history of the later segments; none for the
+ *     last segment) are taken from the window into summ, unless
+ *     HGA_STEP_SUMMARIES_READY.  The host never waits for the selection.
  *   - every other argument, and every result, is that of hga_segment_step:
- *     o, lse, dq, dk, dv, summ and sel equal its results bit for bit (the
- *     window keeps the chosen blocks in ascending order).
+ *     o, lse, dq, dk, dv and sel equal its results bit for bit (the window
+ *     keeps the chosen blocks in ascending order), and after the steps of
+ *     segments 0 .. S/L-1 in order so does summ.
  * HBM use per step is bounded by the window, whatever S is; the tier needs
  * host memory for K and V only.  Requirements: bf16 (else
  * HGA_ERR_UNSUPPORTED); k_host and v_host pinned host memory (else

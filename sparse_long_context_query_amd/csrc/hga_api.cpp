@@ -450,32 +450,53 @@ int check_tier(const hga::Prob& p) {
   return HGA_OK;
 }
 
-// The selection of segment seg, then the fetch of what it chose, on st.
-int tier_fetch_step(const hga::Prob& p, int32_t seg, bool summarize, const void* q,
-                    const void* kh, const void* vh, float* summ, int32_t* sel, const TierWs& t,
-                    int w, hipStream_t st) {
-  hipError_t e;
-  if (seg > 0 && summarize) {
-    // blocks closed by segment seg-1, read from the host copy
-    e = hga::launch_summarize(p, kh, (seg - 1) * p.L / p.Bh, seg * p.L / p.Bh, summ, st);
-    if (e != hipSuccess) return hip_fail(e, "summarize launch");
-  }
-  e = hga::launch_select(p, q, summ, seg, sel, st);
+// The window's geometry for the step kernels.
+hga::Prob tier_prob(const hga::Prob& p) {
+  hga::Prob pw = p;
+  pw.kv_rows = hga::tier_rows(p);
+  pw.kv_local = hga::tier_slots(p) * p.Bh;
+  return pw;
+}
+
+// The summaries of segment seg's own blocks (history of the later segments),
+// read from window w, where the fetch put the segment's rows.  The last
+// segment's blocks are never history.
+int tier_summarize(const hga::Prob& p, int32_t seg, float* summ, const TierWs& t, int w,
+                   hipStream_t st) {
+  if (seg + 1 >= p.S / p.L) return HGA_OK;
+  const hga::Prob pw = tier_prob(p);
+  const hipError_t e = hga::launch_summarize(pw, t.kw[w], seg * p.L / p.Bh,
+                                             (seg + 1) * p.L / p.Bh, summ, st,
+                                             pw.kv_local - seg * p.L);
+  return e == hipSuccess ? HGA_OK : hip_fail(e, "summarize launch");
+}
+
+// The selection of segment seg and the plan of window w's fetch, on st.
+int tier_plan_step(const hga::Prob& p, int32_t seg, const void* q, const float* summ,
+                   int32_t* sel, const TierWs& t, int w, hipStream_t st) {
+  hipError_t e = hga::launch_select(p, q, summ, seg, sel, st);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   e = hga::launch_tier_plan(p, sel, seg, t.wsel, t.list[w], t.count[w], st);
   if (e != hipSuccess) return hip_fail(e, "tier plan launch");
-  e = hga::launch_tier_fetch(p, kh, vh, t.list[w], t.count[w], seg, t.kw[w], t.vw[w], st);
-  if (e != hipSuccess) return hip_fail(e, "tier fetch launch");
   return HGA_OK;
+}
+
+// The selection of segment seg, then the fetch of what it chose, on st.
+int tier_fetch_step(const hga::Prob& p, int32_t seg, const void* q, const void* kh,
+                    const void* vh, const float* summ, int32_t* sel, const TierWs& t, int w,
+                    hipStream_t st) {
+  int rc = tier_plan_step(p, seg, q, summ, sel, t, w, st);
+  if (rc) return rc;
+  const hipError_t e =
+      hga::launch_tier_fetch(p, kh, vh, t.list[w], t.count[w], seg, t.kw[w], t.vw[w], st);
+  return e == hipSuccess ? HGA_OK : hip_fail(e, "tier fetch launch");
 }
 
 // The attention of segment seg over window w, on st.
 int tier_attn_step(const hga::Prob& p, int32_t seg, bool bwd, const void* q, const void* dO,
                    void* o, float* lse, void* dq, void* dk, void* dv, const TierWs& t, int w,
                    hipStream_t st) {
-  hga::Prob pw = p;
-  pw.kv_rows = hga::tier_rows(p);
-  pw.kv_local = hga::tier_slots(p) * p.Bh;
+  const hga::Prob pw = tier_prob(p);
   hipError_t e = hga::launch_fwd(pw, q, t.kw[w], t.vw[w], t.wsel, seg, o, lse, st,
                                  bwd ? dO : nullptr, bwd ? (float*)t.bws : nullptr);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
@@ -543,8 +564,8 @@ int hga_segment_step_host(const hga_config* cfg, int32_t seg, int32_t flags, con
   if ((rc = host_pointer(v_host, "v_host", &vh))) return rc;
   const TierWs t = tier_carve(p, ws, 1);
   hipStream_t st = (hipStream_t)stream;
-  if ((rc = tier_fetch_step(p, seg, !(flags & HGA_STEP_SUMMARIES_READY), q, kh, vh, summ, sel, t,
-                            0, st)))
+  if ((rc = tier_fetch_step(p, seg, q, kh, vh, summ, sel, t, 0, st))) return rc;
+  if (!(flags & HGA_STEP_SUMMARIES_READY) && (rc = tier_summarize(p, seg, summ, t, 0, st)))
     return rc;
   if ((rc = tier_attn_step(p, seg, (flags & HGA_STEP_BWD) != 0, q, dO, o, lse, dq, dk, dv, t, 0,
                            st)))
@@ -586,13 +607,23 @@ int hga_segment_pass_host(const hga_config* cfg, int32_t flags, const void* q,
     if ((e = hipEventRecord(ev[4], sa)) != hipSuccess) return hip_fail(e, "event record");
     if ((e = hipStreamWaitEvent(sf, ev[4], 0)) != hipSuccess) return hip_fail(e, "stream wait");
   }
+  // On sf, per segment s: fetch(s) into window s&1, summaries of its
+  // blocks, then the selection and plan of s+1 (they need those summaries);
+  // only then is the attention of s released on sa, so that the small
+  // selection kernels do not share the CUs with it.  fetch(s+1) then runs
+  // beside attention(s); it waits for attention(s-1), the last reader of its
+  // window.
   const int nseg = p.S / p.L;
+  if ((rc = tier_plan_step(p, 0, q, summ, sel, t, 0, sf))) return rc;
   for (int seg = 0; seg < nseg; ++seg) {
     const int w = seg & 1;
-    // window w was last read by the attention of segment seg-2
     if (two && seg >= 2 && (e = hipStreamWaitEvent(sf, ev[2 + w], 0)) != hipSuccess)
       return hip_fail(e, "stream wait");
-    if ((rc = tier_fetch_step(p, seg, true, q, kh, vh, summ, sel, t, w, sf))) return rc;
+    e = hga::launch_tier_fetch(p, kh, vh, t.list[w], t.count[w], seg, t.kw[w], t.vw[w], sf);
+    if (e != hipSuccess) return hip_fail(e, "tier fetch launch");
+    if ((rc = tier_summarize(p, seg, summ, t, w, sf))) return rc;
+    if (seg + 1 < nseg && (rc = tier_plan_step(p, seg + 1, q, summ, sel, t, w ^ 1, sf)))
+      return rc;
     if (two) {
       if ((e = hipEventRecord(ev[w], sf)) != hipSuccess) return hip_fail(e, "event record");
       if ((e = hipStreamWaitEvent(sa, ev[w], 0)) != hipSuccess) return hip_fail(e, "stream wait");

@@ -38,8 +38,10 @@ constexpr int kMaxTopK = 1024;
 constexpr int kHistMaxEntries = 8192;  // (L / Bq) * k limit of the exact backward
 
 // ---- launchers (host side; return hipSuccess or the launch error) --------
+// K rows per (b, g): p.kv_rows; block i starts at row i * Bh + row_shift
+// (full-sequence storage: row_shift 0).
 hipError_t launch_summarize(const Prob& p, const void* k, int blk_begin,
-                            int blk_end, float* summ, hipStream_t st);
+                            int blk_end, float* summ, hipStream_t st, int row_shift = 0);
 hipError_t launch_select(const Prob& p, const void* q, const float* summ,
                          int seg, int32_t* sel, hipStream_t st);
 // Selection of segments seg0 .. seg0+nseg-1 in one launch.

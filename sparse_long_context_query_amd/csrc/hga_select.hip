@@ -42,7 +42,7 @@ struct SelGeom {
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void summarize_kernel(
     const T* __restrict__ k, float* __restrict__ summ, int S, int Bh, int Hkv,
-    int nblk, int blk_begin) {
+    int nblk, int blk_begin, int row_shift) {
   constexpr int E = Vec16<T>::N;
   constexpr int C = D / E;
   constexpr int R = kThreads / C;
@@ -50,7 +50,8 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
 
   const int i = blk_begin + blockIdx.x;
   const int g = blockIdx.y, b = blockIdx.z;
-  const T* base = k + ((size_t)(b * Hkv + g) * S + (size_t)i * Bh) * D;
+  // rows per (b, g): S; block i's first row: i * Bh + row_shift
+  const T* base = k + ((size_t)(b * Hkv + g) * S + (size_t)(i * Bh + row_shift)) * D;
   const int c = threadIdx.x % C, r = threadIdx.x / C;
 
   float acc[E];
@@ -420,10 +421,10 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 
 template <typename T, int D>
 hipError_t summarize_t(const Prob& p, const void* k, int b0, int b1, float* summ,
-                       hipStream_t st) {
+                       hipStream_t st, int row_shift) {
   dim3 grid(b1 - b0, p.Hkv, p.B);
   HGA_LAUNCH(HGA_K_SUMMARIZE, (summarize_kernel<T, D>), grid, dim3(kThreads), 0, st,
-                     (const T*)k, summ, p.S, p.Bh, p.Hkv, p.nblk, b0);
+                     (const T*)k, summ, p.kv_rows, p.Bh, p.Hkv, p.nblk, b0, row_shift);
   return hipGetLastError();
 }
 
@@ -472,13 +473,13 @@ hipError_t select_any(const Prob& p, const void* q, const float* summ, const Sel
 }  // namespace
 
 hipError_t launch_summarize(const Prob& p, const void* k, int b0, int b1, float* summ,
-                            hipStream_t st) {
+                            hipStream_t st, int row_shift) {
   if (b1 <= b0) return hipSuccess;
   if (p.dtype == HGA_BF16)
-    return p.D == 64 ? summarize_t<__bf16, 64>(p, k, b0, b1, summ, st)
-                     : summarize_t<__bf16, 128>(p, k, b0, b1, summ, st);
-  return p.D == 64 ? summarize_t<float, 64>(p, k, b0, b1, summ, st)
-                   : summarize_t<float, 128>(p, k, b0, b1, summ, st);
+    return p.D == 64 ? summarize_t<__bf16, 64>(p, k, b0, b1, summ, st, row_shift)
+                     : summarize_t<__bf16, 128>(p, k, b0, b1, summ, st, row_shift);
+  return p.D == 64 ? summarize_t<float, 64>(p, k, b0, b1, summ, st, row_shift)
+                   : summarize_t<float, 128>(p, k, b0, b1, summ, st, row_shift);
 }
 
 hipError_t launch_select(const Prob& p, const void* q, const float* summ, int seg,

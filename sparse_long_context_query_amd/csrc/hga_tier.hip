@@ -19,14 +19,19 @@
 //          reading the host memory directly (device-mapped pinned memory).
 // Slots keep block order, so the attention kernels meet the same keys in the
 // same order as with full-sequence storage.
+#include <algorithm>
+
 #include "hga_internal.h"
 
 namespace hga {
 namespace {
 
-constexpr int kRows = 16;  // window rows one block of threads copies
+constexpr int kRows = 16;         // window rows per copy unit
+constexpr int kFetchBlocks = 32;   // blocks of the fetch grid
+constexpr int kUnits = 2;          // copy units per block in flight
 
 struct TierArgs {
+  int nbg;          // B * Hkv
   int Hkv, Bh, L, K, nqb, nqb_all, seg, C;
   int nb;           // history blocks of the segment = seg * L / Bh
   int units_hist;   // C * Bh / kRows
@@ -87,9 +92,13 @@ __global__ __launch_bounds__(256) void tier_plan_kernel(const int32_t* __restric
   if (tid == 0) count[bg] = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
 }
 
-// Block u of (b, g) copies kRows rows of K and of V: history units first
-// (slot = u * kRows / Bh; units of slots beyond the union's size do
-// nothing), then the segment's own rows.
+// Unit u of (b, g) is kRows rows of K and of V: history units first
+// (slot = u * kRows / Bh; units of slots beyond the union's size are
+// skipped), then the segment's own rows.  A small grid walks the units
+// (grid stride, kUnits per pass of the loop, all their loads issued before
+// the first store), which keeps enough requests in flight for the host
+// link while it holds only a few CUs: the attention on the other stream
+// needs every VGPR of the CUs it runs on.
 template <int D>
 __global__ __launch_bounds__(256) void tier_fetch_kernel(const __bf16* __restrict__ kh,
                                                          const __bf16* __restrict__ vh,
@@ -98,44 +107,66 @@ __global__ __launch_bounds__(256) void tier_fetch_kernel(const __bf16* __restric
                                                          __bf16* __restrict__ kw,
                                                          __bf16* __restrict__ vw, TierArgs a) {
   constexpr int CH = kRows * D * 2 / 16;  // 16-byte chunks per tensor
-  const int bg = blockIdx.x / a.units;
-  const int u = blockIdx.x % a.units;
-  int src_row, dst_row;
-  if (u < a.units_hist) {
-    const int r = u * kRows;
-    const int slot = r / a.Bh;
-    if (slot >= count[bg]) return;
-    src_row = list[(size_t)bg * a.C + slot] * a.Bh + r % a.Bh;
-    dst_row = r;
-  } else {
-    const int r = (u - a.units_hist) * kRows;
-    src_row = a.seg * a.L + r;
-    dst_row = a.C * a.Bh + r;
-  }
-  const uint4* ks = reinterpret_cast<const uint4*>(kh + ((size_t)bg * a.S + src_row) * D);
-  const uint4* vs = reinterpret_cast<const uint4*>(vh + ((size_t)bg * a.S + src_row) * D);
-  uint4* kd = reinterpret_cast<uint4*>(kw + ((size_t)bg * a.Sw + dst_row) * D);
-  uint4* vd = reinterpret_cast<uint4*>(vw + ((size_t)bg * a.Sw + dst_row) * D);
-  // every load first, then the stores: the host reads' latency is paid once
   constexpr int PER = (2 * CH + 255) / 256;
-  uint4 x[PER];
+  const int total = a.nbg * a.units;
+  for (int w0 = blockIdx.x; w0 < total; w0 += kUnits * gridDim.x) {
+    const uint4* src[kUnits][2];
+    uint4* dst[kUnits][2];
+    bool ok[kUnits];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    if (c < 2 * CH) x[i] = c < CH ? ks[c] : vs[c - CH];
-  }
+    for (int n = 0; n < kUnits; ++n) {
+      const int w = w0 + n * gridDim.x;
+      ok[n] = w < total;
+      if (!ok[n]) continue;
+      const int bg = w / a.units;
+      const int u = w % a.units;
+      int src_row, dst_row;
+      if (u < a.units_hist) {
+        const int r = u * kRows;
+        const int slot = r / a.Bh;
+        ok[n] = slot < count[bg];
+        if (!ok[n]) continue;
+        src_row = list[(size_t)bg * a.C + slot] * a.Bh + r % a.Bh;
+        dst_row = r;
+      } else {
+        const int r = (u - a.units_hist) * kRows;
+        src_row = a.seg * a.L + r;
+        dst_row = a.C * a.Bh + r;
+      }
+      src[n][0] = reinterpret_cast<const uint4*>(kh + ((size_t)bg * a.S + src_row) * D);
+      src[n][1] = reinterpret_cast<const uint4*>(vh + ((size_t)bg * a.S + src_row) * D);
+      dst[n][0] = reinterpret_cast<uint4*>(kw + ((size_t)bg * a.Sw + dst_row) * D);
+      dst[n][1] = reinterpret_cast<uint4*>(vw + ((size_t)bg * a.Sw + dst_row) * D);
+    }
+    // every load first, then the stores: the host reads' latency is paid once
+    uint4 x[kUnits][PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    if (c < 2 * CH) {
-      if (c < CH) kd[c] = x[i];
-      else vd[c - CH] = x[i];
+    for (int n = 0; n < kUnits; ++n) {
+      if (!ok[n]) continue;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        if (c < 2 * CH) x[n][i] = c < CH ? src[n][0][c] : src[n][1][c - CH];
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < kUnits; ++n) {
+      if (!ok[n]) continue;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        if (c < 2 * CH) {
+          if (c < CH) dst[n][0][c] = x[n][i];
+          else dst[n][1][c - CH] = x[n][i];
+        }
+      }
     }
   }
 }
 
 TierArgs make_tier_args(const Prob& p, int seg) {
   TierArgs a;
+  a.nbg = p.B * p.Hkv;
   a.Hkv = p.Hkv; a.Bh = p.Bh; a.L = p.L; a.K = p.K; a.nqb = p.nqb; a.nqb_all = p.nqb_all;
   a.seg = seg;
   a.C = tier_slots(p);
@@ -171,7 +202,7 @@ hipError_t launch_tier_fetch(const Prob& p, const void* k_host, const void* v_ho
                              void* vw, hipStream_t st) {
   if (p.dtype != HGA_BF16 || p.Bh % kRows || p.L % kRows) return hipErrorInvalidValue;
   const TierArgs a = make_tier_args(p, seg);
-  const dim3 grid(p.B * p.Hkv * a.units);
+  const dim3 grid(std::min(a.nbg * a.units, kFetchBlocks));
   if (p.D == 64)
     HGA_LAUNCH(HGA_K_TIER_FETCH, tier_fetch_kernel<64>, grid, dim3(256), 0, st,
                (const __bf16*)k_host, (const __bf16*)v_host, list, count, (__bf16*)kw,
