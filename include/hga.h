@@ -294,10 +294,12 @@ int hga_segment_step_host(const hga_config* cfg, int32_t seg, int32_t flags, con
                           void* ws, size_t ws_bytes, void* stream);
 
 /* The whole segmented pass with the host tier: hga_segment_step_host for
- * seg = 0 .. S/L-1, with two windows in ws so that the summaries,
- * selection and fetch of segment seg+1 run on stream2 while the attention
- * of segment seg runs on stream (stream2 NULL: everything on stream, in
- * order).  Results equal the steps' bit for bit.  When the call returns,
+ * seg = 0 .. S/L-1, with two windows in ws.  The selections, summaries and
+ * fetches run on stream2, the attention on stream: the fetch of segment
+ * seg+1 runs while the attention of segment seg does (the selection of
+ * seg+1 comes before that attention starts), and waits only for the
+ * attention of seg-1, the last reader of its window (stream2 NULL:
+ * everything on stream, in order).  Results equal the steps' bit for bit.  When the call returns,
  * everything it enqueued is ordered before later work on `stream`; both
  * streams at default priority.  flags: HGA_STEP_BWD or 0.  ws:
  * hga_workspace_size(cfg, HGA_OP_PASS_HOST) bytes.  The library keeps five
