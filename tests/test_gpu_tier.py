@@ -212,3 +212,30 @@ def test_tier_full_size_16k():
     ref = resident_steps(shape, dev, bwd=True)
     got = host_run(shape, dev, True, "pass2")
     assert_identical(got, ref, "train_16k/pass2")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_tier_inference_131k():
+    """The 131,072-token inference workload (forward only, 128 segments, 1,016
+    history blocks of 128 at the last one): K and V in host memory, an HBM
+    window of 128 blocks + one segment per KV head.  The host-tier pass equals
+    the resident steps bit for bit, and a late segment matches the oracle."""
+    shape = WORKLOADS["infer_131k"]
+    print("[tier 131k] generating inputs", flush=True)
+    inp = make_inputs(shape, seed=0)
+    dev = upload(inp, shape)
+    print("[tier 131k] resident steps", flush=True)
+    ref = resident_steps(shape, dev, bwd=False)
+    got = host_run(shape, dev, False, "pass2")
+    assert_identical(got, ref, "infer_131k/pass2")
+    assert max(union_sizes(shape, got.sel)) <= window_slots(shape) == 128
+    s, b, g = 127, 0, 6
+    print(f"[tier 131k] oracle sample seg={s} b={b} g={g}", flush=True)
+    L, nqb, G = shape.seg_len, shape.n_qblocks, shape.group
+    sel = to_np(got.sel)[:, :, s * nqb:(s + 1) * nqb]
+    np.testing.assert_array_equal(sel, orc.select_segment(inp["q"], inp["k"], shape, s))
+    O, LSE = orc.segment_forward(inp["q"], inp["k"], inp["v"], sel, shape, s, groups=[(b, g)])
+    hs = slice(g * G, (g + 1) * G)
+    assert_close("o", to_np(got.o)[b, hs, s * L:(s + 1) * L], O[b, hs], TOL["bf16"])
+    assert_close("lse", to_np(got.lse)[b, hs, s * L:(s + 1) * L], LSE[b, hs], TOL["bf16"])
