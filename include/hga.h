@@ -232,8 +232,8 @@ int hga_segment_step_exact(const hga_config* cfg, int32_t seg, const void* q, co
  * When the call returns, everything it enqueued is ordered before later work
  * on `stream`.  Both streams must be at default priority.  flags:
  * HGA_STEP_BWD or 0.  ws: hga_workspace_size(cfg, HGA_OP_PASS) bytes
- * (needed with HGA_STEP_BWD; bf16: every segment's delta rows).  The library keeps two timing-free HIP events per calling
- * thread for the f32 hand-offs. */
+ * (needed with HGA_STEP_BWD; bf16: every segment's delta rows).  The library keeps two
+ * timing-free HIP events per calling thread and device for the f32 hand-offs. */
 int hga_segment_pass(const hga_config* cfg, int32_t flags, const void* q, const void* k,
                      const void* v, const void* dO, float* summ, int32_t* sel, void* o,
                      float* lse, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
@@ -303,7 +303,7 @@ int hga_segment_step_host(const hga_config* cfg, int32_t seg, int32_t flags, con
  * everything it enqueued is ordered before later work on `stream`; both
  * streams at default priority.  flags: HGA_STEP_BWD or 0.  ws:
  * hga_workspace_size(cfg, HGA_OP_PASS_HOST) bytes.  The library keeps five
- * timing-free HIP events per calling thread for the hand-offs. */
+ * timing-free HIP events per calling thread and device for the hand-offs. */
 int hga_segment_pass_host(const hga_config* cfg, int32_t flags, const void* q,
                           const void* k_host, const void* v_host, const void* dO, float* summ,
                           int32_t* sel, void* o, float* lse, void* dq, void* dk, void* dv,

@@ -366,15 +366,30 @@ int run_step(const hga::Prob& p, int32_t seg, int32_t flags, const void* q, cons
   return HGA_OK;
 }
 
-// Two events per thread for the pass's stream hand-offs, created on first
-// use and kept (timing disabled: they only order work).
+// Stream hand-off events of the passes, per calling thread and per device
+// (an event belongs to the device that was current when it was made):
+// [0, 2) the f32 pass's, [2, 7) the host-tier pass's.  Created on first use
+// and kept; timing disabled, they only order work.
+constexpr int kMaxDevices = 64;
+constexpr int kPassEvents = 7;
+hipError_t device_events(hipEvent_t** out) {
+  thread_local hipEvent_t ev[kMaxDevices][kPassEvents] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  for (int i = 0; i < kPassEvents; ++i)
+    if (ev[dev][i] == nullptr &&
+        (e = hipEventCreateWithFlags(&ev[dev][i], hipEventDisableTiming)) != hipSuccess)
+      return e;
+  *out = ev[dev];
+  return hipSuccess;
+}
+
 hipError_t pass_events(hipEvent_t* a, hipEvent_t* b) {
-  thread_local hipEvent_t ev[2] = {nullptr, nullptr};
-  for (int i = 0; i < 2; ++i)
-    if (ev[i] == nullptr) {
-      hipError_t e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
-      if (e != hipSuccess) return e;
-    }
+  hipEvent_t* ev = nullptr;
+  const hipError_t e = device_events(&ev);
+  if (e != hipSuccess) return e;
   *a = ev[0];
   *b = ev[1];
   return hipSuccess;
@@ -509,15 +524,12 @@ int tier_attn_step(const hga::Prob& p, int32_t seg, bool bwd, const void* q, con
 }
 
 // Events for the host-tier pass: [0, 2) fetch of window w done, [2, 4)
-// attention over window w done, [4] inputs ready (created on first use).
+// attention over window w done, [4] inputs ready.
 hipError_t tier_events(hipEvent_t** out) {
-  thread_local hipEvent_t ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
-  for (int i = 0; i < 5; ++i)
-    if (ev[i] == nullptr) {
-      hipError_t e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
-      if (e != hipSuccess) return e;
-    }
-  *out = ev;
+  hipEvent_t* ev = nullptr;
+  const hipError_t e = device_events(&ev);
+  if (e != hipSuccess) return e;
+  *out = ev + 2;
   return hipSuccess;
 }
 
