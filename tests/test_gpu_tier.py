@@ -216,6 +216,25 @@ def test_tier_full_size_16k():
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
+def test_tier_full_size_batch4_32k():
+    """Four 32K sequences, segments of 2,048, blocks of 128, k = 16: the
+    window holds up to 240 blocks per (sequence, KV head), as many as the
+    history can have.  Host-tier pass and steps equal the resident steps bit
+    for bit."""
+    shape = WORKLOADS["batch4_32k"]
+    print("[tier batch4_32k] generating inputs", flush=True)
+    inp = make_inputs(shape, seed=0)
+    dev = upload(inp, shape)
+    del inp
+    ref = resident_steps(shape, dev, bwd=True)
+    kv = host_kv(dev)
+    for run in ("pass2", "steps"):
+        assert_identical(host_run(shape, dev, True, run, kv), ref, f"batch4_32k/{run}")
+    assert window_slots(shape) == 240
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_tier_inference_131k():
     """The 131,072-token inference workload (forward only, 128 segments, 1,016
     history blocks of 128 at the last one): K and V in host memory, an HBM
