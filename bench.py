@@ -325,6 +325,78 @@ def host_tier_bench(shape, dev, steps, warmup):
                     "and the segment's rows are fetched into HBM (hga_segment_pass_host)"}
 
 
+def host_tier_131k_bench(steps):
+    """The 131,072-token inference workload, forward only, with K and V in
+    pinned host memory (hga_segment_pass_host, fetches on a second stream)
+    against the resident pass (hga_segment_pass) on the same inputs.  Inputs
+    are N(0,1) drawn on the GPU with no planted directions, so the 8 query
+    blocks of a segment mostly choose different blocks and the window is
+    near its 128-block capacity: the tier's heaviest case."""
+    import numpy as np
+    import torch
+    import sparse_long_context_query_amd as hga
+    from synth import WORKLOADS
+    shape = WORKLOADS["infer_131k"]
+    cfg = hga.Config.from_shape(shape)
+    s = hga.Shapes(cfg)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    q = torch.randn(s.q, generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn(s.kv, generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn(s.kv, generator=gen, device="cuda").to(torch.bfloat16)
+    kh, vh = k.cpu().pin_memory(), v.cpu().pin_memory()
+    buf = hga.Buffers(cfg, bwd=False)
+    ws = hga.host_workspace(cfg, hga.HGA_OP_PASS_HOST)
+
+    def tier():
+        hga.segment_pass_host(cfg, q, kh, vh, buf.summ, buf.sel, buf.o, buf.lse, bwd=False,
+                              ws=ws, stream2=buf.stream2)
+
+    def resident():
+        buf.run_pass(q, k, v, None, bwd=False)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        for _ in range(steps):
+            fn()
+        en.record()
+        torch.cuda.synchronize()
+        return st.elapsed_time(en) / steps
+
+    ms_tier = timed(tier)
+    sel = buf.sel.cpu().numpy()
+    ms_res = timed(resident)
+    nqb = shape.seg_len // shape.query_block
+    rows = 0
+    unions = []
+    for seg in range(shape.nseg):
+        part = sel[:, :, seg * nqb:(seg + 1) * nqb, :]
+        for b in range(part.shape[0]):
+            for g in range(part.shape[1]):
+                u = part[b, g]
+                n = len(np.unique(u[u >= 0]))
+                unions.append(n)
+                rows += n * shape.hist_block + shape.seg_len
+    fetch_bytes = rows * shape.head_dim * 2 * 2
+    tokens = shape.batch * shape.seq_len
+    return {"workload": "infer_131k forward (K, V in pinned host memory)",
+            "data": "synthetic N(0,1) drawn on the GPU, no planted directions",
+            "ms_per_pass": round(ms_tier, 3),
+            "tokens_per_s": round(tokens / (ms_tier * 1e-3), 1),
+            "resident_ms_per_pass": round(ms_res, 3),
+            "resident_tokens_per_s": round(tokens / (ms_res * 1e-3), 1),
+            "fetch_bytes_per_pass": fetch_bytes,
+            "fetch_GBps_over_pass": round(fetch_bytes / (ms_tier * 1e-3) / 1e9, 1),
+            "mean_union_blocks": round(float(np.mean(unions)), 1),
+            "window_slots": min(nqb * shape.top_k,
+                                (shape.seq_len - shape.seg_len) // shape.hist_block),
+            "hbm_workspace_bytes": int(ws.numel()),
+            "kv_bytes_in_host_memory": 2 * kh.numel() * 2}
+
+
 def decode_bench(n_steps, news=(1, 16)):
     """Decode steps (hga_decode_step) at the 131,072-token inference shape:
     B 1, 32 query / 8 KV heads, D 128, segments of 1,024, blocks of 128,
@@ -575,6 +647,9 @@ def main():
     if not args.no_host_tier and bwd and shape.dtype == "bf16":
         log("[bench] host-RAM history tier pass")
         extras["host_tier"] = host_tier_bench(shape, dev, max(3, args.steps // 4), 2)
+        if shape.name == "train_16k":
+            log("[bench] host-RAM tier at 131K (forward)")
+            extras["host_tier_131k"] = host_tier_131k_bench(3)
     if not args.no_decode:
         log("[bench] decode steps at 131K")
         del buf
