@@ -55,6 +55,8 @@ def parse():
                          "stream, as in the kernel-timing loops; used for kernel traces)")
     ap.add_argument("--no-exact", action="store_true",
                     help="skip the exact-gradient (history not detached) pass timing")
+    ap.add_argument("--no-hbm", action="store_true",
+                    help="skip the summaries-at-131K and standalone-gather measurements")
     ap.add_argument("--no-host-tier", action="store_true",
                     help="skip the pass with K and V in pinned host memory")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -397,6 +399,67 @@ def host_tier_131k_bench(steps):
             "kv_bytes_in_host_memory": 2 * kh.numel() * 2}
 
 
+def hbm_kernels_bench(shape, dev, buf, steps):
+    """The HBM-bound rows on their own, against the 8 TB/s HBM peak (launch
+    times stamped by the kernels' own dispatches):
+      - a1, summaries of every block of the 131K workload's K (256 MiB);
+      - a4, the standalone gather of the last 16K segment's chosen blocks
+        (K and V read and written once), on the headline pass's selection."""
+    import torch
+    import sparse_long_context_query_amd as hga
+    from synth import WORKLOADS
+    out = {}
+    big = WORKLOADS["infer_131k"]
+    bcfg = hga.Config.from_shape(big)
+    bs = hga.Shapes(bcfg)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1)
+    kb = torch.randn(bs.kv, generator=gen, device="cuda").to(torch.bfloat16)
+    summ = torch.zeros(bs.summ, dtype=torch.float32, device="cuda")
+    nblk = big.seq_len // big.hist_block
+
+    def stamped(cls, fn):
+        fn()
+        torch.cuda.synchronize()
+        hga.profile_begin([cls])
+        for _ in range(steps):
+            fn()
+        prof = hga.profile_end()
+        ms, n = prof[cls]
+        return ms / n
+
+    ms = stamped("summarize", lambda: hga.summarize(bcfg, kb, 0, nblk, summ))
+    nbytes = kb.numel() * 2 + summ.numel() * 4
+    out["summarize_131k"] = {"bytes": nbytes, "us_per_launch": round(ms * 1e3, 2),
+                             "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del kb, summ
+    cfg = hga.Config.from_shape(shape)
+    s = hga.Shapes(cfg)
+    seg = shape.nseg - 1
+    ko = torch.empty(s.gather, dtype=s.dt, device="cuda")
+    vo = torch.empty(s.gather, dtype=s.dt, device="cuda")
+    ms = stamped("gather", lambda: hga.gather(cfg, dev["k"], dev["v"], buf.sel, seg, ko, vo))
+    # HBM bytes at the least: each distinct chosen block's K and V read once
+    # (query blocks that chose the same block re-read it from the caches),
+    # and everything written; the per-query-block count reads every copy
+    import numpy as np
+    nqb = shape.seg_len // shape.query_block
+    rows = buf.sel[:, :, seg * nqb:(seg + 1) * nqb].cpu().numpy()
+    distinct = sum(len(np.unique(r[r >= 0])) for r in rows.reshape(-1, nqb * shape.top_k))
+    written = 2 * ko.numel() * ko.element_size()
+    nbytes = distinct * shape.hist_block * shape.head_dim * 2 * 2 + written
+    out["gather_16k_last_segment"] = {"bytes": nbytes, "per_query_block_bytes": 2 * written,
+                                      "distinct_blocks": distinct,
+                                      "us_per_launch": round(ms * 1e3, 2),
+                                      "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                                    4)}
+    return out
+
+
 def decode_bench(n_steps, news=(1, 16)):
     """Decode steps (hga_decode_step) at the 131,072-token inference shape:
     B 1, 32 query / 8 KV heads, D 128, segments of 1,024, blocks of 128,
@@ -614,6 +677,9 @@ def main():
     extras["pass_tflops_algorithmic"] = round(pass_tf, 1)
     extras["pass_frac_peak"] = round(pass_tf / PEAK_BF16_TFLOPS, 4)
 
+    if not args.no_hbm and shape.name == "train_16k":
+        log("[bench] HBM-bound rows (summaries at 131K, standalone gather)")
+        extras["hbm_kernels"] = hbm_kernels_bench(shape, dev, buf, args.steps)
     if not args.no_dense_self:
         dshape = shape.replace(seg_len=shape.seq_len, top_k=1)
         dcfg = hga.Config.from_shape(dshape)
