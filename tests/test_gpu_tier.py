@@ -258,3 +258,32 @@ def test_tier_inference_131k():
     hs = slice(g * G, (g + 1) * G)
     assert_close("o", to_np(got.o)[b, hs, s * L:(s + 1) * L], O[b, hs], TOL["bf16"])
     assert_close("lse", to_np(got.lse)[b, hs, s * L:(s + 1) * L], LSE[b, hs], TOL["bf16"])
+
+
+def test_tier_interior_pointers_and_summaries_ready():
+    """K and V as slices of larger pinned buffers (their addresses lie inside
+    the allocations), and steps with HGA_STEP_SUMMARIES_READY on summaries
+    made beforehand: the results are still the resident steps'."""
+    shape = shp(seq_len=384, top_k=2)
+    inp = make_inputs(shape, seed=3)
+    dev = upload(inp, shape)
+    ref = resident_steps(shape, dev, bwd=True)
+    cfg = hga.Config.from_shape(shape)
+    big_k = torch.zeros((3,) + tuple(dev["k"].shape), dtype=dev["k"].dtype).pin_memory()
+    big_v = torch.zeros((3,) + tuple(dev["v"].shape), dtype=dev["v"].dtype).pin_memory()
+    big_k[2].copy_(dev["k"].cpu())
+    big_v[1].copy_(dev["v"].cpu())
+    kh, vh = big_k[2], big_v[1]
+    assert kh.is_contiguous() and kh.data_ptr() != big_k.data_ptr()
+    got = host_run(shape, dev, True, "pass2", kv=(kh, vh))
+    assert_identical(got, ref, "interior pointers/pass2")
+    # steps that skip their summaries: summ already complete
+    buf = hga.Buffers(cfg, bwd=True)
+    hga.summarize(cfg, dev["k"], 0, shape.seq_len // shape.hist_block, buf.summ)
+    ws = hga.host_workspace(cfg, hga.HGA_OP_STEP_HOST)
+    for s in range(shape.nseg):
+        hga.segment_step_host(cfg, s, dev["q"], kh, vh, buf.summ, buf.sel, buf.o, buf.lse,
+                              dev["do"], buf.dq, buf.dk, buf.dv, ws=ws, summaries_ready=True)
+    torch.cuda.synchronize()
+    for key in ("sel", "o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(getattr(buf, key), getattr(ref, key)), key
