@@ -3,10 +3,14 @@
 // The keys and values of the whole sequence live in pinned host memory;
 // per segment only what its attention reads is brought into HBM: the
 // history blocks its query blocks selected and the segment's own rows.
-// This is the memory mechanism of the pages (history kept off the GPU, the
-// active segment on it), applied per step with the resident block summaries
-// deciding what to move ([JA] / [FR], overview and analysis sections, on
-// offloading the history and loading only the targeted blocks).
+// This is the memory mechanism of the pages, applied per step, with the
+// resident block summaries deciding what to move:
+//   [JA] 背景と概要, [FR] Contexte: the history KV lives in system RAM and
+//     only the active segment's state on the GPU;
+//   [JA] 深掘り分析, [FR] Analyse approfondie: the block summaries stay
+//     resident, and the limit moves from GPU memory to host capacity;
+//   [JA] 今後の展望, [FR] Perspectives: the GPU-host transfers are the part
+//     left to optimise.
 //
 // Two kernels, both driven by the selection on the GPU, so the host never
 // waits for it:
