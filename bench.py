@@ -55,6 +55,8 @@ def parse():
                          "stream, as in the kernel-timing loops; used for kernel traces)")
     ap.add_argument("--no-exact", action="store_true",
                     help="skip the exact-gradient (history not detached) pass timing")
+    ap.add_argument("--no-tier-131k", action="store_true",
+                    help="skip the host-tier pass at the 131K inference shape")
     ap.add_argument("--no-hbm", action="store_true",
                     help="skip the summaries-at-131K and standalone-gather measurements")
     ap.add_argument("--no-host-tier", action="store_true",
@@ -713,7 +715,7 @@ def main():
     if not args.no_host_tier and bwd and shape.dtype == "bf16":
         log("[bench] host-RAM history tier pass")
         extras["host_tier"] = host_tier_bench(shape, dev, max(3, args.steps // 4), 2)
-        if shape.name == "train_16k":
+        if shape.name == "train_16k" and not args.no_tier_131k:
             log("[bench] host-RAM tier at 131K (forward)")
             extras["host_tier_131k"] = host_tier_131k_bench(3)
     if not args.no_decode:
