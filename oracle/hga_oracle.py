@@ -27,9 +27,10 @@ What the method computes (the pages give prose only, no formula):
     history tokens instead of the full history, together with the active
     segment ([JA] 背景と概要; [FR] Contexte: targeted loading of a bounded
     set of relevant history tokens per query block).
-The summary and score rule is fixed by the benchmark spec, not the pages:
-summary = mean of the block's keys per KV head, score = dot product with the
-query block's mean query, top-k ties go to the lower block index.
+The pages name resident block summaries and a bounded top-k set but define
+neither; the plainest reading is taken and fixed here: summary = mean of the
+block's keys per KV head, score = dot product with the query block's mean
+query, top-k ties go to the lower block index.
 
 Readings where the pages are silent:
   * one selection per (sequence, KV head, query block); the query mean
@@ -66,7 +67,7 @@ def softmax_scale(head_dim: int, scale: Optional[float] = None) -> float:
 
 
 # --------------------------------------------------------------------------
-# a1: resident block summaries ([JA] 深掘り分析; rule fixed by the task)
+# a1: resident block summaries ([JA] 深掘り分析; the mean-key reading above)
 # --------------------------------------------------------------------------
 def block_summaries(k: np.ndarray, hist_block: int) -> np.ndarray:
     """Mean key of every whole block: [B,Hkv,S,D] -> [B,Hkv,S//Bh,D]."""
@@ -92,7 +93,7 @@ def query_means(q: np.ndarray, n_kv_heads: int, seg_start: int, seg_len: int,
 
 
 # --------------------------------------------------------------------------
-# a3: score + top-k ([JA] 背景と概要, [FR] Contexte; tie rule from the task)
+# a3: score + top-k ([JA] 背景と概要, [FR] Contexte; the tie reading above)
 # --------------------------------------------------------------------------
 def block_scores(qbar: np.ndarray, kbar: np.ndarray, nb: int,
                  precision: str = "f64") -> np.ndarray:
