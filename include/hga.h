@@ -34,10 +34,14 @@
  *  Every call reads and writes only the rows of the segment it is given
  *  (history K/V and summaries are read as well).  Gradients are written,
  *  not accumulated.  Work is enqueued on `stream` (a hipStream_t, NULL =
- *  the default stream); no entry point synchronizes, allocates device
- *  memory or keeps state between calls, except the optional profiling
- *  hooks at the end of this file.  Scratch space comes from `ws`, of at
- *  least hga_workspace_size() bytes.  Results are bitwise deterministic
+ *  the default stream); no entry point synchronizes or allocates device
+ *  memory.  State kept between calls: the optional profiling hooks at the
+ *  end of this file, and the timing-free HIP events that hga_segment_pass
+ *  (f32) and hga_segment_pass_host use to hand work between their two
+ *  streams -- created on a calling thread's first such call on a device,
+ *  kept for that thread and device and reused by its later calls, never
+ *  freed.  Every other entry point keeps nothing.  Scratch space comes from
+ *  `ws`, of at least hga_workspace_size() bytes.  Results are bitwise deterministic
  *  (no floating-point atomics).
  *
  *  Errors: every entry point returns HGA_OK (0) or a negative code.  The

@@ -28,7 +28,10 @@ What the method computes (the pages give prose only, no formula):
     segment ([JA] 背景と概要; [FR] Contexte: targeted loading of a bounded
     set of relevant history tokens per query block).
 The pages name resident block summaries and a bounded top-k set but define
-neither; the plainest reading is taken and fixed here: summary = mean of the
+neither, and say nothing of how a block is scored or how ties break.  The
+rule below is therefore not a reading of any passage: it is the
+specification this library implements, fixed outside the pages and stated
+again in the C interface's header: summary = mean of the
 block's keys per KV head, score = dot product with the query block's mean
 query, top-k ties go to the lower block index.
 
@@ -141,16 +144,20 @@ def select_segment(q, k, shape, seg: int, precision: str = "f64",
     return sel
 
 
-def selection_gap(q, k, shape, seg: int) -> float:
+def selection_gap(q, k, shape, seg: int, kbar: Optional[np.ndarray] = None) -> float:
     """Smallest score gap at the k-th boundary over the segment's query
-    blocks (inf when every history block is taken).  Scores in fp64 from the
-    dtype-rounded inputs."""
+    blocks: min over (b, g, j) of (k-th largest score) - ((k+1)-th largest
+    score), where equal scores count separately (so a tie across the
+    boundary gives 0).  inf when every history block is taken (nb <= k).
+    Scores in fp64 from the dtype-rounded inputs.  `kbar`, when given, holds
+    the summaries of at least the segment's history blocks."""
     L, Bq, Bh, kk = shape.seg_len, shape.query_block, shape.hist_block, shape.top_k
     t0 = seg * L
     nb = t0 // Bh
     if nb <= kk:
         return math.inf
-    kbar = block_summaries(k[:, :, :t0], Bh)
+    if kbar is None:
+        kbar = block_summaries(k[:, :, :t0], Bh)
     qbar = query_means(q, shape.n_kv_heads, t0, L, Bq)
     sc = block_scores(qbar, kbar, nb)
     srt = -np.sort(-sc, axis=-1)

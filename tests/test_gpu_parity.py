@@ -9,7 +9,7 @@ import pytest
 from oracle import hga_oracle as orc
 from synth import HGAShape, WORKLOADS, make_inputs
 
-from gpu_util import TOL, assert_close, run_pass, to_np, upload
+from gpu_util import TOL, assert_close, max_abs_rel, run_pass, to_np, upload
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -396,6 +396,12 @@ def test_attention_with_top_k_1024():
     nqb = shape.n_qblocks
     sel = to_np(buf.sel)[:, :, s * nqb:(s + 1) * nqb]
     assert (sel >= 0).sum(axis=-1).min() == 1024
+    # 1,408 candidates: the register radix-select path; the planted inputs
+    # keep the k-th boundary clear, so the chosen set is checked bit for bit
+    kbar = orc.block_summaries(inp["k"], shape.hist_block)
+    assert orc.selection_gap(inp["q"], inp["k"], shape, s, kbar=kbar) >= 1e-3
+    np.testing.assert_array_equal(sel, orc.select_segment(inp["q"], inp["k"], shape, s,
+                                                          kbar=kbar))
     O, LSE = orc.segment_forward(inp["q"], inp["k"], inp["v"], sel, shape, s)
     dQ, dK, dV = orc.segment_backward(inp["q"], inp["k"], inp["v"], inp["do"], sel, shape, s,
                                       O, LSE)
@@ -405,3 +411,31 @@ def test_attention_with_top_k_1024():
     assert_close("dq", to_np(buf.dq)[:, :, t0:t0 + L], dQ, tol)
     assert_close("dk", to_np(buf.dk)[:, :, t0:t0 + L], dK, tol)
     assert_close("dv", to_np(buf.dv)[:, :, t0:t0 + L], dV, tol)
+
+
+@pytest.mark.parametrize("shape,scale", [
+    (shp(), 0.05),                                                   # bf16 whole-pass kernels
+    (shp(head_dim=64, query_block=64, hist_block=64, seg_len=128, top_k=2), 0.3),
+    (shp(dtype="f32", head_dim=64, n_q_heads=4, n_kv_heads=2), 0.3),  # f32 kernels
+])
+@pytest.mark.parametrize("per_step", [False, True])
+def test_softmax_scale_non_default(shape, scale, per_step):
+    """A softmax scale other than 1/sqrt(D), through hga_segment_pass (bf16:
+    the whole-pass kernels) and hga_segment_step (the one-segment kernels),
+    against the oracle at the same scale.  The selection score is unscaled,
+    so the chosen blocks are those of the default scale; the outputs are
+    not, which shows that the scale reached the kernels."""
+    inp = make_inputs(shape, seed=7)
+    dev = upload(inp, shape)
+    cfg = hga.Config.from_shape(shape, softmax_scale=scale)
+    buf = hga.Buffers(cfg)
+    buf.run_pass(dev["q"], dev["k"], dev["v"], dev["do"], per_step=per_step)
+    torch.cuda.synchronize()
+    ref = orc.run(inp, shape, scale=scale)
+    np.testing.assert_array_equal(to_np(buf.sel), ref["sel"])
+    tol = TOL[shape.dtype]
+    for key in ("o", "lse", "dq", "dk", "dv"):
+        assert_close(key, to_np(getattr(buf, key)), ref[key], tol)
+    default = orc.run(inp, shape)
+    np.testing.assert_array_equal(default["sel"], ref["sel"])
+    assert max_abs_rel(to_np(buf.o), default["o"]) > 10 * tol

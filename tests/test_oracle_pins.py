@@ -120,15 +120,146 @@ def test_selection_recovers_planted_blocks(name):
                 assert list(sel[0, g, j]) == want, (s, g, j)
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_2k", "train_16k"])
+# ------------------------------------------------------ selection gap
+def _gap_inputs(score_rows, G=1, Bq=2, Bh=2, D=3):
+    """q, k and a shape whose block scores are exactly score_rows[j][i]:
+    block i's keys all equal (score_rows[0][i], score_rows[1][i], ...) in
+    the first len(score_rows) coordinates, and the queries of query block j
+    of the last segment are e_j (every head, every token).  Integer and
+    dyadic values only, so every mean and dot product is exact."""
+    rows = np.asarray(score_rows, dtype=np.float64)
+    nqb, nb = rows.shape
+    L = nqb * Bq
+    assert L % Bh == 0 and nqb <= D
+    nb_seg = L // Bh
+    nseg = -(-nb // nb_seg) + 1
+    S = nseg * L
+    seg = nseg - 1
+    shape = HGAShape("gap", 1, S, G, 1, D, L, Bh, Bq, 1, "f32")
+    q = np.zeros((1, G, S, D))
+    k = np.zeros((1, 1, S, D))
+    t0 = seg * L
+    for j in range(nqb):
+        q[0, :, t0 + j * Bq:t0 + (j + 1) * Bq, j] = 1.0
+    for i in range(nb):
+        k[0, 0, i * Bh:(i + 1) * Bh, :nqb] = rows[:, i]
+    # blocks between the given ones and the segment start score a large
+    # negative value, below every given score
+    for i in range(nb, t0 // Bh):
+        k[0, 0, i * Bh:(i + 1) * Bh, :nqb] = -1000.0
+    return q, k, shape, seg
+
+
+@pytest.mark.parametrize("scores,top_k,expect", [
+    # sorted: 5, 3, 3, 2.5, 1 -> k=3: 3 - 2.5; an off-by-one would read
+    # 3 - 3 = 0 (k-1 / k) or 2.5 - 1 = 1.5 (k+1 / k+2)
+    ([[3, 5, 1, 2.5, 3]], 3, 0.5),
+    ([[3, 5, 1, 2.5, 3]], 2, 0.0),            # tie of 3, 3 across the boundary
+    ([[3, 5, 1, 2.5, 3]], 1, 2.0),
+    ([[3, 5, 1, 2.5, 3]], 4, 1.5),
+    ([[4, 4, 4, 4]], 2, 0.0),                 # all tied
+    ([[-1, -2, -0.5, -4]], 2, 1.0),           # negative scores: -0.5, -1 | -2
+    ([[-1, -2, -0.5, -4]], 1, 0.5),           # -0.5 | -1
+    # two query blocks: the smaller of their gaps (row 1: 7, 6.75 | 2)
+    ([[3, 5, 1, 2.5, 3], [7, 2, 6.75, 0, 1]], 2, 0.0),
+    ([[9, 5, 1, 2.5, 3], [7, 2, 6.75, 0, 1]], 2, 2.0),   # row 0: 9, 5 | 3; row 1: 4.75
+    ([[9, 5, 1, 2.5, 3], [7, 2, 6.75, 0, 1]], 3, 0.5),   # row 0: 3 | 2.5; row 1: 2 | 1
+])
+def test_selection_gap_hand_built(scores, top_k, expect):
+    """selection_gap on block scores fixed by construction (exact values):
+    the gap between the k-th and (k+1)-th largest score, minimum over the
+    segment's query blocks, 0 for a tie across the boundary."""
+    q, k, shape, seg = _gap_inputs(scores, G=2)
+    nb = len(scores[0])
+    shape = shape.replace(top_k=top_k)
+    # the padding blocks (score -1000) sit below every given score, so the
+    # gap is decided by the given ones whenever k < nb
+    assert top_k < nb
+    assert orc.selection_gap(q, k, shape, seg) == expect
+
+
+def test_selection_gap_inf_when_all_taken():
+    """nb <= k: every history block is taken, there is no boundary."""
+    q, k, shape, seg = _gap_inputs([[3, 5, 1, 2.5]])
+    nb = shape.n_hist_blocks(seg)
+    assert orc.selection_gap(q, k, shape.replace(top_k=nb), seg) == math.inf
+    assert orc.selection_gap(q, k, shape.replace(top_k=nb + 5), seg) == math.inf
+    assert orc.selection_gap(q, k, shape.replace(top_k=nb - 1), seg) < math.inf
+    assert orc.selection_gap(q, k, shape.replace(top_k=1), 0) == math.inf
+
+
+def _loop_gap(q, k, shape, seg):
+    """The k-th boundary gap written with explicit loops: block means, the
+    group-and-token mean query, every score, then a selection sort of the
+    scores (largest first) and the difference of places k and k+1."""
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    L, Bh, Bq, kk = shape.seg_len, shape.hist_block, shape.query_block, shape.top_k
+    t0 = seg * L
+    nb = t0 // Bh
+    if nb <= kk:
+        return math.inf
+    best = math.inf
+    for b in range(B):
+        for g in range(Hkv):
+            kbar = []
+            for i in range(nb):
+                m = [0.0] * D
+                for t in range(i * Bh, (i + 1) * Bh):
+                    for d in range(D):
+                        m[d] += float(k[b, g, t, d])
+                kbar.append([x / Bh for x in m])
+            for j in range(L // Bq):
+                qb = [0.0] * D
+                for h in range(g * G, (g + 1) * G):
+                    for t in range(t0 + j * Bq, t0 + (j + 1) * Bq):
+                        for d in range(D):
+                            qb[d] += float(q[b, h, t, d])
+                qb = [x / (G * Bq) for x in qb]
+                sc = [sum(qb[d] * kbar[i][d] for d in range(D)) for i in range(nb)]
+                for a in range(kk + 1):       # selection sort of the first k+1 places
+                    m = max(range(a, nb), key=lambda i: sc[i])
+                    sc[a], sc[m] = sc[m], sc[a]
+                best = min(best, sc[kk - 1] - sc[kk])
+    return best
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_selection_gap_loop_form(seed):
+    """Random inputs (GQA, batch 2, several query blocks): selection_gap
+    equals the loop-written gap to rounding."""
+    shape = small_shape(batch=2, n_q_heads=4, n_kv_heads=2, seq_len=96, seg_len=32,
+                        hist_block=4, query_block=8, top_k=3)
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((2, 4, 96, 8))
+    k = rng.standard_normal((2, 2, 96, 8))
+    for seg in range(shape.nseg):
+        a = orc.selection_gap(q, k, shape, seg)
+        b = _loop_gap(q, k, shape, seg)
+        if math.isinf(b):
+            assert math.isinf(a)
+        else:
+            assert abs(a - b) <= 1e-12, (seg, a, b)
+    # and with the summaries handed in
+    kbar = orc.block_summaries(k, shape.hist_block)
+    assert orc.selection_gap(q, k, shape, 2, kbar=kbar) == orc.selection_gap(q, k, shape, 2)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_2k", "train_16k", "infer_131k",
+                                  "batch4_32k"])
 def test_generator_gap_and_fp32_selection(name):
+    """Every workload's planted inputs keep a gap of at least 1e-3 at the
+    k-th boundary of every (sequence, KV head, query block) with more
+    history blocks than k, and fp32 scoring picks the fp64 sets."""
     shape = WORKLOADS[name]
     inp = make_inputs(shape, seed=0, with_do=False)
+    kbar = orc.block_summaries(inp["k"], shape.hist_block)
     for s in range(shape.nseg):
-        gap = orc.selection_gap(inp["q"], inp["k"], shape, s)
+        gap = orc.selection_gap(inp["q"], inp["k"], shape, s, kbar=kbar)
         assert gap >= 1e-3, (s, gap)
-        a = orc.select_segment(inp["q"], inp["k"], shape, s, precision="f64")
-        b = orc.select_segment(inp["q"], inp["k"], shape, s, precision="f32")
+        a = orc.select_segment(inp["q"], inp["k"], shape, s, precision="f64", kbar=kbar)
+        b = orc.select_segment(inp["q"], inp["k"], shape, s, precision="f32", kbar=kbar)
         np.testing.assert_array_equal(a, b)
 
 
