@@ -44,8 +44,24 @@ def parse():
     ap.add_argument("--no-dense-self", action="store_true")
     ap.add_argument("--no-diverse", action="store_true",
                     help="skip the extra timing on diverse-selection inputs")
-    ap.add_argument("--dense-sdpa", action="store_true",
-                    help="also time torch SDPA (flash backend) dense causal fwd+bwd")
+    ap.add_argument("--no-dense-sdpa", action="store_true",
+                    help="skip torch SDPA (flash backend) dense causal fwd+bwd at the same shape")
+    ap.add_argument("--no-sequential", action="store_true",
+                    help="skip the segment-by-segment form (hga_segment_step per segment)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the 131K inference and 4 x 32K training workloads")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated legs to run without the headline (for profiler runs): "
+                         "hbm, sequential, infer_131k, batch4_32k, exact, decode, host_tier; "
+                         "prints one JSON line with those legs only")
+    ap.add_argument("--trace-summary", nargs="+", metavar="CSV",
+                    help="no GPU: per-kernel statistics (median over warm launches) of rocprofv3 "
+                         "--kernel-trace CSV files, as a markdown table")
+    ap.add_argument("--pmc-table", nargs="+", metavar="CSV",
+                    help="no GPU: per-kernel averages of rocprofv3 --pmc counter CSV files, as a "
+                         "markdown table")
+    ap.add_argument("--skip-launches", type=int, default=1,
+                    help="--trace-summary: launches of each kernel left out at the start (warm-up)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step timing at the 131,072-token inference shape")
@@ -592,10 +608,293 @@ def cpu_baseline(inp, shape, budget_s):
     }
 
 
+def short_kernel_name(name: str) -> str:
+    """Kernel name without namespace and arguments, template arguments kept
+    (works on both the mangled and the demangled forms rocprofv3 prints)."""
+    import re
+    m = re.search(r"_GLOBAL__N_1(\d+)", name)
+    if m:  # mangled: _ZN3hga12_GLOBAL__N_1<len><name>I<args>E...
+        n = int(m.group(1))
+        base, rest = name[m.end():m.end() + n], name[m.end() + n:]
+        args = []
+        if rest.startswith("I"):
+            for a in re.finditer(r"DF16b|Li(\d+)E|f(?=[ELi])", rest[1:rest.find("EE") + 1]):
+                args.append("bf16" if a.group(0) == "DF16b" else (a.group(1) or "float"))
+        return base + (f"<{','.join(args)}>" if args else "")
+    m = re.search(r"(\w+)(<[^()]*>)?\(", name)
+    return (m.group(1) + (m.group(2) or "")) if m else name[:40]
+
+
+def trace_summary(paths, skip):
+    """Per-kernel statistics of rocprofv3 kernel-trace CSVs: every launch,
+    and the launches after the first `skip` of each kernel (warm), with
+    median and mean; for the whole-pass kernels of the 16K training
+    workload also the algorithmic TFLOP/s and fraction of the bf16 peak at
+    the warm median."""
+    import csv
+    import statistics
+    from sparse_long_context_query_amd import work
+    from synth import WORKLOADS
+    durs = {}
+    for path in paths:
+        rows = list(csv.DictReader(open(path)))
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        for r in rows:
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            durs.setdefault(short_kernel_name(r["Kernel_Name"]), []).append(d)
+    fl = work.flops(WORKLOADS["train_16k"])
+    flop_of = {"fwd_pass_kernel<128>": fl["fwd"], "dq_pass_kernel<128>": fl["bwd_dq"],
+               "dkdv_pass_kernel<128>": fl["bwd_dkdv"]}
+    print(f"| kernel | launches | mean us | warm launches | warm median us | warm mean us | "
+          f"warm min us | algorithmic TFLOP/s at warm median | fraction of 2.5 PFLOP/s |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|---:|")
+    for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        w = v[skip:] if len(v) > skip else v
+        med = statistics.median(w)
+        f = flop_of.get(k)
+        tf = f"{f / (med * 1e-6) / 1e12:.1f}" if f else ""
+        fr = f"{f / (med * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.4f}" if f else ""
+        print(f"| {k} | {len(v)} | {statistics.mean(v):.1f} | {len(w)} | {med:.1f} | "
+              f"{statistics.mean(w):.1f} | {min(w):.1f} | {tf} | {fr} |")
+
+
+# counters whose per-dispatch value is a sum over the 8 XCDs of a per-XCD
+# clock count (GRBM) or a sum over SIMDs (SQ_*_CYCLES), and derived ones
+PMC_DERIVED_NOTE = ("MfmaUtil = 100 * sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) * "
+                    "SIMDs); LDSBankConflict = 100 * sum(SQ_LDS_BANK_CONFLICT) / "
+                    "max(GRBM_GUI_ACTIVE) / CUs (rocprofv3's own definitions); clock = "
+                    "GRBM_GUI_ACTIVE / 8 XCDs / dispatch duration, for dispatches of 100 us "
+                    "or more")
+
+
+def pmc_table(paths):
+    """Per-kernel averages of rocprofv3 --pmc counter CSVs (one row per
+    kernel, one column per counter), with the clock the dispatches ran at."""
+    import csv
+    vals, durs = {}, {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            k = short_kernel_name(r["Kernel_Name"])
+            if "at::" in r["Kernel_Name"] or "copyBuffer" in r["Kernel_Name"]:
+                continue
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            durs.setdefault(k, {})[(path, r["Dispatch_Id"])] = (
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    counters = sorted({c for v in vals.values() for c in v})
+    print("| kernel | dispatches | mean us | clock GHz | " + " | ".join(counters) + " |")
+    print("|---|---:|---:|---:|" + "---:|" * len(counters))
+    for k in sorted(vals, key=lambda k: -sum(durs[k].values())):
+        d = sum(durs[k].values()) / len(durs[k])
+        gui = vals[k].get("GRBM_GUI_ACTIVE")
+        # GRBM_GUI_ACTIVE also counts a little time around the dispatch, so
+        # the clock is shown for long dispatches only
+        clk = f"{sum(gui) / len(gui) / 8 / d:.2f}" if gui and d >= 100e3 else ""
+        cells = []
+        for c in counters:
+            x = vals[k].get(c)
+            cells.append("" if not x else f"{sum(x) / len(x):.4g}")
+        print(f"| {k} | {len(durs[k])} | {d / 1e3:.1f} | {clk} | " + " | ".join(cells) + " |")
+    print()
+    print(PMC_DERIVED_NOTE)
+
+
+def stamped_kernels(fn, n):
+    """Runs fn() n times with every library kernel's dispatches stamping HIP
+    events; {class: (ms per call, launches per call)}."""
+    import torch
+    import sparse_long_context_query_amd as hga
+    torch.cuda.synchronize()
+    hga.profile_begin()
+    for _ in range(n):
+        fn()
+    prof = hga.profile_end()
+    return {c: (v[0] / n, v[1] // n) for c, v in prof.items() if v[1]}
+
+
+def event_timed(fn, n, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    for _ in range(n):
+        fn()
+    en.record()
+    torch.cuda.synchronize()
+    return st.elapsed_time(en) / n
+
+
+def fractions(shape, kern, bwd):
+    """fwd / bwd algorithmic TFLOP/s and fractions of the bf16 peak from
+    per-class kernel times (ms per pass)."""
+    from sparse_long_context_query_amd import work
+    fl = work.flops(shape)
+    out = {"kernels_ms_per_pass": {c: round(v[0], 4) for c, v in kern.items()},
+           "launches_per_pass": {c: v[1] for c, v in kern.items()}}
+    fwd_ms = kern["fwd"][0]
+    out["fwd_tflops"] = round(fl["fwd"] / (fwd_ms * 1e-3) / 1e12, 1)
+    out["fwd_frac_peak"] = round(fl["fwd"] / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    if bwd:
+        bwd_ms = sum(kern[c][0] for c in ("bwd_pre", "bwd_dq", "bwd_dkdv") if c in kern)
+        out["bwd_tflops"] = round(fl["bwd"] / (bwd_ms * 1e-3) / 1e12, 1)
+        out["bwd_frac_peak"] = round(fl["bwd"] / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    return out
+
+
+def sequential_bench(shape, dev, steps, warmup):
+    """The workload's segment-by-segment form: hga_segment_step for segment
+    0, 1, ... in order, each step summarizing the blocks the previous
+    segment closed, then selecting, running the forward and the backward of
+    its own segment (the one-segment kernels), all on one stream.  Also on
+    two streams: the summaries of every block first (hga_summarize), then
+    the steps alternate between the streams (HGA_STEP_SUMMARIES_READY, one
+    workspace per stream), so a step's kernels can fill the CUs the
+    previous step's leave idle."""
+    import torch
+    import sparse_long_context_query_amd as hga
+    from sparse_long_context_query_amd import work
+    cfg = hga.Config.from_shape(shape)
+    bwd = shape.bwd
+    buf = hga.Buffers(cfg, bwd=bwd)
+    ws2 = torch.empty_like(buf.ws) if bwd else None
+    nseg = shape.nseg
+    nblk = (shape.seq_len - shape.seg_len) // shape.hist_block
+
+    def one_stream():
+        for s_ in range(nseg):
+            hga.segment_step(cfg, s_, dev["q"], dev["k"], dev["v"], buf.summ, buf.sel, buf.o,
+                             buf.lse, dev.get("do"), buf.dq, buf.dk, buf.dv, buf.ws, bwd=bwd)
+
+    main = torch.cuda.current_stream()
+    other = buf.stream2
+
+    def two_streams():
+        hga.summarize(cfg, dev["k"], 0, nblk, buf.summ)
+        other.wait_stream(main)
+        for s_ in range(nseg):
+            st, ws = (main, buf.ws) if s_ % 2 == 0 else (other, ws2)
+            with torch.cuda.stream(st):
+                hga.segment_step(cfg, s_, dev["q"], dev["k"], dev["v"], buf.summ, buf.sel,
+                                 buf.o, buf.lse, dev.get("do"), buf.dq, buf.dk, buf.dv, ws,
+                                 bwd=bwd, summaries_ready=True)
+        main.wait_stream(other)
+
+    ms1 = event_timed(one_stream, steps, warmup)
+    ms2 = event_timed(two_streams, steps, warmup)
+    kern = stamped_kernels(one_stream, steps)
+    fl = work.flops(shape)
+    tokens = shape.batch * shape.seq_len
+    out = {"ms_per_pass": round(ms1, 4), "tokens_per_s": round(tokens / (ms1 * 1e-3), 1),
+           "two_streams_ms_per_pass": round(ms2, 4),
+           "two_streams_tokens_per_s": round(tokens / (ms2 * 1e-3), 1),
+           "pass_frac_peak": round((fl["fwd"] + (fl["bwd"] if bwd else 0)) / (ms1 * 1e-3)
+                                   / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    out.update(fractions(shape, kern, bwd))
+    out["note"] = ("hga_segment_step per segment in order (summarize the blocks the previous "
+                   "segment closed, select, forward, backward), one-segment kernels; "
+                   "kernel times from one-stream passes")
+    del buf, ws2
+    return out
+
+
+WORKLOAD_NOTES = {
+    "infer_131k": ("forward only; local causal window of 1,024 read as segment-aligned (segments "
+                   "of 1,024 tokens, causal within the segment, history = whole blocks before "
+                   "the segment); a sliding token window is not the reading taken"),
+    "batch4_32k": "four sequences of 32,768 tokens, per-sequence seeds and planted directions",
+}
+
+
+def workload_bench(name, steps, warmup):
+    """A whole segmented pass (hga_segment_pass) of another workload on its
+    planted-direction inputs, resident in HBM: tokens/s, and the forward and
+    backward kernels' fractions of the bf16 peak from stamped passes."""
+    import torch
+    import sparse_long_context_query_amd as hga
+    from sparse_long_context_query_amd import work
+    from synth import WORKLOADS, make_inputs
+    shape = WORKLOADS[name]
+    log(f"[bench] {name}: generating inputs")
+    inp = make_inputs(shape, seed=0)
+    dev = {k: torch.from_numpy(inp[k]).cuda().to(torch.bfloat16)
+           for k in ("q", "k", "v", "do") if inp.get(k) is not None}
+    del inp
+    cfg = hga.Config.from_shape(shape)
+    bwd = shape.bwd
+    buf = hga.Buffers(cfg, bwd=bwd)
+
+    def one():
+        buf.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=bwd)
+
+    log(f"[bench] {name}: timing")
+    ms = event_timed(one, steps, warmup)
+    kern = stamped_kernels(one, steps)
+    fl = work.flops(shape)
+    tokens = shape.batch * shape.seq_len
+    out = {"workload": name, "batch": shape.batch, "seq_len": shape.seq_len,
+           "seg_len": shape.seg_len, "hist_block": shape.hist_block,
+           "query_block": shape.query_block, "top_k": shape.top_k,
+           "step": "summarize + select + fwd" + (" + bwd" if bwd else "") +
+                   " of all segments (hga_segment_pass)",
+           "data": "synthetic (planted-direction N(0,1), seed 0)",
+           "ms_per_pass": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+           "algorithmic_flop_per_pass": fl["fwd"] + (fl["bwd"] if bwd else 0),
+           "pass_frac_peak": round((fl["fwd"] + (fl["bwd"] if bwd else 0)) / (ms * 1e-3)
+                                   / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "note": WORKLOAD_NOTES[name]}
+    out.update(fractions(shape, kern, bwd))
+    del buf, dev
+    torch.cuda.empty_cache()
+    return out
+
+
+
+def only_legs(args, shape):
+    """The legs named by --only, without the headline (profiler runs)."""
+    import torch
+    import sparse_long_context_query_amd as hga
+    from synth import make_inputs
+    legs = [x.strip() for x in args.only.split(",") if x.strip()]
+    out = {"only": legs}
+    dev = buf = None
+    if {"hbm", "sequential", "exact", "host_tier"} & set(legs):
+        inp = make_inputs(shape, seed=0, mode=args.mode)
+        dev = {k: torch.from_numpy(inp[k]).cuda().to(torch.bfloat16)
+               for k in ("q", "k", "v", "do") if inp.get(k) is not None}
+        buf = hga.Buffers(hga.Config.from_shape(shape), bwd=shape.bwd)
+        for _ in range(2):
+            buf.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=shape.bwd)
+        torch.cuda.synchronize()
+    for leg in legs:
+        log(f"[bench] leg {leg}")
+        if leg == "hbm":
+            out[leg] = hbm_kernels_bench(shape, dev, buf, args.steps)
+        elif leg == "sequential":
+            out[leg] = sequential_bench(shape, dev, args.steps, args.warmup)
+        elif leg in ("infer_131k", "batch4_32k"):
+            out[leg] = workload_bench(leg, args.steps, args.warmup)
+        elif leg == "exact":
+            out[leg] = exact_bench(shape, dev, args.steps, args.warmup)
+        elif leg == "host_tier":
+            out[leg] = host_tier_bench(shape, dev, args.steps, args.warmup)
+        elif leg == "decode":
+            out[leg] = decode_bench(args.decode_steps)
+        else:
+            raise SystemExit(f"unknown leg {leg!r}")
+    return out
+
+
 def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.skip_launches)
+        return
+    if args.pmc_table:
+        pmc_table(args.pmc_table)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the HGA hot "
@@ -624,6 +923,9 @@ def main():
 
     shape = WORKLOADS[args.workload]
     bwd = shape.bwd
+    if args.only:
+        print(json.dumps(only_legs(args, shape)), flush=True)
+        return
     log(f"[bench] generating {shape.name} inputs ({args.mode})")
     inp = make_inputs(shape, seed=0, mode=args.mode)
     dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
@@ -692,7 +994,8 @@ def main():
         extras["dense_causal_same_kernels_ms"] = round(dms, 3)
         extras["speedup_vs_dense_same_kernels"] = round(dms / ms, 2)
         del dbuf
-    if args.dense_sdpa:
+    if not args.no_dense_sdpa:
+        log("[bench] torch SDPA dense causal comparator")
         extras.update(dense_sdpa(dev, shape, bwd, ms))
     if not args.no_diverse and args.mode == "planted":
         # the same pass on inputs whose query blocks pick different history
@@ -709,6 +1012,13 @@ def main():
                              "data": "synthetic (one planted direction per query block)"}
         del ddev, dinp
 
+    if not args.no_sequential and shape.dtype == "bf16":
+        log("[bench] segment-by-segment form (hga_segment_step per segment)")
+        extras["sequential_steps"] = sequential_bench(shape, dev, args.steps, 3)
+    if not args.no_workloads and shape.name == "train_16k":
+        extras["workloads"] = {}
+        for wname in ("infer_131k", "batch4_32k"):
+            extras["workloads"][wname] = workload_bench(wname, max(3, args.steps // 4), 2)
     if not args.no_exact and bwd and shape.dtype == "bf16":
         log("[bench] exact-gradient pass")
         extras["exact_gradient"] = exact_bench(shape, dev, max(3, args.steps // 4), 1)

@@ -247,10 +247,14 @@ def attn_bwd(cfg: Config, q, k, v, o, lse, do, sel, seg: int, dq, dk, dv, ws) ->
 
 
 def segment_step(cfg: Config, seg: int, q, k, v, summ, sel, o, lse=None, do=None, dq=None,
-                 dk=None, dv=None, ws=None, bwd: bool = True) -> None:
+                 dk=None, dv=None, ws=None, bwd: bool = True,
+                 summaries_ready: bool = False) -> None:
+    """hga_segment_step on the current stream; summaries_ready sets
+    HGA_STEP_SUMMARIES_READY (summ already holds every block before the
+    segment, so the step does not summarize)."""
     s = Shapes(cfg)
     torch = _torch()
-    flags = HGA_STEP_BWD if bwd else 0
+    flags = (HGA_STEP_BWD if bwd else 0) | (HGA_STEP_SUMMARIES_READY if summaries_ready else 0)
     _check(lib().hga_segment_step(
         ctypes.byref(cfg), seg, flags, _ptr(q, "q", s.dt, s.q), _ptr(k, "k", s.dt, s.kv),
         _ptr(v, "v", s.dt, s.kv), _ptr(do, "do", s.dt, s.q, allow_none=not bwd),
