@@ -243,6 +243,28 @@ int hga_segment_pass(const hga_config* cfg, int32_t flags, const void* q, const 
                      float* lse, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
                      void* stream, void* stream2);
 
+/* hga_segment_pass without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The scratch space hga_segment_pass takes
+ * from `ws` (hga_workspace_size(cfg, HGA_OP_PASS) bytes, needed with
+ * HGA_STEP_BWD) comes instead from a fixed array of
+ * HGA_NOALLOC_SCRATCH_BYTES (64 MiB) in device memory that the library holds
+ * on every GPU it runs on, from the code object's load until the process
+ * ends; at train_16k the pass needs 2 MiB of it, at 4 x 32K 16 MiB.  Larger
+ * needs return HGA_ERR_WORKSPACE before anything is enqueued.  Everything
+ * runs on `stream` (the f32 pass does not use a second stream here, so no
+ * event is created either); the call makes no hipMalloc, hipFree or other
+ * allocating call.  The array keeps the last call's contents and nothing in
+ * it needs to start at zero.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and must not be made; calls ordered on one stream are fine.  Results
+ * equal hga_segment_pass's (same kernels, same order) bit for bit.  Other
+ * arguments, requirements and errors as hga_segment_pass. */
+#define HGA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int hga_segment_pass_noalloc(const hga_config* cfg, int32_t flags, const void* q, const void* k,
+                             const void* v, const void* dO, float* summ, int32_t* sel, void* o,
+                             float* lse, void* dq, void* dk, void* dv, void* stream);
+
 /* The whole exact-gradient pass ([SeCO] 提案手法: the backward visits the
  * chunks from the last one and the gradient is exact; here the history
  * keys are not detached): hga_summarize over every block a later segment

@@ -82,6 +82,8 @@ _SIGNATURES = {
                                         _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "hga_segment_pass": (ctypes.c_int, [_CP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P,
                                         _P, _P, _P, _P, ctypes.c_size_t, _P, _P]),
+    "hga_segment_pass_noalloc": (ctypes.c_int, [_CP, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
+                                                _P, _P, _P, _P, _P, _P]),
     "hga_segment_step_host": (ctypes.c_int, [_CP, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                              _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                              ctypes.c_size_t, _P]),
@@ -363,6 +365,26 @@ def segment_pass(cfg: Config, q, k, v, summ, sel, o, lse=None, do=None, dq=None,
         _ptr(ws, "ws", allow_none=not bwd),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(),
         None if stream2 is None else ctypes.c_void_p(stream2.cuda_stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # HGA_NOALLOC_SCRATCH_BYTES
+
+
+def segment_pass_noalloc(cfg: Config, q, k, v, summ, sel, o, lse=None, do=None, dq=None,
+                         dk=None, dv=None, bwd: bool = True) -> None:
+    """hga_segment_pass_noalloc on the current stream: the pass with its
+    scratch in the library's fixed per-GPU array instead of a workspace."""
+    s = Shapes(cfg)
+    torch = _torch()
+    flags = HGA_STEP_BWD if bwd else 0
+    _check(lib().hga_segment_pass_noalloc(
+        ctypes.byref(cfg), flags, _ptr(q, "q", s.dt, s.q), _ptr(k, "k", s.dt, s.kv),
+        _ptr(v, "v", s.dt, s.kv), _ptr(do, "do", s.dt, s.q, allow_none=not bwd),
+        _ptr(summ, "summ", torch.float32, s.summ), _ptr(sel, "sel", torch.int32, s.sel),
+        _ptr(o, "o", s.dt, s.q), _ptr(lse, "lse", torch.float32, s.lse, allow_none=not bwd),
+        _ptr(dq, "dq", s.dt, s.q, allow_none=not bwd),
+        _ptr(dk, "dk", s.dt, s.kv, allow_none=not bwd),
+        _ptr(dv, "dv", s.dt, s.kv, allow_none=not bwd), _stream()))
 
 
 def _host_args(cfg: Config, q, k_host, v_host, summ, sel, o, lse, do, dq, dk, dv, ws, bwd):

@@ -386,6 +386,34 @@ hipError_t device_events(hipEvent_t** out) {
   return hipSuccess;
 }
 
+// Scratch array of hga_segment_pass_noalloc, one per GPU (each device holds
+// its own copy from the code object's load until the process ends).  In
+// host code `scratch` is only a handle for hipGetSymbolAddress: host code
+// passes the device address scratch_address() returns, never the name.
+constexpr size_t kNoallocScratchBytes = HGA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and kept.
+hipError_t scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
 hipError_t pass_events(hipEvent_t* a, hipEvent_t* b) {
   hipEvent_t* ev = nullptr;
   const hipError_t e = device_events(&ev);
@@ -709,6 +737,45 @@ int hga_segment_pass(const hga_config* cfg, int32_t flags, const void* q, const 
     if ((e = hipStreamWaitEvent(st[0], ev_out, 0)) != hipSuccess) return hip_fail(e, "stream wait");
   }
   return ok();
+}
+
+int hga_segment_pass_noalloc(const hga_config* cfg, int32_t flags, const void* q, const void* k,
+                             const void* v, const void* dO, float* summ, int32_t* sel, void* o,
+                             float* lse, void* dq, void* dk, void* dv, void* stream) {
+  hga::Prob p;
+  int rc = make_prob(cfg, &p);
+  if (rc) return rc;
+  // hga_segment_pass's argument checks (the workspace aside), before the
+  // scratch array is looked up
+  if (flags & ~HGA_STEP_BWD)
+    return fail(HGA_ERR_ARG, "unknown flags 0x%x (the pass summarizes the history itself)",
+                flags);
+  HGA_REQUIRE(q);
+  HGA_REQUIRE(k);
+  HGA_REQUIRE(v);
+  HGA_REQUIRE(summ);
+  HGA_REQUIRE(sel);
+  HGA_REQUIRE(o);
+  if (flags & HGA_STEP_BWD) {
+    HGA_REQUIRE(lse);
+    HGA_REQUIRE(dO);
+    HGA_REQUIRE(dq);
+    HGA_REQUIRE(dk);
+    HGA_REQUIRE(dv);
+  }
+  // the scratch hga_segment_pass would take from its workspace argument
+  const size_t need = (flags & HGA_STEP_BWD) ? pass_workspace_bytes(p) : 0;
+  if (need > kNoallocScratchBytes)
+    return fail(HGA_ERR_WORKSPACE,
+                "the pass needs %zu bytes of scratch; the no-allocation form holds %zu per GPU",
+                need, kNoallocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return hip_fail(e, "scratch address");
+  }
+  return hga_segment_pass(cfg, flags, q, k, v, dO, summ, sel, o, lse, dq, dk, dv, ws, need,
+                          stream, nullptr);
 }
 
 int hga_segment_step_exact(const hga_config* cfg, int32_t seg, const void* q, const void* k,

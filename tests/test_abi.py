@@ -279,3 +279,23 @@ def test_segment_pass_validation(L):
     assert call(ws_bytes=two - 1) == hga.HGA_ERR_WORKSPACE
     # on one stream the pass needs the same workspace
     assert call(ws_bytes=two - 1, stream2=None) == hga.HGA_ERR_WORKSPACE
+
+
+def test_segment_pass_noalloc_validation(L):
+    """The no-allocation pass: host-side rejections before anything is
+    enqueued, including a scratch need beyond the fixed per-GPU array."""
+    cfg = good_cfg()
+
+    def call(c, flags=hga.HGA_STEP_BWD, dq=FAKE):
+        return L.hga_segment_pass_noalloc(ctypes.byref(c), flags, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          FAKE, FAKE, FAKE, dq, FAKE, FAKE, None)
+
+    assert call(cfg, flags=8) == hga.HGA_ERR_ARG and "flags" in hga.last_error()
+    assert call(cfg, dq=None) == hga.HGA_ERR_ARG and "dq is NULL" in hga.last_error()
+    assert call(cfg, flags=hga.HGA_STEP_BWD | hga.HGA_STEP_SUMMARIES_READY) == hga.HGA_ERR_ARG
+    # bf16: the delta rows of every segment, B*Hq*S*4 bytes; 2^20 tokens x 32
+    # heads x 4 bytes is 128 MiB, beyond the 64 MiB array
+    big = good_cfg(seq_len=1 << 20, seg_len=1024, hist_block=128)
+    need = L.hga_workspace_size(ctypes.byref(big), hga.HGA_OP_PASS)
+    assert need > hga.NOALLOC_SCRATCH_BYTES
+    assert call(big) == hga.HGA_ERR_WORKSPACE and "scratch" in hga.last_error()
