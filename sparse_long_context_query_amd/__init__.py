@@ -17,7 +17,9 @@ import os
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhga.so")
+# HGA_LIB names another build of the same library (the host-sanitized one
+# used by the CPU checks); the default is the package's own libhga.so
+LIB_PATH = os.environ.get("HGA_LIB") or os.path.join(_PKG, "libhga.so")
 
 HGA_OK = 0
 HGA_ERR_ARG = -1
