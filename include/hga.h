@@ -186,8 +186,11 @@ int hga_segment_step(const hga_config* cfg, int32_t seg, int32_t flags,
  * Requirements: 0 <= pos, n >= 1, pos+n <= S, the n tokens in one segment
  * (else HGA_ERR_ARG); G*n <= 64 (else HGA_ERR_UNSUPPORTED).  ws:
  * hga_workspace_size(cfg, HGA_OP_DECODE) bytes of scratch (per-chunk
- * partial sums, combined in a fixed order: results are deterministic);
- * calls sharing a workspace must not overlap. */
+ * partial sums, combined in a fixed order: results are deterministic; the
+ * selection scores); calls sharing a workspace must not overlap.  bf16
+ * steps with k < t0/Bh <= 1024 run as three launches (scores; attention,
+ * in which each history chunk takes the top-k itself; merge), the others
+ * as three or four (selection, attention, merge). */
 int hga_decode_step(const hga_config* cfg, int32_t pos, int32_t n, const void* q,
                     const void* k, const void* v, float* summ, int32_t* sel, void* o,
                     float* lse, void* ws, size_t ws_bytes, void* stream);

@@ -103,13 +103,17 @@ size_t bwd_exact_workspace_bytes(const Prob& p);
 // Decode step: selection of the n new tokens of q_new [B, Hq, n, D] (one
 // unit, sel [B, Hkv, k]; scores: B*Hkv*nblk floats of scratch), then their
 // attention (o [B, Hq, n, D], lse [B, Hq, n]) with the chunk partial sums
-// in ws.  decode_score_ws points at the scores' part of the decode workspace.
+// in ws.  decode_score_ws points at the scores' part of the decode
+// workspace.  decode_fused: the history chunks of the attention launch take
+// the top-k of the scores themselves (the selection launch then only scores
+// and leaves sel to the attention launch).
+bool decode_fused(const Prob& p, int pos, int n);
 hipError_t launch_select_decode(const Prob& p, const void* q_new, int n, int t0,
                                 const float* summ, int32_t* sel, float* scores,
-                                hipStream_t st);
+                                hipStream_t st, bool scores_only = false);
 hipError_t launch_decode(const Prob& p, int pos, int n, const void* q_new, const void* k,
-                         const void* v, const int32_t* sel, void* o, float* lse, float* ws,
-                         hipStream_t st);
+                         const void* v, int32_t* sel, void* o, float* lse, float* ws,
+                         bool fused, hipStream_t st);
 size_t decode_workspace_bytes(const Prob& p);
 float* decode_score_ws(const Prob& p, void* ws);
 int decode_max_rows();  // limit of G * n

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include "hga_internal.h"
+#include "hga_topk.h"
 
 namespace hga {
 namespace {
@@ -104,30 +105,6 @@ __device__ void bitonic_desc(unsigned long long* a, int n) {
   }
 }
 
-// Orderable 32-bit image of a score (larger score -> larger word; -0 and +0
-// tie); 0 lies below every finite score.
-__device__ __forceinline__ uint32_t score_ord(float s) {
-  s = s + 0.0f;
-  const uint32_t u = __float_as_uint(s);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// The k-th largest of the 64*E words held by one wave, counted with
-// multiplicity (E per lane, unused slots 0): the largest T with
-// #{words >= T} >= k, found bit by bit from the top.
-template <int E>
-__device__ __forceinline__ uint32_t wave_kth_largest32(const uint32_t (&v)[E], int k) {
-  uint32_t t = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = t | (1u << bit);
-    int c = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) c += __popcll(__ballot(v[e] >= cand));
-    if (c >= k) t = cand;
-  }
-  return t;
-}
-
 // qbar[d] = mean over the G heads of group g and the nrows query rows of
 // unit j of q (float32): every row load of a thread in flight at once, then
 // an LDS fold over the R row slots.  Ends with a barrier (qbar is ready).
@@ -177,43 +154,6 @@ __device__ __forceinline__ void group_query_mean(const T* __restrict__ q, const 
     qbar[d] = sum * inv;
   }
   __syncthreads();
-}
-
-// The k best of nb scores (nb <= 64 E) by (score desc, index asc), written
-// ascending to out[0, k): one wave finds the k-th largest score thr (with
-// multiplicity) by a bitwise search over the 32-bit score order held in its
-// registers, then keeps every score above thr and the lowest-index ties at
-// thr, compacting them in index order with ballots.  Called by the 64
-// threads of one wave; `score` may be in LDS or global memory.
-template <int E>
-__device__ __forceinline__ void wave_topk(const float* score, int nb, int K, int32_t* out,
-                                          int lane) {
-  uint32_t v[E];
-  float sv[E];
-  // unconditional loads (index clamped) so that all E are in flight at once
-#pragma unroll
-  for (int e = 0; e < E; ++e) sv[e] = score[min(64 * e + lane, nb - 1)];
-#pragma unroll
-  for (int e = 0; e < E; ++e) v[e] = 64 * e + lane < nb ? score_ord(sv[e]) : 0u;
-  const uint32_t thr = wave_kth_largest32<E>(v, K);
-  int gt = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) gt += __popcll(__ballot(v[e] > thr));
-  const int need = K - gt;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  int count = 0, ties = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = 64 * e + lane;
-    const bool ok = i < nb;
-    const bool eq = ok && v[e] == thr;
-    const unsigned long long meq = __ballot(eq);
-    const bool take = (ok && v[e] > thr) || (eq && ties + __popcll(meq & below) < need);
-    const unsigned long long m = __ballot(take);
-    if (take) out[count + __popcll(m & below)] = i;
-    count += __popcll(m);
-    ties += __popcll(meq);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -335,6 +275,87 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// a2 + a3 of several query blocks of one segment per block of threads (the
+// whole-pass selection, up to 1,024 candidates): up to U query blocks j0 ..
+// j0+nu-1 of segment seg share the segment's candidate blocks, so each
+// thread reads a candidate's summary row once and forms the nu scores from
+// it (the per-unit kernel reads every summary row once per query block).
+//   1. qbar of each of the nu query blocks (group_query_mean, one after the
+//      other, float32, the same sums as select_kernel's);
+//   2. score[u][i] = qbar_u . summ_i, one candidate per thread;
+//   3. + 4. wave w picks the k best of query blocks w, w+4, ... (wave_topk).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int E, int U>
+__global__ __launch_bounds__(kThreads) void select_multi_kernel(
+    const T* __restrict__ q, const float* __restrict__ summ,
+    int32_t* __restrict__ sel, SelGeom geo, int K, int Hq, int Hkv, int G, int nblk) {
+  constexpr int EL = Vec16<T>::N;
+  constexpr int C = D / EL;
+  constexpr int R = kThreads / C;
+  constexpr int NC = 64 * E;  // candidates a wave's search holds
+  __shared__ float part[R][D + 1];
+  __shared__ __attribute__((aligned(16))) float qbar[U][D];
+  __shared__ float s_score[U][NC];
+
+  const int gps = (geo.per_seg + U - 1) / U;  // groups of query blocks per segment
+  const int seg = geo.seg0 + (int)blockIdx.x / gps;
+  const int j0 = ((int)blockIdx.x % gps) * U;
+  const int nu = min(U, geo.per_seg - j0);
+  const int g = blockIdx.y, b = blockIdx.z;
+  geo.q0 = seg * geo.seg_len;
+  geo.out_j0 = seg * geo.per_seg;
+  const int nb = geo.q0 / geo.bh;
+  int32_t* out = sel + ((size_t)(b * Hkv + g) * geo.out_units + geo.out_j0 + j0) * K;
+
+  if (nb <= K) {  // every history block is taken (none at seg 0)
+    for (int t = threadIdx.x; t < nu * K; t += kThreads) {
+      const int kk = t % K;
+      out[t] = kk < nb ? kk : -1;
+    }
+    return;
+  }
+
+  // 1. the query-block means
+  for (int u = 0; u < nu; ++u) group_query_mean<T, D>(q, geo, b, g, j0 + u, Hq, G, part, qbar[u]);
+
+  // 2. scores, one candidate per thread, every unit from one read of its row
+  constexpr int NV = D / 4;
+  const float* sbase = summ + (size_t)(b * Hkv + g) * nblk * D;
+  for (int i = threadIdx.x; i < nb; i += kThreads) {
+    const float4* rowp = reinterpret_cast<const float4*>(sbase + (size_t)i * D);
+    float sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) sc[u] = 0.f;
+    constexpr int UV = 16;
+#pragma unroll
+    for (int v0 = 0; v0 < NV; v0 += UV) {
+      float4 x[UV];
+#pragma unroll
+      for (int w = 0; w < UV; ++w) x[w] = rowp[v0 + w];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (u < nu) {
+#pragma unroll
+          for (int w = 0; w < UV; ++w) {
+            const float4 qv = *reinterpret_cast<const float4*>(&qbar[u][4 * (v0 + w)]);
+            sc[u] += qv.x * x[w].x + qv.y * x[w].y + qv.z * x[w].z + qv.w * x[w].w;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (u < nu) s_score[u][i] = sc[u];
+  }
+  __syncthreads();
+
+  // 3. + 4. the k best of each query block, one wave per query block
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int u = wave; u < nu; u += kThreads / 64)
+    wave_topk<E>(s_score[u], nb, K, out + (size_t)u * K, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -470,6 +491,39 @@ hipError_t select_any(const Prob& p, const void* q, const float* summ, const Sel
                    : select_t<float, 128>(p, q, summ, geo, units, sel, st);
 }
 
+// Several query blocks of a segment per block of threads (U = 8), the
+// register search sized for the most candidates (<= 1,024).
+template <typename T, int D, int E>
+hipError_t select_multi_launch(const Prob& p, const void* q, const float* summ,
+                               const SelGeom& geo, int nseg, int32_t* sel, hipStream_t st) {
+  constexpr int U = 8;
+  const int gps = (geo.per_seg + U - 1) / U;
+  dim3 grid(nseg * gps, p.Hkv, p.B);
+  HGA_LAUNCH(HGA_K_SELECT, (select_multi_kernel<T, D, E, U>), grid, dim3(kThreads), 0, st,
+             (const T*)q, summ, sel, geo, p.K, p.Hq, p.Hkv, p.G, p.nblk);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t select_multi_t(const Prob& p, const void* q, const float* summ, const SelGeom& geo,
+                          int nseg, int32_t* sel, hipStream_t st) {
+  const int nb = geo.nb;
+  if (nb <= 64) return select_multi_launch<T, D, 1>(p, q, summ, geo, nseg, sel, st);
+  if (nb <= 128) return select_multi_launch<T, D, 2>(p, q, summ, geo, nseg, sel, st);
+  if (nb <= 256) return select_multi_launch<T, D, 4>(p, q, summ, geo, nseg, sel, st);
+  if (nb <= 512) return select_multi_launch<T, D, 8>(p, q, summ, geo, nseg, sel, st);
+  return select_multi_launch<T, D, 16>(p, q, summ, geo, nseg, sel, st);
+}
+
+hipError_t select_multi_any(const Prob& p, const void* q, const float* summ,
+                            const SelGeom& geo, int nseg, int32_t* sel, hipStream_t st) {
+  if (p.dtype == HGA_BF16)
+    return p.D == 64 ? select_multi_t<__bf16, 64>(p, q, summ, geo, nseg, sel, st)
+                     : select_multi_t<__bf16, 128>(p, q, summ, geo, nseg, sel, st);
+  return p.D == 64 ? select_multi_t<float, 64>(p, q, summ, geo, nseg, sel, st)
+                   : select_multi_t<float, 128>(p, q, summ, geo, nseg, sel, st);
+}
+
 }  // namespace
 
 hipError_t launch_summarize(const Prob& p, const void* k, int b0, int b1, float* summ,
@@ -496,12 +550,14 @@ hipError_t launch_select_pass(const Prob& p, const void* q, const float* summ, i
   // is sized for the last segment, which has the most candidates
   const int last = seg0 + nseg - 1;
   const SelGeom geo{p.S, 0, p.Bq, p.Bq, p.nqb_all, 0, last * p.L / p.Bh, p.nqb, seg0, p.L, p.Bh};
+  if (p.nqb >= 2 && geo.nb > p.K && geo.nb <= 1024)
+    return select_multi_any(p, q, summ, geo, nseg, sel, st);
   return select_any(p, q, summ, geo, p.nqb * nseg, sel, st);
 }
 
 hipError_t launch_select_decode(const Prob& p, const void* q_new, int n, int t0,
                                 const float* summ, int32_t* sel, float* scores,
-                                hipStream_t st) {
+                                hipStream_t st, bool scores_only) {
   // one unit: the n new tokens of q_new [B, Hq, n, D]; sel is [B, Hkv, k]
   const SelGeom geo{n, 0, 0, n, 1, 0, t0 / p.Bh, 0, 0, 0, 0};
   const int nb = geo.nb;
@@ -523,7 +579,8 @@ hipError_t launch_select_decode(const Prob& p, const void* q_new, int n, int t0,
                          (const float*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // scores_only: the attention launch takes the top-k itself
+  if (e != hipSuccess || scores_only) return e;
   const dim3 g1(1, p.Hkv, p.B);
   if (nb <= 64)
     HGA_LAUNCH(HGA_K_SELECT, topk_kernel<1>, g1, dim3(64), 0, st,
