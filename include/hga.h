@@ -187,10 +187,12 @@ int hga_segment_step(const hga_config* cfg, int32_t seg, int32_t flags,
  * (else HGA_ERR_ARG); G*n <= 64 (else HGA_ERR_UNSUPPORTED).  ws:
  * hga_workspace_size(cfg, HGA_OP_DECODE) bytes of scratch (per-chunk
  * partial sums, combined in a fixed order: results are deterministic; the
- * selection scores); calls sharing a workspace must not overlap.  bf16
- * steps with k < t0/Bh <= 1024 run as three launches (scores; attention,
- * in which each history chunk takes the top-k itself; merge), the others
- * as three or four (selection, attention, merge). */
+ * selection scores and top-k candidate lists); calls sharing a workspace
+ * must not overlap.  bf16 steps with k < t0/Bh <= 1024 and k <= 256 run as
+ * three launches: the scores, where every block of 256 candidates also
+ * keeps its own k best; the attention, whose history chunks pick the k best
+ * of those lists (the k best of the union, by the same rule); the merge.
+ * The others run as three or four launches (selection, attention, merge). */
 int hga_decode_step(const hga_config* cfg, int32_t pos, int32_t n, const void* q,
                     const void* k, const void* v, float* summ, int32_t* sel, void* o,
                     float* lse, void* ws, size_t ws_bytes, void* stream);

@@ -919,12 +919,13 @@ int hga_decode_step(const hga_config* cfg, int32_t pos, int32_t n, const void* q
     e = hga::launch_summarize(p, k, (t0 - p.L) / p.Bh, t0 / p.Bh, summ, st);
     if (e != hipSuccess) return hip_fail(e, "summarize launch");
   }
-  // bf16 with k < history blocks <= 1024: scores, attention (whose history
-  // chunks take the top-k themselves), merge; else selection, attention,
-  // merge
+  // bf16 with k < history blocks <= 1024: scores (each scoring block also
+  // keeps its own k best), attention (whose history chunks finish the top-k
+  // from those lists), merge; else selection, attention, merge
   const bool fused = hga::decode_fused(p, pos, n);
   e = hga::launch_select_decode(p, q, n, t0, summ, sel, hga::decode_score_ws(p, ws), st,
-                                fused);
+                                fused ? hga::decode_cand_score_ws(p, ws) : nullptr,
+                                fused ? hga::decode_cand_idx_ws(p, ws) : nullptr);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   e = hga::launch_decode(p, pos, n, q, k, v, sel, o, lse, (float*)ws, fused, st);
   if (e != hipSuccess) return hip_fail(e, "decode launch");

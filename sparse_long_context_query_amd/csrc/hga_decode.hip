@@ -24,6 +24,7 @@
 // 32-row tile of the G*n rows), f32 on the vector ALU (decode_attn_kernel).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "hga_internal.h"
@@ -44,9 +45,9 @@ struct DecArgs {
   int nch_h;  // history chunks
   int nc;     // chunks in all
   float c2;   // softmax scale * log2(e)
-  // bf16: the history chunks take the top-k of the nb scores themselves
-  // (scores rows are nblk apart)
-  int fused, nb, nblk;
+  // bf16: the history chunks finish the top-k themselves from the m
+  // candidates the scoring launch kept (ncs lists of K per (b, g))
+  int fused, m, ncs;
 };
 
 template <typename T> struct Elt;
@@ -275,14 +276,16 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
 //   S^T = K.Q^T (two 32-key halves),  per row: chunk max m, P = exp2(S c2 - m)
 //   on the visible keys, l = sum P,  O^T = V^T.P^T (V^T read transposed)
 // then writes m, l and the unnormalised O rows like decode_attn_kernel.
-// With a.fused, a history chunk first picks the k best of the step's nb
-// scores itself (wave_topk, the rule select_kernel applies, so every block
+// With a.fused, a history chunk first picks the k best of the m (score,
+// index) candidates the scoring launch kept (each of its blocks' k best, in
+// index order; wave_topk, the rule select_kernel applies, so every block
 // finds the same set; chunk 0 also writes it to sel): the step then needs
 // no top-k launch between the scores and the attention.
 template <int D>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    int32_t* __restrict__ sel, const float* __restrict__ scores, float* __restrict__ part_o,
+    int32_t* __restrict__ sel, const float* __restrict__ cand_score,
+    const int32_t* __restrict__ cand_idx, float* __restrict__ part_o,
     float* __restrict__ part_ml, DecArgs a) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
@@ -292,6 +295,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char s_k[TILE_B];
   __shared__ __attribute__((aligned(1024))) unsigned char s_v[TILE_B];
   __shared__ int s_sel[kMaxTopK];
+  __shared__ int s_pos[kMaxTopK];
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int bg = b * a.Hkv + g;
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hi = lane >> 5;
@@ -302,10 +306,22 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   // the scores, found here
   const int32_t* hsel = sel + (size_t)bg * a.K;
   if (a.fused && c < a.nch_h) {
-    if (wave == 0) wave_topk<16>(scores + (size_t)bg * a.nblk, a.nb, a.K, s_sel, lane);
+    const float* cs = cand_score + (size_t)bg * a.ncs * a.K;
+    if (wave == 0) {
+      if (a.m <= 64) wave_topk<1>(cs, a.m, a.K, s_pos, lane);
+      else if (a.m <= 128) wave_topk<2>(cs, a.m, a.K, s_pos, lane);
+      else if (a.m <= 256) wave_topk<4>(cs, a.m, a.K, s_pos, lane);
+      else if (a.m <= 512) wave_topk<8>(cs, a.m, a.K, s_pos, lane);
+      else wave_topk<16>(cs, a.m, a.K, s_pos, lane);
+    }
     __syncthreads();
-    if (c == 0)
-      for (int i = tid; i < a.K; i += 256) sel[(size_t)bg * a.K + i] = s_sel[i];
+    const int32_t* ci = cand_idx + (size_t)bg * a.ncs * a.K;
+    for (int i = tid; i < a.K; i += 256) {
+      const int blk = ci[s_pos[i]];
+      s_sel[i] = blk;
+      if (c == 0) sel[(size_t)bg * a.K + i] = blk;
+    }
+    __syncthreads();
     hsel = s_sel;
   }
 
@@ -450,8 +466,8 @@ DecPlan plan(const Prob& p, int pos, int n) {
   a.nc = a.nch_h + (pos + n - a.t0 + kCK - 1) / kCK;
   a.c2 = p.scale * kLog2e;
   a.fused = 0;
-  a.nb = nb;
-  a.nblk = p.nblk;
+  a.ncs = decode_cand_slots(p);
+  a.m = (nb + 255) / 256 * p.K;
   d.R = p.G * n;
   return d;
 }
@@ -473,7 +489,8 @@ hipError_t decode_t(const Prob& p, int pos, int n, const void* q_new, const void
     d.a.fused = fused ? 1 : 0;
     HGA_LAUNCH(HGA_K_DECODE, (decode_mfma_kernel<D>), dim3(d.a.nc, p.Hkv, p.B), dim3(256), 0, st,
                (const __bf16*)q_new, (const __bf16*)k, (const __bf16*)v, sel,
-               (const float*)decode_score_ws(p, ws), part_o, part_ml, d.a);
+               (const float*)decode_cand_score_ws(p, ws),
+               (const int32_t*)decode_cand_idx_ws(p, ws), part_o, part_ml, d.a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     HGA_LAUNCH(HGA_K_DECODE_MERGE, (decode_merge_kernel<T, D>), dim3(d.R, p.Hkv, p.B), dim3(64),
@@ -505,23 +522,43 @@ int decode_max_rows() { return kMaxRows; }
 
 // Workspace: chunk partial O [B, Hkv, chunks, 64, D], then the chunk (max,
 // sum) pairs [B, Hkv, chunks, 64, 2], then the selection scores
-// [B, Hkv, nblk], all float32.
+// [B, Hkv, nblk], all float32; then the two-stage top-k's candidate scores
+// [B, Hkv, slots, k] float32 and block indices [B, Hkv, slots, k] int32.
 static size_t partial_floats(const Prob& p) {
   return (size_t)p.B * p.Hkv * max_chunks(p) * kMaxRows * (p.D + 2);
 }
 
+int decode_cand_slots(const Prob& p) { return (std::min(p.nblk, 1024) + 255) / 256; }
+
+static size_t cand_entries(const Prob& p) {
+  return (size_t)p.B * p.Hkv * decode_cand_slots(p) * p.K;
+}
+
 size_t decode_workspace_bytes(const Prob& p) {
-  return (partial_floats(p) + (size_t)p.B * p.Hkv * p.nblk) * sizeof(float);
+  return (partial_floats(p) + (size_t)p.B * p.Hkv * p.nblk + cand_entries(p)) * sizeof(float) +
+         cand_entries(p) * sizeof(int32_t);
 }
 
 float* decode_score_ws(const Prob& p, void* ws) {
   return reinterpret_cast<float*>(ws) + partial_floats(p);
 }
 
+float* decode_cand_score_ws(const Prob& p, void* ws) {
+  return decode_score_ws(p, ws) + (size_t)p.B * p.Hkv * p.nblk;
+}
+
+int32_t* decode_cand_idx_ws(const Prob& p, void* ws) {
+  return reinterpret_cast<int32_t*>(decode_cand_score_ws(p, ws) + cand_entries(p));
+}
+
+// two-stage top-k: k < nb <= 1,024 history blocks (the scoring blocks hold
+// 256 candidates each), k <= 256 (one block's list), and at most 1,024
+// candidates left for the attention blocks' search
 bool decode_fused(const Prob& p, int pos, int n) {
   (void)n;
   const int nb = pos / p.L * p.L / p.Bh;
-  return p.dtype == HGA_BF16 && nb > p.K && nb <= 64 * 16;
+  return p.dtype == HGA_BF16 && nb > p.K && nb <= 1024 && p.K <= 256 &&
+         (nb + 255) / 256 * p.K <= 1024;
 }
 
 hipError_t launch_decode(const Prob& p, int pos, int n, const void* q_new, const void* k,

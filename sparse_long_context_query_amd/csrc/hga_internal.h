@@ -104,13 +104,19 @@ size_t bwd_exact_workspace_bytes(const Prob& p);
 // unit, sel [B, Hkv, k]; scores: B*Hkv*nblk floats of scratch), then their
 // attention (o [B, Hq, n, D], lse [B, Hq, n]) with the chunk partial sums
 // in ws.  decode_score_ws points at the scores' part of the decode
-// workspace.  decode_fused: the history chunks of the attention launch take
-// the top-k of the scores themselves (the selection launch then only scores
-// and leaves sel to the attention launch).
+// workspace, decode_cand_score_ws / decode_cand_idx_ws at the two-stage
+// top-k's candidate lists (decode_cand_slots lists of k per (b, g)).
+// decode_fused: the scoring launch also keeps each of its blocks' k best
+// (score, index) pairs, and the history chunks of the attention launch pick
+// the k best of those lists themselves (so no top-k launch runs between).
 bool decode_fused(const Prob& p, int pos, int n);
+int decode_cand_slots(const Prob& p);
+float* decode_cand_score_ws(const Prob& p, void* ws);
+int32_t* decode_cand_idx_ws(const Prob& p, void* ws);
 hipError_t launch_select_decode(const Prob& p, const void* q_new, int n, int t0,
                                 const float* summ, int32_t* sel, float* scores,
-                                hipStream_t st, bool scores_only = false);
+                                hipStream_t st, float* cand_score = nullptr,
+                                int32_t* cand_idx = nullptr);
 hipError_t launch_decode(const Prob& p, int pos, int n, const void* q_new, const void* k,
                          const void* v, int32_t* sel, void* o, float* lse, float* ws,
                          bool fused, hipStream_t st);

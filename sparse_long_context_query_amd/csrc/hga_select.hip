@@ -365,16 +365,28 @@ __global__ __launch_bounds__(kThreads) void select_multi_kernel(
 // threads, writes the fp32 scores (the same dot products select_kernel
 // forms); topk_kernel: one wave per (b, g) picks the k best (wave_topk).
 // ---------------------------------------------------------------------------
+//
+// With cand_score / cand_idx (the decode step's two-stage top-k), each block
+// also keeps the k best of its own 256 candidates (wave_topk, or all of them
+// when it has no more than k) as (score, block index) pairs, ascending in
+// block index, at slot blockIdx.x of its (b, g) row of cand_* (ncs slots of
+// k entries per row), padded with (-inf, -1).  The top-k of all candidates
+// is the top-k of these lists under the same (score desc, index asc) rule,
+// and blocks and entries follow the index order, so the decode attention
+// can finish the selection from at most ncs * k entries.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void score_kernel(
     const T* __restrict__ q, const float* __restrict__ summ, float* __restrict__ scores,
-    SelGeom geo, int Hq, int Hkv, int G, int nblk) {
+    SelGeom geo, int Hq, int Hkv, int G, int nblk, float* __restrict__ cand_score,
+    int32_t* __restrict__ cand_idx, int K, int ncs) {
   constexpr int EL = Vec16<T>::N;
   constexpr int C = D / EL;
   constexpr int R = kThreads / C;
   constexpr int NV = D / 4;
   __shared__ float part[R][D + 1];
   __shared__ __attribute__((aligned(16))) float qbar[D];
+  __shared__ float s_sc[kThreads];
+  __shared__ int32_t s_pos[kThreads];
   const int g = blockIdx.y, b = blockIdx.z;
   const int i = blockIdx.x * kThreads + threadIdx.x;
   // the candidate's summary row first, so that it overlaps the query mean
@@ -391,6 +403,27 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     sc += qv.x * x[u].x + qv.y * x[u].y + qv.z * x[u].z + qv.w * x[u].w;
   }
   if (i < geo.nb) scores[(size_t)(b * Hkv + g) * nblk + i] = sc;
+  if (cand_score == nullptr) return;
+  // the block's own k best (kThreads = 256 candidates: four per lane)
+  const int nbb = min(kThreads, geo.nb - (int)blockIdx.x * kThreads);
+  s_sc[threadIdx.x] = sc;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    if (nbb > K) {
+      wave_topk<kThreads / 64>(s_sc, nbb, K, s_pos, lane);
+    } else {
+      for (int t = lane; t < nbb; t += 64) s_pos[t] = t;
+    }
+  }
+  __syncthreads();
+  const int kept = min(K, nbb);
+  const size_t row = ((size_t)(b * Hkv + g) * ncs + blockIdx.x) * K;
+  for (int t = threadIdx.x; t < K; t += kThreads) {
+    const bool ok = t < kept;
+    cand_score[row + t] = ok ? s_sc[s_pos[t]] : -INFINITY;
+    cand_idx[row + t] = ok ? (int)blockIdx.x * kThreads + s_pos[t] : -1;
+  }
 }
 
 template <int E>
@@ -557,30 +590,35 @@ hipError_t launch_select_pass(const Prob& p, const void* q, const float* summ, i
 
 hipError_t launch_select_decode(const Prob& p, const void* q_new, int n, int t0,
                                 const float* summ, int32_t* sel, float* scores,
-                                hipStream_t st, bool scores_only) {
+                                hipStream_t st, float* cand_score, int32_t* cand_idx) {
   // one unit: the n new tokens of q_new [B, Hq, n, D]; sel is [B, Hkv, k]
   const SelGeom geo{n, 0, 0, n, 1, 0, t0 / p.Bh, 0, 0, 0, 0};
   const int nb = geo.nb;
   if (nb <= p.K || nb > 1024) return select_any(p, q_new, summ, geo, 1, sel, st);
   const dim3 grid((nb + kThreads - 1) / kThreads, p.Hkv, p.B);
+  const int ncs = decode_cand_slots(p);
   if (p.dtype == HGA_BF16) {
     if (p.D == 64)
       HGA_LAUNCH(HGA_K_SELECT, (score_kernel<__bf16, 64>), grid, dim3(kThreads), 0, st,
-                         (const __bf16*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk);
+                         (const __bf16*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk,
+                 cand_score, cand_idx, p.K, ncs);
     else
       HGA_LAUNCH(HGA_K_SELECT, (score_kernel<__bf16, 128>), grid, dim3(kThreads), 0, st,
-                         (const __bf16*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk);
+                         (const __bf16*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk,
+                 cand_score, cand_idx, p.K, ncs);
   } else {
     if (p.D == 64)
       HGA_LAUNCH(HGA_K_SELECT, (score_kernel<float, 64>), grid, dim3(kThreads), 0, st,
-                         (const float*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk);
+                         (const float*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk,
+                 cand_score, cand_idx, p.K, ncs);
     else
       HGA_LAUNCH(HGA_K_SELECT, (score_kernel<float, 128>), grid, dim3(kThreads), 0, st,
-                         (const float*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk);
+                         (const float*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk,
+                 cand_score, cand_idx, p.K, ncs);
   }
   hipError_t e = hipGetLastError();
-  // scores_only: the attention launch takes the top-k itself
-  if (e != hipSuccess || scores_only) return e;
+  // with the candidate lists the attention launch finishes the top-k
+  if (e != hipSuccess || cand_score != nullptr) return e;
   const dim3 g1(1, p.Hkv, p.B);
   if (nb <= 64)
     HGA_LAUNCH(HGA_K_SELECT, topk_kernel<1>, g1, dim3(64), 0, st,

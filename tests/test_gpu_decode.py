@@ -125,3 +125,51 @@ def test_decode_full_size_131k():
         np.testing.assert_array_equal(sel, want_sel)
         assert_close("o", o, O, TOL[shape.dtype])
         assert_close("lse", lse, LSE, TOL[shape.dtype])
+
+
+def tied_score_inputs(shape, seed, nvalues):
+    """Keys of history block x all equal to v_x e_0 and queries equal to e_0:
+    the block summary is v_x e_0 and the step's query mean e_0 exactly, so
+    every selection score is the small integer v_x on both sides, and with
+    far more blocks than values the k-th boundary falls inside a run of
+    equal scores that spans several 256-block groups.  V is random."""
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, S, D = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.seq_len, shape.head_dim
+    vals = rng.integers(0, nvalues, size=(B, Hkv, S // shape.hist_block)).astype(np.float32)
+    k = np.zeros((B, Hkv, S, D), np.float32)
+    k[..., 0] = np.repeat(vals, shape.hist_block, axis=2)
+    q = np.zeros((B, Hq, S, D), np.float32)
+    q[..., 0] = 1.0
+    v = rng.standard_normal((B, Hkv, S, D)).astype(np.float32)
+    return {"q": q, "k": k, "v": v}
+
+
+# (top-k, first new token, new tokens): 1,016 candidates (four scoring
+# blocks) with lists of 8 to 256, and 264 / 300 candidates, whose last
+# scoring block holds fewer than k and keeps them all
+TWO_STAGE_CASES = [(8, 16256, 1), (30, 16300, 4), (60, 16383, 1), (100, 16256, 16),
+                   (256, 16383, 1), (256, 4224, 2), (200, 4800, 1)]
+
+
+@pytest.mark.parametrize("top_k,pos,n", TWO_STAGE_CASES)
+def test_decode_two_stage_topk_ties(top_k, pos, n):
+    """The two-stage top-k of the bf16 decode step (each scoring block keeps
+    its own k best, the attention blocks pick the k best of those lists)
+    against the oracle's single top-k over all candidates, with exact integer
+    scores and ties at the k-th boundary: the selection bit for bit (the
+    lower block index wins every tie), O and LSE within the tolerance."""
+    shape = shp(seq_len=16384, seg_len=128, hist_block=16, query_block=16, top_k=top_k,
+                n_q_heads=2, n_kv_heads=1, head_dim=64)
+    inp = tied_score_inputs(shape, 5, 40)
+    dev = upload(inp, shape)
+    kbar = orc.block_summaries(inp["k"], shape.hist_block)
+    nb = pos // shape.seg_len * shape.seg_len // shape.hist_block
+    sc = kbar[0, 0, :nb, 0]
+    kth = np.sort(sc)[::-1][top_k - 1]
+    assert (sc > kth).sum() < top_k < (sc >= kth).sum()  # a tie at the boundary
+    q_new = inp["q"][:, :, pos:pos + n]
+    sel, o, lse, _ = run_decode(shape, dev, pos, n)
+    want_sel, O, LSE = orc.decode_step(q_new, inp["k"], inp["v"], shape, pos, kbar=kbar)
+    np.testing.assert_array_equal(sel, want_sel)
+    assert_close("o", o, O, TOL["bf16"])
+    assert_close("lse", lse, LSE, TOL["bf16"])
