@@ -156,6 +156,59 @@ __device__ __forceinline__ void group_query_mean(const T* __restrict__ q, const 
   __syncthreads();
 }
 
+// Scores of summary rows, 8 lanes per row: a wave covers 8 rows per pass and
+// 64 rows in 8 passes.  Lane (rr = lane / 8, sub = lane % 8) reads the
+// 16-byte pieces sub, sub + 8, ... of its row, so one wave load covers
+// eight whole 128-byte lines (a thread per row touches 64 lines per load).
+// Each lane forms its part of the dot product (fmaf, in piece order) and
+// the 8 parts are added by a butterfly over the lanes (xor 1, 2, 4), which
+// leaves the same value in the 8 lanes of the row.  Every selection kernel
+// scores through these two functions, so a row's fp32 score is the same
+// whichever kernel forms it.
+template <int D>
+struct RowPieces {
+  static constexpr int F = D / 32;  // pieces per lane and row
+  float4 x[8][F];
+};
+
+// Requests the pieces of rows row0 + 8p + lane / 8 (p < 8) of sbase; rows at
+// or past nrows read row 0 instead (their scores are not used).
+template <int D>
+__device__ __forceinline__ void load_rows64(RowPieces<D>& rp, const float* __restrict__ sbase,
+                                            int row0, int nrows, int lane) {
+  const int rr = lane >> 3, sub = lane & 7;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r = row0 + 8 * p + rr;
+    const float4* rowp =
+        reinterpret_cast<const float4*>(sbase + (size_t)(r < nrows ? r : 0) * D);
+#pragma unroll
+    for (int u = 0; u < RowPieces<D>::F; ++u) rp.x[p][u] = rowp[8 * u + sub];
+  }
+}
+
+// Score of the row of pass p against the query mean qm (D floats in LDS).
+// Called by whole waves (the butterfly needs every lane).
+template <int D>
+__device__ __forceinline__ float row_score8(const RowPieces<D>& rp, int p,
+                                            const float* qm, int lane) {
+  const int sub = lane & 7;
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < RowPieces<D>::F; ++u) {
+    const float4 qv = *reinterpret_cast<const float4*>(&qm[4 * (8 * u + sub)]);
+    const float4 x = rp.x[p][u];
+    s = fmaf(qv.x, x.x, s);
+    s = fmaf(qv.y, x.y, s);
+    s = fmaf(qv.z, x.z, s);
+    s = fmaf(qv.w, x.w, s);
+  }
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  return s;
+}
+
 // ---------------------------------------------------------------------------
 // a2 + a3: one block of threads per (unit j, KV head g, sequence b); a unit
 // is a query block of a segment, or the new tokens of a decode step.
@@ -205,45 +258,27 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     return;
   }
 
-  // 2a. the first candidate's summary row of every thread, requested first
-  constexpr int NV = D / 4;
+  // 2a. the first 256 candidates' summary rows, requested first
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const float* sbase = summ + (size_t)(b * Hkv + g) * nblk * D;
-  float4 srow0[NV];
-  {
-    const int i = threadIdx.x < nb ? threadIdx.x : 0;
-    const float4* rowp = reinterpret_cast<const float4*>(sbase + (size_t)i * D);
-#pragma unroll
-    for (int u = 0; u < NV; ++u) srow0[u] = rowp[u];
-  }
+  RowPieces<D> rp;
+  if (wave * 64 < nb) load_rows64<D>(rp, sbase, wave * 64, nb, lane);
 
   // 1. query-block mean over (head in group, token in block)
   group_query_mean<T, D>(q, geo, b, g, j, Hq, G, part, qbar);
 
-  // 2. scores, one candidate per thread
-  for (int i = threadIdx.x; i < nb; i += kThreads) {
-    float sc = 0.f;
-    if (i == threadIdx.x) {
+  // 2. scores, 64 candidates per wave and round (8 lanes per row)
+  for (int c0 = 0; c0 < nb; c0 += kThreads) {
+    const int row0 = c0 + wave * 64;
+    if (row0 < nb) {  // uniform over the wave
+      if (c0 > 0) load_rows64<D>(rp, sbase, row0, nb, lane);
 #pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        const float4 qv = *reinterpret_cast<const float4*>(&qbar[4 * u]);
-        sc += qv.x * srow0[u].x + qv.y * srow0[u].y + qv.z * srow0[u].z + qv.w * srow0[u].w;
-      }
-    } else {
-      const float4* rowp = reinterpret_cast<const float4*>(sbase + (size_t)i * D);
-      constexpr int UV = 16;
-#pragma unroll
-      for (int v0 = 0; v0 < NV; v0 += UV) {
-        float4 x[UV];
-#pragma unroll
-        for (int u = 0; u < UV; ++u) x[u] = rowp[v0 + u];
-#pragma unroll
-        for (int u = 0; u < UV; ++u) {
-          const float4 qv = *reinterpret_cast<const float4*>(&qbar[4 * (v0 + u)]);
-          sc += qv.x * x[u].x + qv.y * x[u].y + qv.z * x[u].z + qv.w * x[u].w;
-        }
+      for (int p = 0; p < 8; ++p) {
+        const float sc = row_score8<D>(rp, p, qbar, lane);
+        const int r = row0 + 8 * p + (lane >> 3);
+        if ((lane & 7) == 0 && r < nb) s_score[r] = sc;
       }
     }
-    s_score[i] = sc;
   }
   __syncthreads();
 
@@ -321,39 +356,31 @@ __global__ __launch_bounds__(kThreads) void select_multi_kernel(
   // 1. the query-block means
   for (int u = 0; u < nu; ++u) group_query_mean<T, D>(q, geo, b, g, j0 + u, Hq, G, part, qbar[u]);
 
-  // 2. scores, one candidate per thread, every unit from one read of its row
-  constexpr int NV = D / 4;
+  // 2. scores, 64 candidates per wave and round (8 lanes per row), every
+  // unit from one read of the row
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const float* sbase = summ + (size_t)(b * Hkv + g) * nblk * D;
-  for (int i = threadIdx.x; i < nb; i += kThreads) {
-    const float4* rowp = reinterpret_cast<const float4*>(sbase + (size_t)i * D);
-    float sc[U];
+  for (int c0 = 0; c0 < nb; c0 += kThreads) {
+    const int row0 = c0 + wave * 64;
+    if (row0 < nb) {  // uniform over the wave
+      RowPieces<D> rp;
+      load_rows64<D>(rp, sbase, row0, nb, lane);
 #pragma unroll
-    for (int u = 0; u < U; ++u) sc[u] = 0.f;
-    constexpr int UV = 16;
+      for (int p = 0; p < 8; ++p) {
+        const int r = row0 + 8 * p + (lane >> 3);
 #pragma unroll
-    for (int v0 = 0; v0 < NV; v0 += UV) {
-      float4 x[UV];
-#pragma unroll
-      for (int w = 0; w < UV; ++w) x[w] = rowp[v0 + w];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (u < nu) {
-#pragma unroll
-          for (int w = 0; w < UV; ++w) {
-            const float4 qv = *reinterpret_cast<const float4*>(&qbar[u][4 * (v0 + w)]);
-            sc[u] += qv.x * x[w].x + qv.y * x[w].y + qv.z * x[w].z + qv.w * x[w].w;
+        for (int u = 0; u < U; ++u) {
+          if (u < nu) {  // uniform
+            const float sc = row_score8<D>(rp, p, qbar[u], lane);
+            if ((lane & 7) == 0 && r < nb) s_score[u][r] = sc;
           }
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (u < nu) s_score[u][i] = sc[u];
   }
   __syncthreads();
 
   // 3. + 4. the k best of each query block, one wave per query block
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int u = wave; u < nu; u += kThreads / 64)
     wave_topk<E>(s_score[u], nb, K, out + (size_t)u * K, lane);
 }
@@ -382,32 +409,33 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
   constexpr int EL = Vec16<T>::N;
   constexpr int C = D / EL;
   constexpr int R = kThreads / C;
-  constexpr int NV = D / 4;
   __shared__ float part[R][D + 1];
   __shared__ __attribute__((aligned(16))) float qbar[D];
   __shared__ float s_sc[kThreads];
   __shared__ int32_t s_pos[kThreads];
   const int g = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = blockIdx.x * kThreads + threadIdx.x;
-  // the candidate's summary row first, so that it overlaps the query mean
-  const float4* rowp = reinterpret_cast<const float4*>(
-      summ + ((size_t)(b * Hkv + g) * nblk + (i < geo.nb ? i : 0)) * D);
-  float4 x[NV];
-#pragma unroll
-  for (int u = 0; u < NV; ++u) x[u] = rowp[u];
+  // the block's summary rows first (8 lanes per row), so that they overlap
+  // the query mean
+  const int row0 = blockIdx.x * kThreads + wave * 64;
+  RowPieces<D> rp;
+  if (row0 < geo.nb) load_rows64<D>(rp, summ + (size_t)(b * Hkv + g) * nblk * D, row0, geo.nb,
+                                    lane);
   group_query_mean<T, D>(q, geo, b, g, 0, Hq, G, part, qbar);
-  float sc = 0.f;
+  if (row0 < geo.nb) {  // uniform over the wave
 #pragma unroll
-  for (int u = 0; u < NV; ++u) {
-    const float4 qv = *reinterpret_cast<const float4*>(&qbar[4 * u]);
-    sc += qv.x * x[u].x + qv.y * x[u].y + qv.z * x[u].z + qv.w * x[u].w;
+    for (int p = 0; p < 8; ++p) {
+      const float s = row_score8<D>(rp, p, qbar, lane);
+      if ((lane & 7) == 0) s_sc[wave * 64 + 8 * p + (lane >> 3)] = s;
+    }
   }
+  __syncthreads();
+  const float sc = s_sc[threadIdx.x];
   if (i < geo.nb) scores[(size_t)(b * Hkv + g) * nblk + i] = sc;
   if (cand_score == nullptr) return;
   // the block's own k best (kThreads = 256 candidates: four per lane)
   const int nbb = min(kThreads, geo.nb - (int)blockIdx.x * kThreads);
-  s_sc[threadIdx.x] = sc;
-  __syncthreads();
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     if (nbb > K) {
