@@ -36,6 +36,10 @@ namespace {
 
 constexpr int kCK = 64;     // keys per chunk (one per lane)
 constexpr int kMaxRows = 64;  // G * n limit
+// 64-key parts per chunk of decode_mfma_kernel: for up to 32 query rows
+// (one row tile) and for more
+constexpr int kPartsFewRows = 1;
+constexpr int kPartsManyRows = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -48,6 +52,7 @@ struct DecArgs {
   // bf16: the history chunks finish the top-k themselves from the m
   // candidates the scoring launch kept (ncs lists of K per (b, g))
   int fused, m, ncs;
+  int ck;     // keys per chunk (kCK for f32; 128 or 256 for bf16)
 };
 
 template <typename T> struct Elt;
@@ -269,33 +274,48 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
   if (lse != nullptr && lane == 0) lse[orow] = (M + log2f(l)) * kLn2;
 }
 
-// bf16, MFMA form of decode_attn_kernel (same chunks, same partial sums).
-// The chunk's K and V rows are copied straight into swizzled row-major LDS
-// tiles; wave w takes query rows 32w .. 32w+31 of the R = G*n rows (row r =
-// head r / n, token r % n) and, with Q^T in registers as the B operand:
-//   S^T = K.Q^T (two 32-key halves),  per row: chunk max m, P = exp2(S c2 - m)
-//   on the visible keys, l = sum P,  O^T = V^T.P^T (V^T read transposed)
-// then writes m, l and the unnormalised O rows like decode_attn_kernel.
+// bf16, MFMA form of decode_attn_kernel (the same partial sums, over
+// chunks of CK = 64 * 4 / RT keys).  The chunk's K and V rows are copied
+// straight into swizzled row-major LDS tiles.  The R = G*n query rows (row r
+// = head r / n, token r % n) form RT tiles of 32; wave w takes row tile
+// w % RT and the 64 keys 64 (w / RT) .. +63 of the chunk, so all 4 waves
+// work whatever n is, and, with Q^T in registers as the B operand:
+//   S^T = K.Q^T (two 32-key halves),  per row: max m, P = exp2(S c2 - m) on
+//   the visible keys, l = sum P,  O^T = V^T.P^T (V^T read transposed).
+// The 4 / RT key parts of a row tile are then combined through LDS in part
+// order (M = max m, l = sum l 2^(m - M), O likewise), and one wave writes
+// the chunk's m, l and unnormalised O rows like decode_attn_kernel.  Larger
+// chunks for fewer rows keep the partial sums the merge reads few.
 // With a.fused, a history chunk first picks the k best of the m (score,
 // index) candidates the scoring launch kept (each of its blocks' k best, in
 // index order; wave_topk, the rule select_kernel applies, so every block
 // finds the same set; chunk 0 also writes it to sel): the step then needs
 // no top-k launch between the scores and the attention.
-template <int D>
+template <int D, int RT, int KPARTS>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     int32_t* __restrict__ sel, const float* __restrict__ cand_score,
     const int32_t* __restrict__ cand_idx, float* __restrict__ part_o,
     float* __restrict__ part_ml, DecArgs a) {
+  static_assert(RT == 1 || RT == 2, "row tiles");
+  static_assert(RT * KPARTS <= 4, "one wave per (row tile, key part)");
+  // idle waves leave before the compute; the merge's barriers need all 4
+  static_assert(KPARTS == 1 || RT * KPARTS == 4, "no idle wave with a merge");
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int TILE_B = kCK * 2 * D;
+  constexpr int CK = 64 * KPARTS;       // keys per chunk (a.ck)
+  constexpr int TILE_B = CK * 2 * D;
+  constexpr int PART_B = 64 * 2 * D;    // bytes of one part's rows
   constexpr int CPR = (2 * D) / 16;     // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;         // rows per 1 KB copy instruction
+  // the parts' O^T sums (64 lanes x NDB x 16 floats per wave) go where the
+  // K rows were once every wave is done with them
+  static_assert((KPARTS - 1) * RT * 64 * NDB * 16 * 4 <= TILE_B, "merge slots");
   __shared__ __attribute__((aligned(1024))) unsigned char s_k[TILE_B];
   __shared__ __attribute__((aligned(1024))) unsigned char s_v[TILE_B];
   __shared__ int s_sel[kMaxTopK];
   __shared__ int s_pos[kMaxTopK];
+  __shared__ float s_ml[4][32][2];
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int bg = b * a.Hkv + g;
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hi = lane >> 5;
@@ -328,12 +348,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   // token of key `key` of this chunk; rows that hold no key read a valid row
   auto token_of = [&](int key, bool& valid, bool& local) {
     if (c < a.nch_h) {
-      const int hp = c * kCK + key;
+      const int hp = c * CK + key;
       valid = hp < a.nht;
       local = false;
       return valid ? hsel[hp / a.Bh] * a.Bh + hp % a.Bh : 0;
     }
-    const int t = a.t0 + (c - a.nch_h) * kCK + key;
+    const int t = a.t0 + (c - a.nch_h) * CK + key;
     valid = t < a.pos + a.n;
     local = true;
     return valid ? t : a.t0;
@@ -343,7 +363,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kv_base, (uint32_t)a.S * (2 * D));
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kv_base, (uint32_t)a.S * (2 * D));
 #pragma unroll
-    for (int n = 0; n < kCK / RPI / 4; ++n) {
+    for (int n = 0; n < CK / RPI / 4; ++n) {
       const int i = wave + 4 * n;
       const int row = i * RPI + lane / CPR;
       bool vld, loc;
@@ -355,7 +375,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   }
   // this wave's query rows as B operands: lane (row lq, hi) holds
   // Q[row][16kk + 8hi .. +7]
-  const int r = 32 * wave + lq;
+  const int rt = wave % RT, kp = wave / RT;
+  const int r = 32 * rt + lq;
   const bool row_ok = r < R;
   const int hh = row_ok ? r / a.n : 0, ti = row_ok ? r % a.n : 0;
   bf16x8 qreg[NKK];
@@ -368,70 +389,132 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   drain_vmem_loads();
   __syncthreads();
 
-  if (32 * wave < R) {
-    FragOffsets<D> fo;
-    fo.init(lane);
-    floatx16 sacc[2];
+  // waves past the RT * KPARTS (row tile, key part) pairs only copy
+  if (wave >= RT * KPARTS) return;
+  const unsigned char* sk = s_k + kp * PART_B;
+  const unsigned char* sv = s_v + kp * PART_B;
+  FragOffsets<D> fo;
+  fo.init(lane);
+  floatx16 sacc[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) sacc[st] = floatx16{};
+  for (int st = 0; st < 2; ++st) sacc[st] = floatx16{};
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
+  for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) sacc[st] = mfma32(fo.row(s_k, st, kk), qreg[kk], sacc[st]);
-    // C layout: lane = query row lq, item rr of half st = key 32st + 8(rr/4) + 4hi + rr%4
-    float mt = -INFINITY;
+    for (int st = 0; st < 2; ++st) sacc[st] = mfma32(fo.row(sk, st, kk), qreg[kk], sacc[st]);
+  // C layout: lane = query row lq, item rr of half st = key 32st + 8(rr/4) + 4hi + rr%4
+  float mt = -INFINITY;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+  for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int key = 32 * st + 8 * (rr >> 2) + 4 * hi + (rr & 3);
-        // history keys: every selected token; local keys: up to this row's token
-        const int tl = a.t0 + (c - a.nch_h) * kCK + key;
-        const bool vis = c < a.nch_h ? c * kCK + key < a.nht : tl <= a.pos + ti;
-        sacc[st][rr] = vis ? sacc[st][rr] * a.c2 : -INFINITY;
-        mt = fmaxf(mt, sacc[st][rr]);
-      }
-    mt = pair_max(mt);
-    float lsum = 0.f;
+    for (int rr = 0; rr < 16; ++rr) {
+      const int key = 64 * kp + 32 * st + 8 * (rr >> 2) + 4 * hi + (rr & 3);
+      // history keys: every selected token; local keys: up to this row's token
+      const int tl = a.t0 + (c - a.nch_h) * CK + key;
+      const bool vis = c < a.nch_h ? c * CK + key < a.nht : tl <= a.pos + ti;
+      sacc[st][rr] = vis ? sacc[st][rr] * a.c2 : -INFINITY;
+      mt = fmaxf(mt, sacc[st][rr]);
+    }
+  mt = pair_max(mt);
+  float lsum = 0.f;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+  for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const float p = mt == -INFINITY ? 0.f : exp2f(sacc[st][rr] - mt);
-        sacc[st][rr] = p;
-        lsum += p;
-      }
-    lsum = pair_sum(lsum);
-    floatx16 oacc[NDB];
+    for (int rr = 0; rr < 16; ++rr) {
+      const float p = mt == -INFINITY ? 0.f : exp2f(sacc[st][rr] - mt);
+      sacc[st][rr] = p;
+      lsum += p;
+    }
+  lsum = pair_sum(lsum);
+  floatx16 oacc[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
+  for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+  for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int r0 = 8 * ks;
-        const bf16x8 pb = to_bf16x8(sacc[st][r0], sacc[st][r0 + 1], sacc[st][r0 + 2],
-                                    sacc[st][r0 + 3], sacc[st][r0 + 4], sacc[st][r0 + 5],
-                                    sacc[st][r0 + 6], sacc[st][r0 + 7]);
+    for (int ks = 0; ks < 2; ++ks) {
+      const int r0 = 8 * ks;
+      const bf16x8 pb = to_bf16x8(sacc[st][r0], sacc[st][r0 + 1], sacc[st][r0 + 2],
+                                  sacc[st][r0 + 3], sacc[st][r0 + 4], sacc[st][r0 + 5],
+                                  sacc[st][r0 + 6], sacc[st][r0 + 7]);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          oacc[db] = mfma32(fo.tr(s_v, 32 * st + 16 * ks, db), pb, oacc[db]);
-      }
-    if (row_ok) {
-      float* ml = part_ml + ((size_t)bg * a.nc + c) * kMaxRows * 2;
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = mfma32(fo.tr(sv, 32 * st + 16 * ks, db), pb, oacc[db]);
+    }
+
+  // combine the key parts of each row tile in part order: parts 1.. leave
+  // (m, l) and O^T in LDS (the K rows' space, free once every wave is past
+  // its score products), part 0 adds them
+  if constexpr (KPARTS > 1) {
+    float4* slots = reinterpret_cast<float4*>(s_k);
+    __syncthreads();  // every wave is done reading the K rows
+    if (kp > 0) {
       if (hi == 0) {
-        ml[2 * r] = mt;
-        ml[2 * r + 1] = lsum;
+        s_ml[wave][lq][0] = mt;
+        s_ml[wave][lq][1] = lsum;
       }
-      float* po = part_o + (((size_t)bg * a.nc + c) * kMaxRows + r) * D;
+      float4* mine = slots + (size_t)(wave - RT) * NDB * 4 * 64 + lane;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
-          *reinterpret_cast<float4*>(po + 32 * db + 8 * r4 + 4 * hi) =
-              make_float4(oacc[db][4 * r4], oacc[db][4 * r4 + 1], oacc[db][4 * r4 + 2],
-                          oacc[db][4 * r4 + 3]);
+          mine[(db * 4 + r4) * 64] = make_float4(oacc[db][4 * r4], oacc[db][4 * r4 + 1],
+                                                 oacc[db][4 * r4 + 2], oacc[db][4 * r4 + 3]);
     }
+    __syncthreads();
+    if (kp > 0) return;
+    float mp[KPARTS], lp[KPARTS];
+    mp[0] = mt;
+    lp[0] = lsum;
+    float M = mt;
+#pragma unroll
+    for (int j = 1; j < KPARTS; ++j) {
+      mp[j] = s_ml[rt + RT * j][lq][0];
+      lp[j] = s_ml[rt + RT * j][lq][1];
+      M = fmaxf(M, mp[j]);
+    }
+    // a part with no visible key of the row has (m, l) = (-inf, 0)
+    float f[KPARTS];
+    lsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < KPARTS; ++j) {
+      f[j] = lp[j] > 0.f ? exp2f(mp[j] - M) : 0.f;
+      lsum += lp[j] * f[j];
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] *= f[0];
+#pragma unroll
+    for (int j = 1; j < KPARTS; ++j) {
+      const float4* theirs = slots + (size_t)(rt + RT * j - RT) * NDB * 4 * 64 + lane;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 t = theirs[(db * 4 + r4) * 64];
+          oacc[db][4 * r4] += t.x * f[j];
+          oacc[db][4 * r4 + 1] += t.y * f[j];
+          oacc[db][4 * r4 + 2] += t.z * f[j];
+          oacc[db][4 * r4 + 3] += t.w * f[j];
+        }
+    }
+    mt = M;
+  }
+  if (row_ok) {
+    float* ml = part_ml + ((size_t)bg * a.nc + c) * kMaxRows * 2;
+    if (hi == 0) {
+      ml[2 * r] = mt;
+      ml[2 * r + 1] = lsum;
+    }
+    float* po = part_o + (((size_t)bg * a.nc + c) * kMaxRows + r) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(po + 32 * db + 8 * r4 + 4 * hi) =
+            make_float4(oacc[db][4 * r4], oacc[db][4 * r4 + 1], oacc[db][4 * r4 + 2],
+                        oacc[db][4 * r4 + 3]);
   }
 }
 
@@ -461,9 +544,11 @@ DecPlan plan(const Prob& p, int pos, int n) {
   a.t0 = pos / p.L * p.L;
   a.K = p.K;
   const int nb = a.t0 / p.Bh;
+  // bf16: decode_mfma_kernel's chunks, 64 keys per part
+  a.ck = p.dtype == HGA_BF16 ? 64 * (p.G * n <= 32 ? kPartsFewRows : kPartsManyRows) : kCK;
   a.nht = (nb < p.K ? nb : p.K) * p.Bh;
-  a.nch_h = (a.nht + kCK - 1) / kCK;
-  a.nc = a.nch_h + (pos + n - a.t0 + kCK - 1) / kCK;
+  a.nch_h = (a.nht + a.ck - 1) / a.ck;
+  a.nc = a.nch_h + (pos + n - a.t0 + a.ck - 1) / a.ck;
   a.c2 = p.scale * kLog2e;
   a.fused = 0;
   a.ncs = decode_cand_slots(p);
@@ -487,10 +572,16 @@ hipError_t decode_t(const Prob& p, int pos, int n, const void* q_new, const void
   float* part_ml = ws + (size_t)p.B * p.Hkv * max_chunks(p) * kMaxRows * p.D;
   if constexpr (std::is_same<T, __bf16>::value) {
     d.a.fused = fused ? 1 : 0;
-    HGA_LAUNCH(HGA_K_DECODE, (decode_mfma_kernel<D>), dim3(d.a.nc, p.Hkv, p.B), dim3(256), 0, st,
-               (const __bf16*)q_new, (const __bf16*)k, (const __bf16*)v, sel,
-               (const float*)decode_cand_score_ws(p, ws),
-               (const int32_t*)decode_cand_idx_ws(p, ws), part_o, part_ml, d.a);
+    if (d.R <= 32)
+      HGA_LAUNCH(HGA_K_DECODE, (decode_mfma_kernel<D, 1, kPartsFewRows>), dim3(d.a.nc, p.Hkv, p.B),
+                 dim3(256), 0, st, (const __bf16*)q_new, (const __bf16*)k, (const __bf16*)v, sel,
+                 (const float*)decode_cand_score_ws(p, ws),
+                 (const int32_t*)decode_cand_idx_ws(p, ws), part_o, part_ml, d.a);
+    else
+      HGA_LAUNCH(HGA_K_DECODE, (decode_mfma_kernel<D, 2, kPartsManyRows>), dim3(d.a.nc, p.Hkv, p.B),
+                 dim3(256), 0, st, (const __bf16*)q_new, (const __bf16*)k, (const __bf16*)v, sel,
+                 (const float*)decode_cand_score_ws(p, ws),
+                 (const int32_t*)decode_cand_idx_ws(p, ws), part_o, part_ml, d.a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     HGA_LAUNCH(HGA_K_DECODE_MERGE, (decode_merge_kernel<T, D>), dim3(d.R, p.Hkv, p.B), dim3(64),
