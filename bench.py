@@ -93,7 +93,7 @@ KERNEL_CLASS_OF = {"tier_fetch_kernel": "tier_fetch", "tier_plan_kernel": "tier_
                    "dkdv_pass_kernel": "bwd_dkdv", "fwd_bf16_kernel": "fwd",
                    "dq_bf16_kernel": "bwd_dq", "dkdv_bf16_kernel": "bwd_dkdv",
                    "delta_kernel": "bwd_pre", "select_kernel": "select",
-                   "summarize_kernel": "summarize"}
+                   "select_multi_kernel": "select", "summarize_kernel": "summarize"}
 
 
 def sources_sha256() -> str:
