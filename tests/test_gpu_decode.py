@@ -173,3 +173,34 @@ def test_decode_two_stage_topk_ties(top_k, pos, n):
     np.testing.assert_array_equal(sel, want_sel)
     assert_close("o", o, O, TOL["bf16"])
     assert_close("lse", lse, LSE, TOL["bf16"])
+
+
+# (top-k, sequence length, first new token, new tokens) of the bf16 steps
+# that do not take the two-stage top-k: k above 256 (the scores, then one
+# top-k launch), and more than 1,024 candidates (the LDS sort of the
+# selection kernel)
+FALLBACK_CASES = [(300, 16384, 16383, 1), (300, 16384, 12000, 4), (8, 20480, 20479, 1),
+                  (64, 20480, 20000, 16)]
+
+
+@pytest.mark.parametrize("top_k,seq_len,pos,n", FALLBACK_CASES)
+def test_decode_fallback_selection_ties(top_k, seq_len, pos, n):
+    """The bf16 decode step's other selection paths against the oracle, with
+    exact integer scores and ties at the k-th boundary: selection bit for
+    bit, O and LSE within the tolerance."""
+    shape = shp(seq_len=seq_len, seg_len=128, hist_block=16, query_block=16, top_k=top_k,
+                n_q_heads=2, n_kv_heads=1, head_dim=64)
+    inp = tied_score_inputs(shape, 7, 40)
+    dev = upload(inp, shape)
+    kbar = orc.block_summaries(inp["k"], shape.hist_block)
+    nb = pos // shape.seg_len * shape.seg_len // shape.hist_block
+    assert nb > top_k and (top_k > 256 or nb > 1024)
+    sc = kbar[0, 0, :nb, 0]
+    kth = np.sort(sc)[::-1][top_k - 1]
+    assert (sc > kth).sum() < top_k < (sc >= kth).sum()  # a tie at the boundary
+    q_new = inp["q"][:, :, pos:pos + n]
+    sel, o, lse, _ = run_decode(shape, dev, pos, n)
+    want_sel, O, LSE = orc.decode_step(q_new, inp["k"], inp["v"], shape, pos, kbar=kbar)
+    np.testing.assert_array_equal(sel, want_sel)
+    assert_close("o", o, O, TOL["bf16"])
+    assert_close("lse", lse, LSE, TOL["bf16"])
