@@ -13,15 +13,16 @@
 //
 // Work split (split over keys): per (sequence, KV head) the step's key list
 // -- the selected history tokens in ascending order, then the local tokens
-// t0 .. pos+n-1 -- is cut into chunks of 64 keys.  One block of 4 waves per
-// (chunk, KV head, sequence) stages the chunk's K and V rows in LDS (16-byte
-// loads, every one in flight at once, each row read once); wave w then
-// takes the query rows r = w, w+4, ... of the R = G*n rows of the group and
-// writes the chunk's max, sum of exponentials and unnormalised P.V (fp32)
-// to the workspace.  A merge kernel then combines the chunks of every row in
-// chunk order (deterministic) into o and lse.  bf16 runs the chunk products
-// on the matrix cores (decode_mfma_kernel: S^T = K.Q^T and O^T = V^T.P^T per
-// 32-row tile of the G*n rows), f32 on the vector ALU (decode_attn_kernel).
+// t0 .. pos+n-1 -- is cut into chunks (64 keys; bf16 steps with more than
+// 32 query rows: 128).  One block of 4 waves per (chunk, KV head, sequence)
+// stages the chunk's K and V rows in LDS (every load in flight at once, each
+// row read once) and writes the chunk's max, sum of exponentials and
+// unnormalised P.V (fp32) for each of the R = G*n rows of the group to the
+// workspace.  A merge kernel then combines the chunks of every row in chunk
+// order (deterministic) into o and lse.  bf16 runs the chunk products on
+// the matrix cores (decode_mfma_kernel: S^T = K.Q^T and O^T = V^T.P^T per
+// 32-row tile of the G*n rows), f32 on the vector ALU (decode_attn_kernel,
+// wave w taking the rows w, w+4, ...).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -52,7 +53,7 @@ struct DecArgs {
   // bf16: the history chunks finish the top-k themselves from the m
   // candidates the scoring launch kept (ncs lists of K per (b, g))
   int fused, m, ncs;
-  int ck;     // keys per chunk (kCK for f32; 128 or 256 for bf16)
+  int ck;     // keys per chunk (kCK, or 128 for bf16 steps of over 32 rows)
 };
 
 template <typename T> struct Elt;
@@ -322,8 +323,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int R = a.G * a.n;
 
-  // the chosen history blocks: from sel, or (one-launch form) the top-k of
-  // the scores, found here
+  // the chosen history blocks: from sel, or (two-stage top-k) the k best of
+  // the scoring launch's candidate lists, found here
   const int32_t* hsel = sel + (size_t)bg * a.K;
   if (a.fused && c < a.nch_h) {
     const float* cs = cand_score + (size_t)bg * a.ncs * a.K;

@@ -387,10 +387,11 @@ __global__ __launch_bounds__(kThreads) void select_multi_kernel(
 
 // ---------------------------------------------------------------------------
 // Selection of a decode step, which has a single unit per (b, g) but up to
-// 1,024 candidates: two launches so that reading the summaries spreads over
-// many CUs.  score_kernel: one candidate per thread, 256 per block of
-// threads, writes the fp32 scores (the same dot products select_kernel
-// forms); topk_kernel: one wave per (b, g) picks the k best (wave_topk).
+// 1,024 candidates: the scoring spreads over many CUs.  score_kernel: 256
+// candidates per block of threads (8 lanes per summary row, the scoring
+// helper every selection kernel uses), writes the fp32 scores; topk_kernel:
+// one wave per (b, g) picks the k best (wave_topk), where the two-stage
+// form below does not apply.
 // ---------------------------------------------------------------------------
 //
 // With cand_score / cand_idx (the decode step's two-stage top-k), each block
