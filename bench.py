@@ -52,7 +52,8 @@ def parse():
                     help="skip the 131K inference and 4 x 32K training workloads")
     ap.add_argument("--only", default=None,
                     help="comma-separated legs to run without the headline (for profiler runs): "
-                         "hbm, sequential, infer_131k, batch4_32k, exact, decode, host_tier; "
+                         "hbm, sequential, infer_131k, batch4_32k, exact, decode, host_tier, "
+                         "peaks; "
                          "prints one JSON line with those legs only")
     ap.add_argument("--trace-summary", nargs="+", metavar="CSV",
                     help="no GPU: per-kernel statistics (median over warm launches) of rocprofv3 "
@@ -73,6 +74,8 @@ def parse():
                     help="skip the exact-gradient (history not detached) pass timing")
     ap.add_argument("--no-tier-131k", action="store_true",
                     help="skip the host-tier pass at the 131K inference shape")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured bf16 GEMM and copy rates (measured_peaks)")
     ap.add_argument("--no-hbm", action="store_true",
                     help="skip the summaries-at-131K and standalone-gather measurements")
     ap.add_argument("--no-host-tier", action="store_true",
@@ -880,6 +883,8 @@ def only_legs(args, shape):
             out[leg] = host_tier_bench(shape, dev, args.steps, args.warmup)
         elif leg == "decode":
             out[leg] = decode_bench(args.decode_steps)
+        elif leg == "peaks":
+            out[leg] = measured_peaks()
         else:
             raise SystemExit(f"unknown leg {leg!r}")
     return out
@@ -1071,12 +1076,55 @@ def main():
         },
     }
     out.update(extras)
+    if not args.no_peaks:
+        log("[bench] measured peaks (bf16 GEMM, device copy)")
+        mp = measured_peaks()
+        if achieved:
+            mp["dominant_frac_of_gemm"] = round(achieved / mp["bf16_gemm_tflops"], 4)
+        out["measured_peaks"] = mp
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline (oracle, ~{args.cpu_seconds:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(inp, shape, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def measured_peaks(steps=20):
+    """What the machine sustains, to read the fractions against beside the
+    published peaks: a square bf16 GEMM through torch (hipBLASLt; plain 2-D
+    mm on contiguous tensors) and a 1 GiB device-to-device copy (bytes read
+    + written)."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2.0 * n ** 3 / (e0.elapsed_time(e1) / steps * 1e-3) / 1e12
+    del a, b, c
+    src = torch.empty(1 << 30, device="cuda", dtype=torch.uint8)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * (1 << 30) / (e0.elapsed_time(e1) / steps * 1e-3) / 1e9
+    del src, dst
+    return {"bf16_gemm_tflops": round(gemm_tflops, 1), "gemm": f"torch.mm bf16 {n}^3",
+            "copy_gbs": round(copy_gbs, 1), "copy": "1 GiB device-to-device, read + written"}
 
 
 def dense_sdpa(dev, shape, bwd, hga_ms):
