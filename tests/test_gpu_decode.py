@@ -77,6 +77,7 @@ CASES = [(0, 1), (1, 4), (128, 1), (200, 2), (255, 1), (256, 2), (300, 1), (511,
     (shp(n_q_heads=16, n_kv_heads=2, top_k=4), [(130, 8), (500, 8), (3, 8)]),  # G*n = 64
     (shp(n_q_heads=2, n_kv_heads=2), [(129, 1), (510, 2), (260, 64)]),  # G = 1, n = 64
     (shp(head_dim=64, hist_block=64, query_block=64, top_k=2), CASES),  # D = 64
+    (shp(head_dim=64, hist_block=32, query_block=32, top_k=3), [(300, 16), (130, 12)]),  # D = 64, G*n > 32
     (shp(batch=2, seq_len=256), [(0, 1), (128, 3), (255, 1)]),        # batch 2
     (shp(dtype="f32", head_dim=64, n_q_heads=4, n_kv_heads=2), CASES),
     (shp(dtype="f32", hist_block=8, query_block=8, top_k=6, seq_len=256), [(64, 1), (200, 5)]),
