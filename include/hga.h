@@ -7,6 +7,13 @@
  *        プロpagationの実践」, sns.style (Japanese edition)
  *   [FR] « Ajustement fin long-contexte à faible VRAM : une approche
  *        d'optimisation avec attention globale hiérarchique », sns.style
+ *   [DE] „Geringer-VRAM Lang-Kontext Fine-Tuning: Hierarchische globale
+ *        Aufmerksamkeit und segmentierte Rückwärtsausbreitung in der
+ *        Praxis", sns.style (German edition)
+ *   [KO] 「저VRAM 긴 컨텍스트 미세조정: 계층적 글로벌 주의와 분할 역전파의
+ *        실전 적용」, sns.style (Korean edition)
+ *   [SeCO] notes on "Training Long-Context LLMs Efficiently via Chunk-wise
+ *        Optimization", f-binder
  *
  * The method ([JA] 背景と概要; [FR] Contexte, Analyse approfondie): a long
  * sequence is processed segment by segment; only the active segment is
