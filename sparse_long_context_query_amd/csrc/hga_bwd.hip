@@ -239,6 +239,9 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
   floatx16 dqacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqacc[db] = floatx16{};
+  floatx16 negd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negd[r] = -dlt;
   FragOffsets<D> fo;
   fo.init(lane);
 
@@ -274,7 +277,9 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
           kf[kk] = fo.row(kt, st, kk);
           vf[kk] = fo.row(vt, st, kk);
         }
-        floatx16 sacc = floatx16{}, pacc = floatx16{};
+        // dP starts from -delta (constant along a lane, the query), so the
+        // products give dP - delta directly
+        floatx16 sacc = floatx16{}, pacc = negd;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
           sacc = mfma32(kf[kk], qreg[kk], sacc);
@@ -301,7 +306,7 @@ __global__ __launch_bounds__(512) void dq_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(fmaf(sacc[r], a.c2, -lse2));
-          sacc[r] = p * (pacc[r] - dlt);
+          sacc[r] = p * pacc[r];
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -443,6 +448,9 @@ __global__ __launch_bounds__(256, 2) void dq_pass_kernel(
   floatx16 dqacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqacc[db] = floatx16{};
+  floatx16 negd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negd[r] = -dlt;
   FragOffsets<D> fo;
   fo.init(lane);
   drain_vmem_loads();
@@ -471,7 +479,9 @@ __global__ __launch_bounds__(256, 2) void dq_pass_kernel(
           kf[kk] = fo.row(kt, st, kk);
           vf[kk] = fo.row(vt, st, kk);
         }
-        floatx16 sacc = floatx16{}, pacc = floatx16{};
+        // dP starts from -delta (constant along a lane, the query), so the
+        // products give dP - delta directly
+        floatx16 sacc = floatx16{}, pacc = negd;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
           sacc = mfma32(kf[kk], qreg[kk], sacc);
@@ -499,7 +509,7 @@ __global__ __launch_bounds__(256, 2) void dq_pass_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(fmaf(sacc[r], a.c2, -lse2));
-          sacc[r] = p * (pacc[r] - dlt);
+          sacc[r] = p * pacc[r];
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
