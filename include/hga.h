@@ -196,8 +196,9 @@ int hga_segment_step(const hga_config* cfg, int32_t seg, int32_t flags,
  * partial sums, combined in a fixed order: results are deterministic; the
  * selection scores and top-k candidate lists); calls sharing a workspace
  * must not overlap.  bf16 steps with k < t0/Bh <= 1024 and k <= 256 run as
- * three launches: the scores, where every block of 256 candidates also
- * keeps its own k best; the attention, whose history chunks pick the k best
+ * three launches: the scores, where every block of 128 candidates (256
+ * when 128-candidate lists would leave over 1,024 entries) also keeps its
+ * own k best; the attention, whose history chunks pick the k best
  * of those lists (the k best of the union, by the same rule); the merge.
  * The others run as three or four launches (selection, attention, merge). */
 int hga_decode_step(const hga_config* cfg, int32_t pos, int32_t n, const void* q,

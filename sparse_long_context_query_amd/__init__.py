@@ -151,13 +151,13 @@ def _ptr(t, name, dtype=None, shape=None, allow_none=False):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must live on the GPU (got {t.device})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
     return ctypes.c_void_p(t.data_ptr())
 

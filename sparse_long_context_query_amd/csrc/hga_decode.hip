@@ -219,19 +219,40 @@ __global__ __launch_bounds__(64 * kWaves) void decode_attn_kernel(
 
 // Combines the chunks of query row r of (g, b) in chunk order, one wave
 // (lane = column group).  With M = max_c m_c: l = sum_c l_c 2^(m_c - M),
-// o = sum_c O_c 2^(m_c - M) / l, lse = (M + log2 l) ln 2.
+// o = sum_c O_c 2^(m_c - M) / l, lse = (M + log2 l) ln 2.  The rows of the
+// first kMergeBatch chunks do not depend on M and are requested together
+// with the chunk maxima; later chunks follow in batches of as many.
+constexpr int kMergeBatch = 16;
+
 template <typename T, int D>
 __device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
                                           const float* __restrict__ part_ml, T* __restrict__ o,
                                           float* __restrict__ lse, const DecArgs& a, int r,
                                           int g, int b, int lane) {
   constexpr int ND = D / 64;
+  constexpr int CB = kMergeBatch;
   const size_t base = (size_t)(b * a.Hkv + g) * a.nc;
+  float x[CB][ND];
+  auto request = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int cc = min(c0 + u, a.nc - 1);
+      const float* po = part_o + ((base + cc) * kMaxRows + r) * D;
+#pragma unroll
+      for (int e = 0; e < ND; ++e) x[u][e] = po[lane + 64 * e];
+    }
+  };
+  request(0);
   // chunk maxima and sums, lane c holding chunk c (+ 64 j)
   float M = -INFINITY;
+  float2 ml0 = make_float2(-INFINITY, 0.f);
   for (int c0 = 0; c0 < a.nc; c0 += 64) {
     const int c = c0 + lane;
-    if (c < a.nc) M = fmaxf(M, part_ml[((base + c) * kMaxRows + r) * 2]);
+    if (c < a.nc) {
+      const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((base + c) * kMaxRows + r) * 2);
+      if (c0 == 0) ml0 = ml;
+      M = fmaxf(M, ml.x);
+    }
   }
   M = wave_max(M);
   float l = 0.f, acc[ND];
@@ -241,29 +262,24 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
     const int c = c0 + lane;
     float f = 0.f, lc = 0.f;
     if (c < a.nc) {
-      const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((base + c) * kMaxRows + r) * 2);
+      const float2 ml =
+          c0 == 0 ? ml0
+                  : *reinterpret_cast<const float2*>(part_ml + ((base + c) * kMaxRows + r) * 2);
       // a chunk with no visible key of this row has ml = (-inf, 0)
       f = ml.y > 0.f ? exp2f(ml.x - M) : 0.f;
       lc = ml.y * f;
     }
     l += lc;
     const int cn = min(64, a.nc - c0);
-    for (int j = 0; j < cn; j += 8) {
-      // eight chunks' rows requested together, then accumulated in order
-      float x[8][ND], fj[8];
+    for (int j = 0; j < cn; j += CB) {
+      if (c0 + j > 0) request(c0 + j);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        fj[u] = __shfl(f, j + u, 64);
-        const int cc = min(c0 + j + u, a.nc - 1);
-        const float* po = part_o + ((base + cc) * kMaxRows + r) * D;
-#pragma unroll
-        for (int e = 0; e < ND; ++e) x[u][e] = po[lane + 64 * e];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < CB; ++u) {
+        const float fj = __shfl(f, j + u, 64);
         if (j + u < cn)
 #pragma unroll
-          for (int e = 0; e < ND; ++e) acc[e] += x[u][e] * fj[u];
+          for (int e = 0; e < ND; ++e) acc[e] += x[u][e] * fj;
+      }
     }
   }
   l = wave_sum(l);
@@ -315,7 +331,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char s_k[TILE_B];
   __shared__ __attribute__((aligned(1024))) unsigned char s_v[TILE_B];
   __shared__ int s_sel[kMaxTopK];
-  __shared__ int s_pos[kMaxTopK];
   __shared__ float s_ml[4][32][2];
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int bg = b * a.Hkv + g;
@@ -328,21 +343,17 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   const int32_t* hsel = sel + (size_t)bg * a.K;
   if (a.fused && c < a.nch_h) {
     const float* cs = cand_score + (size_t)bg * a.ncs * a.K;
-    if (wave == 0) {
-      if (a.m <= 64) wave_topk<1>(cs, a.m, a.K, s_pos, lane);
-      else if (a.m <= 128) wave_topk<2>(cs, a.m, a.K, s_pos, lane);
-      else if (a.m <= 256) wave_topk<4>(cs, a.m, a.K, s_pos, lane);
-      else if (a.m <= 512) wave_topk<8>(cs, a.m, a.K, s_pos, lane);
-      else wave_topk<16>(cs, a.m, a.K, s_pos, lane);
-    }
-    __syncthreads();
     const int32_t* ci = cand_idx + (size_t)bg * a.ncs * a.K;
-    for (int i = tid; i < a.K; i += 256) {
-      const int blk = ci[s_pos[i]];
-      s_sel[i] = blk;
-      if (c == 0) sel[(size_t)bg * a.K + i] = blk;
+    if (wave == 0) {  // the kept entries' block indices straight into s_sel
+      if (a.m <= 64) wave_topk<1>(cs, a.m, a.K, s_sel, lane, ci);
+      else if (a.m <= 128) wave_topk<2>(cs, a.m, a.K, s_sel, lane, ci);
+      else if (a.m <= 256) wave_topk<4>(cs, a.m, a.K, s_sel, lane, ci);
+      else if (a.m <= 512) wave_topk<8>(cs, a.m, a.K, s_sel, lane, ci);
+      else wave_topk<16>(cs, a.m, a.K, s_sel, lane, ci);
     }
     __syncthreads();
+    if (c == 0)
+      for (int i = tid; i < a.K; i += 256) sel[(size_t)bg * a.K + i] = s_sel[i];
     hsel = s_sel;
   }
 
@@ -553,7 +564,8 @@ DecPlan plan(const Prob& p, int pos, int n) {
   a.c2 = p.scale * kLog2e;
   a.fused = 0;
   a.ncs = decode_cand_slots(p);
-  a.m = (nb + 255) / 256 * p.K;
+  const int cpb = decode_scoring_block(p, nb);
+  a.m = (nb + cpb - 1) / cpb * p.K;
   d.R = p.G * n;
   return d;
 }
@@ -620,7 +632,9 @@ static size_t partial_floats(const Prob& p) {
   return (size_t)p.B * p.Hkv * max_chunks(p) * kMaxRows * (p.D + 2);
 }
 
-int decode_cand_slots(const Prob& p) { return (std::min(p.nblk, 1024) + 255) / 256; }
+int decode_cand_slots(const Prob& p) { return (std::min(p.nblk, 1024) + 127) / 128; }
+
+int decode_scoring_block(const Prob& p, int nb) { return (nb + 127) / 128 * p.K <= 1024 ? 128 : 256; }
 
 static size_t cand_entries(const Prob& p) {
   return (size_t)p.B * p.Hkv * decode_cand_slots(p) * p.K;
@@ -643,9 +657,9 @@ int32_t* decode_cand_idx_ws(const Prob& p, void* ws) {
   return reinterpret_cast<int32_t*>(decode_cand_score_ws(p, ws) + cand_entries(p));
 }
 
-// two-stage top-k: k < nb <= 1,024 history blocks (the scoring blocks hold
-// 256 candidates each), k <= 256 (one block's list), and at most 1,024
-// candidates left for the attention blocks' search
+// two-stage top-k: k < nb <= 1,024 history blocks, k <= 256 (one block's
+// list), and at most 1,024 candidates left for the attention blocks' search
+// (with 256-candidate scoring blocks at the most)
 bool decode_fused(const Prob& p, int pos, int n) {
   (void)n;
   const int nb = pos / p.L * p.L / p.Bh;

@@ -109,8 +109,12 @@ size_t bwd_exact_workspace_bytes(const Prob& p);
 // decode_fused: the scoring launch also keeps each of its blocks' k best
 // (score, index) pairs, and the history chunks of the attention launch pick
 // the k best of those lists themselves (so no top-k launch runs between).
+// decode_scoring_block: candidates per scoring block of a two-stage step
+// with nb history blocks (128, or 256 when 128-candidate lists would leave
+// more than 1,024 entries for the attention launch).
 bool decode_fused(const Prob& p, int pos, int n);
 int decode_cand_slots(const Prob& p);
+int decode_scoring_block(const Prob& p, int nb);
 float* decode_cand_score_ws(const Prob& p, void* ws);
 int32_t* decode_cand_idx_ws(const Prob& p, void* ws);
 hipError_t launch_select_decode(const Prob& p, const void* q_new, int n, int t0,

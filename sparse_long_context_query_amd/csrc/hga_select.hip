@@ -387,22 +387,23 @@ __global__ __launch_bounds__(kThreads) void select_multi_kernel(
 
 // ---------------------------------------------------------------------------
 // Selection of a decode step, which has a single unit per (b, g) but up to
-// 1,024 candidates: the scoring spreads over many CUs.  score_kernel: 256
-// candidates per block of threads (8 lanes per summary row, the scoring
+// 1,024 candidates: the scoring spreads over many CUs.  score_kernel: 128 or
+// 256 candidates per block of threads (8 lanes per summary row, the scoring
 // helper every selection kernel uses), writes the fp32 scores; topk_kernel:
 // one wave per (b, g) picks the k best (wave_topk), where the two-stage
 // form below does not apply.
 // ---------------------------------------------------------------------------
 //
-// With cand_score / cand_idx (the decode step's two-stage top-k), each block
-// also keeps the k best of its own 256 candidates (wave_topk, or all of them
+// A block scores CPB candidates (128 or 256: one row of 64 per wave).  With
+// cand_score / cand_idx (the decode step's two-stage top-k), each block
+// also keeps the k best of its own candidates (wave_topk, or all of them
 // when it has no more than k) as (score, block index) pairs, ascending in
 // block index, at slot blockIdx.x of its (b, g) row of cand_* (ncs slots of
 // k entries per row), padded with (-inf, -1).  The top-k of all candidates
 // is the top-k of these lists under the same (score desc, index asc) rule,
 // and blocks and entries follow the index order, so the decode attention
 // can finish the selection from at most ncs * k entries.
-template <typename T, int D>
+template <typename T, int D, int CPB>
 __global__ __launch_bounds__(kThreads) void score_kernel(
     const T* __restrict__ q, const float* __restrict__ summ, float* __restrict__ scores,
     SelGeom geo, int Hq, int Hkv, int G, int nblk, float* __restrict__ cand_score,
@@ -416,15 +417,16 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
   __shared__ int32_t s_pos[kThreads];
   const int g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int i = blockIdx.x * kThreads + threadIdx.x;
+  static_assert(CPB % 64 == 0 && CPB <= kThreads, "one row of 64 candidates per wave");
+  const int i = blockIdx.x * CPB + threadIdx.x;
   // the block's summary rows first (8 lanes per row), so that they overlap
-  // the query mean
-  const int row0 = blockIdx.x * kThreads + wave * 64;
+  // the query mean (which every wave helps with)
+  const int row0 = blockIdx.x * CPB + wave * 64;
+  const bool scoring = wave * 64 < CPB && row0 < geo.nb;  // uniform over the wave
   RowPieces<D> rp;
-  if (row0 < geo.nb) load_rows64<D>(rp, summ + (size_t)(b * Hkv + g) * nblk * D, row0, geo.nb,
-                                    lane);
+  if (scoring) load_rows64<D>(rp, summ + (size_t)(b * Hkv + g) * nblk * D, row0, geo.nb, lane);
   group_query_mean<T, D>(q, geo, b, g, 0, Hq, G, part, qbar);
-  if (row0 < geo.nb) {  // uniform over the wave
+  if (scoring) {
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const float s = row_score8<D>(rp, p, qbar, lane);
@@ -432,15 +434,14 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     }
   }
   __syncthreads();
-  const float sc = s_sc[threadIdx.x];
-  if (i < geo.nb) scores[(size_t)(b * Hkv + g) * nblk + i] = sc;
+  if (threadIdx.x < CPB && i < geo.nb) scores[(size_t)(b * Hkv + g) * nblk + i] = s_sc[threadIdx.x];
   if (cand_score == nullptr) return;
-  // the block's own k best (kThreads = 256 candidates: four per lane)
-  const int nbb = min(kThreads, geo.nb - (int)blockIdx.x * kThreads);
+  // the block's own k best (CPB / 64 candidates per lane)
+  const int nbb = min(CPB, geo.nb - (int)blockIdx.x * CPB);
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     if (nbb > K) {
-      wave_topk<kThreads / 64>(s_sc, nbb, K, s_pos, lane);
+      wave_topk<CPB / 64>(s_sc, nbb, K, s_pos, lane);
     } else {
       for (int t = lane; t < nbb; t += 64) s_pos[t] = t;
     }
@@ -451,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
   for (int t = threadIdx.x; t < K; t += kThreads) {
     const bool ok = t < kept;
     cand_score[row + t] = ok ? s_sc[s_pos[t]] : -INFINITY;
-    cand_idx[row + t] = ok ? (int)blockIdx.x * kThreads + s_pos[t] : -1;
+    cand_idx[row + t] = ok ? (int)blockIdx.x * CPB + s_pos[t] : -1;
   }
 }
 
@@ -624,26 +625,28 @@ hipError_t launch_select_decode(const Prob& p, const void* q_new, int n, int t0,
   const SelGeom geo{n, 0, 0, n, 1, 0, t0 / p.Bh, 0, 0, 0, 0};
   const int nb = geo.nb;
   if (nb <= p.K || nb > 1024) return select_any(p, q_new, summ, geo, 1, sel, st);
-  const dim3 grid((nb + kThreads - 1) / kThreads, p.Hkv, p.B);
+  // with the candidate lists (two-stage top-k) blocks of 128 candidates when
+  // their lists fit the attention launch's search, else of 256
+  const int cpb = cand_score != nullptr ? decode_scoring_block(p, nb) : kThreads;
+  const dim3 grid((nb + cpb - 1) / cpb, p.Hkv, p.B);
   const int ncs = decode_cand_slots(p);
+  auto go = [&](auto kern, auto qv) {
+    HGA_LAUNCH(HGA_K_SELECT, kern, grid, dim3(kThreads), 0, st, qv, summ, scores, geo, p.Hq,
+               p.Hkv, p.G, p.nblk, cand_score, cand_idx, p.K, ncs);
+  };
   if (p.dtype == HGA_BF16) {
+    const __bf16* qb = (const __bf16*)q_new;
     if (p.D == 64)
-      HGA_LAUNCH(HGA_K_SELECT, (score_kernel<__bf16, 64>), grid, dim3(kThreads), 0, st,
-                         (const __bf16*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk,
-                 cand_score, cand_idx, p.K, ncs);
+      cpb == 128 ? go(score_kernel<__bf16, 64, 128>, qb) : go(score_kernel<__bf16, 64, kThreads>, qb);
     else
-      HGA_LAUNCH(HGA_K_SELECT, (score_kernel<__bf16, 128>), grid, dim3(kThreads), 0, st,
-                         (const __bf16*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk,
-                 cand_score, cand_idx, p.K, ncs);
+      cpb == 128 ? go(score_kernel<__bf16, 128, 128>, qb)
+                 : go(score_kernel<__bf16, 128, kThreads>, qb);
   } else {
+    const float* qf = (const float*)q_new;
     if (p.D == 64)
-      HGA_LAUNCH(HGA_K_SELECT, (score_kernel<float, 64>), grid, dim3(kThreads), 0, st,
-                         (const float*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk,
-                 cand_score, cand_idx, p.K, ncs);
+      go(score_kernel<float, 64, kThreads>, qf);
     else
-      HGA_LAUNCH(HGA_K_SELECT, (score_kernel<float, 128>), grid, dim3(kThreads), 0, st,
-                         (const float*)q_new, summ, scores, geo, p.Hq, p.Hkv, p.G, p.nblk,
-                 cand_score, cand_idx, p.K, ncs);
+      go(score_kernel<float, 128, kThreads>, qf);
   }
   hipError_t e = hipGetLastError();
   // with the candidate lists the attention launch finishes the top-k

@@ -38,15 +38,22 @@ __device__ __forceinline__ uint32_t wave_kth_largest32(const uint32_t (&v)[E], i
 // multiplicity) by a bitwise search over the 32-bit score order held in its
 // registers, then keeps every score above thr and the lowest-index ties at
 // thr, compacting them in index order with ballots.  Called by the 64
-// threads of one wave; `score` may be in LDS or global memory.
+// threads of one wave; `score` may be in LDS or global memory.  With
+// `payload`, out receives payload[i] instead of each kept index i (its
+// entries are requested together with the scores).
 template <int E>
 __device__ __forceinline__ void wave_topk(const float* score, int nb, int K, int32_t* out,
-                                          int lane) {
+                                          int lane, const int32_t* payload = nullptr) {
   uint32_t v[E];
   float sv[E];
+  int32_t pv[E];
   // unconditional loads (index clamped) so that all E are in flight at once
 #pragma unroll
   for (int e = 0; e < E; ++e) sv[e] = score[min(64 * e + lane, nb - 1)];
+  if (payload != nullptr) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) pv[e] = payload[min(64 * e + lane, nb - 1)];
+  }
 #pragma unroll
   for (int e = 0; e < E; ++e) v[e] = 64 * e + lane < nb ? score_ord(sv[e]) : 0u;
   const uint32_t thr = wave_kth_largest32<E>(v, K);
@@ -64,7 +71,7 @@ __device__ __forceinline__ void wave_topk(const float* score, int nb, int K, int
     const unsigned long long meq = __ballot(eq);
     const bool take = (ok && v[e] > thr) || (eq && ties + __popcll(meq & below) < need);
     const unsigned long long m = __ballot(take);
-    if (take) out[count + __popcll(m & below)] = i;
+    if (take) out[count + __popcll(m & below)] = payload != nullptr ? pv[e] : i;
     count += __popcll(m);
     ties += __popcll(meq);
   }

@@ -159,9 +159,9 @@ def test_decode_step_validation(L):
     # per (b, g): 32 history chunks (k 32 x Bh 64 / 64) + 16 local chunks of
     # 64 keys, 64 query rows each, D + 2 floats per row; then one score per
     # history block; then the two-stage top-k's candidate lists, one slot of
-    # k (score, index) pairs per 256 history blocks
+    # k (score, index) pairs per 128 history blocks (256 blocks: 2 slots)
     assert ws == (1 * 8 * (32 + 16) * 64 * (128 + 2) * 4 + 1 * 8 * 256 * 4
-                  + 1 * 8 * 1 * 32 * (4 + 4))
+                  + 1 * 8 * 2 * 32 * (4 + 4))
 
     def call(pos, n, ws_bytes=ws, sel=FAKE):
         return L.hga_decode_step(ctypes.byref(cfg), pos, n, FAKE, FAKE, FAKE, FAKE, sel, FAKE,
