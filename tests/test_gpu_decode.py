@@ -148,8 +148,11 @@ def tied_score_inputs(shape, seed, nvalues):
 # (top-k, first new token, new tokens): 1,016 candidates (four scoring
 # blocks) with lists of 8 to 256, and 264 / 300 candidates, whose last
 # scoring block holds fewer than k and keeps them all
+# (top-k, first new token, new tokens): 1,016 history blocks with lists of 8
+# to 256 entries per scoring block; 264 and 300 blocks; 96 blocks (one
+# scoring block)
 TWO_STAGE_CASES = [(8, 16256, 1), (30, 16300, 4), (60, 16383, 1), (100, 16256, 16),
-                   (256, 16383, 1), (256, 4224, 2), (200, 4800, 1)]
+                   (256, 16383, 1), (256, 4224, 2), (200, 4800, 1), (8, 1650, 1), (30, 1650, 3)]
 
 
 @pytest.mark.parametrize("top_k,pos,n", TWO_STAGE_CASES)
