@@ -848,23 +848,32 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
 
 // ---------------------------------------------------------------------------
 // a8, bf16 MFMA, whole segmented pass: dk/dv of the local keys of segments
-// a.seg .. a.seg+a.nseg-1 in one launch.  A block of 4 waves owns 128
-// consecutive keys of one (segment, b, g); wave w owns keys k0+32w .. +31,
+// a.seg .. a.seg+a.nseg-1 in one launch.  A block of 4 waves takes two key
+// blocks of 128 consecutive keys of one (segment, b, g), kb and its mirror
+// nkb-1-kb, one after the other; for each, wave w owns keys k0+32w .. +31,
 // holds their K rows in registers (B operand of S = Q.K^T), their V rows in
 // LDS (B operand of dP = dO.V^T) and their dK^T, dV^T accumulators.  The
-// block walks the (32-query tile, head) pairs that can see its keys --
-// query tiles from the block's first key on, every head of the group -- and
-// copies each pair's Q and dO tiles (with lse and delta) into LDS once for
-// its 4 waves, double-buffered so that the next pair's copies land while
-// the current one is computed.  Per wave and pair, with the products of
+// block walks the (32-query tile, head) pairs that can see the key block --
+// query tiles from its first key on, every head of the group -- and copies
+// each pair's Q and dO tiles (with lse and delta) into LDS once for its 4
+// waves, double-buffered so that the next pair's copies land while the
+// current one is computed.  Per wave and pair, with the products of
 // dkdv_item:
 //   S = Q.K^T, dP = dO.V^T,  P = exp2(S c2 - lse2), dS = P (dP - delta)
 //   dV^T += dO^T.P,  dK^T += Q^T.dS      (transposed reads of the Q, dO tiles)
 // Each key has one owner, so its dK, dV rows are written directly (plus,
 // for the exact gradient, the fp32 sums a.hdk / a.hdv that later segments'
-// queries left in those rows).  Key block kb sees about nqt - 4kb query tiles; blocks run from the first key
-// block to the last (the most pairs first), segments innermost, so the
-// launch ends on short blocks.
+// queries left in those rows).
+//
+// Work order: key block kb sees nqt - 4kb query tiles (32-row tiles, L/32
+// of them), so the pair kb, nkb-1-kb gives every block the same work.  The
+// blocks of one (segment, b, g) are consecutive, so they run together on
+// one XCD, and they read the same Q/dO tiles at the same time: the first
+// key block walks its query tiles from the last down (tile nqt-1-t at step
+// t in every block), the second from its first tile up, which every block
+// reaches at the same step (tile t - nqt/8 at step t for L = 1024).  Each
+// tile is thus read from memory about once per direction, and the L2
+// serves the other blocks.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void dkdv_pass_kernel(
@@ -884,190 +893,208 @@ __global__ __launch_bounds__(256, 2) void dkdv_pass_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char s_stage[2][STAGE_B];
 
   const int nkb = (a.L + KB - 1) / KB;
+  const int nbpg = (nkb + 1) / 2;  // blocks per (segment, b, g)
   int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int pr = w % nbpg;
+  w /= nbpg;
   const int sg = a.nseg - 1 - w % a.nseg;
   w /= a.nseg;
-  const int kb = w % nkb;
-  w /= nkb;
   const int g = w % a.Hkv;
   const int b = w / a.Hkv;
   const int seg = a.seg + sg;
   const int t0 = seg * a.L, tend = t0 + a.L;
-  const int k0 = t0 + kb * KB;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
+  const int lane_id = tid & 63;
   const size_t kv_base = (size_t)(b * a.Hkv + g) * a.S * D;
   const float* dlt = delta + (size_t)sg * a.dchunk;
-
-  // keys of this wave; rows past the segment end read the last row (masked)
-  const int kfirst = k0 + 32 * wave;
-  const int nkey = max(0, min(32, tend - kfirst));
-  const int tk = kfirst + lq;
-  const bool key_ok = lq < nkey;
-  const int nkey_blk = min(KB, tend - k0);
-  // V rows of the block's keys into LDS (4 waves x 8 instructions)
-  {
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(v + kv_base + (size_t)k0 * D, (uint32_t)nkey_blk * (2 * D));
-#pragma unroll
-    for (int n = 0; n < KB / RPI / 4; ++n) {
-      const int i = wave + 4 * n;
-      const int row = i * RPI + lane / CPR;
-      const int c = (lane % CPR) ^ swz<D>(row);
-      const int rr = row < nkey_blk ? row : nkey_blk - 1;
-      buffer_to_lds16(r, (uint32_t)rr * (2 * D) + c * 16, s_v + i * 1024);
-    }
-  }
-  // K rows of this wave's keys as B operands: lane (key lq, hi) holds
-  // K[key][16kk + 8hi .. +7]
-  bf16x8 kreg[NKK];
-  {
-    const int krow = key_ok ? tk : (nkey > 0 ? kfirst : tend - 1);
-    const __bf16* kp = k + kv_base + (size_t)krow * D + 8 * hi;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) kreg[kk] = *reinterpret_cast<const bf16x8*>(kp + 16 * kk);
-  }
-
   const int nqt = (a.L + TQ - 1) / TQ;
-  const int qt0 = (kb * KB) / TQ;        // first query tile that sees any key
-  const int npairs = (nqt - qt0) * a.G;
-  // copies of pair pi's tiles (every wave a quarter of Q and dO; waves 0 / 1
-  // the lse / delta of its 32 queries) into stage buffer `st`
-  auto stage_pair = [&](int pi, int st) __attribute__((always_inline)) {
-    const bool ok = pi < npairs;
-    const int pc = ok ? pi : 0;
-    const int qt = qt0 + pc / a.G, h = g * a.G + pc % a.G;
-    const int tq0 = t0 + qt * TQ;
-    const int nval = min(TQ, tend - tq0);
-    const size_t hrow = (size_t)(b * a.Hq + h) * a.S;
-    const uint32_t nb = ok ? (uint32_t)nval * (2 * D) : 0u;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + (hrow + tq0) * D, nb);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dO + (hrow + tq0) * D, nb);
-    unsigned char* sq = s_stage[st];
-    unsigned char* sd = sq + TILE_B;
-#pragma unroll
-    for (int n = 0; n < TQ / RPI / 4; ++n) {
-      const int i = wave + 4 * n;
-      const int row = i * RPI + lane / CPR;
-      const int c = (lane % CPR) ^ swz<D>(row);
-      const int rr = row < nval ? row : nval - 1;
-      buffer_to_lds16(rq, (uint32_t)rr * (2 * D) + c * 16, sq + i * 1024);
-      buffer_to_lds16(rd, (uint32_t)rr * (2 * D) + c * 16, sd + i * 1024);
-    }
-    if (wave < 2) {
-      const float* base = wave == 0 ? lse + hrow + tq0
-                                    : dlt + (size_t)(b * a.Hq + h) * a.L + (tq0 - t0);
-      const __amdgpu_buffer_rsrc_t rl = make_rsrc(base, ok ? (uint32_t)nval * 4u : 0u);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, to_lds(sq + 2 * TILE_B + wave * 256), 4,
-                                               (int)((lane & 31) * 4), 0, 0, 0);
-    }
-  };
-
-  floatx16 dkacc[NDB], dvacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) { dkacc[db] = floatx16{}; dvacc[db] = floatx16{}; }
   FragOffsets<D> fo;
-  fo.init(lane);
+  fo.init(lane_id);
   const unsigned char* vt = s_v + wave * 32 * (2 * D);
 
-  stage_pair(0, 0);
-  drain_vmem_loads();
-  __syncthreads();
-
-  for (int pi = 0; pi < npairs; ++pi) {
-    stage_pair(pi + 1, (pi + 1) & 1);
-    const int qt = qt0 + pi / a.G;
-    const int tq0 = t0 + qt * TQ;
-    const int nval = min(TQ, tend - tq0);
-    // a wave whose keys all come after the tile's queries has nothing to do
-    if (nkey > 0 && tq0 + TQ - 1 >= kfirst) {
-      const unsigned char* sq = s_stage[pi & 1];
-      const unsigned char* sd = sq + TILE_B;
-      const float* sl = reinterpret_cast<const float*>(sq + 2 * TILE_B);
-      floatx16 sacc = floatx16{}, pacc = floatx16{};
+  // key block pr, its query tiles from the last down, then key block
+  // nkb-1-pr, its query tiles from the first up (nothing more for the middle
+  // block of an odd nkb)
+  const int nphase = nkb - 1 - pr != pr ? 2 : 1;
+  for (int ph = 0; ph < nphase; ++ph) {
+    // the lane index, opaque to the compiler, so that the offsets derived
+    // from it are recomputed per key block rather than held through the
+    // pair loop
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    const int lq = lane & 31, hi = lane >> 5;
+    const int kb = ph == 0 ? pr : nkb - 1 - pr;
+    const bool down = ph == 0;
+    const int k0 = t0 + kb * KB;
+    // keys of this wave; rows past the segment end read the last row (masked)
+    const int kfirst = k0 + 32 * wave;
+    const int nkey = max(0, min(32, tend - kfirst));
+    const int tk = kfirst + lq;
+    const bool key_ok = lq < nkey;
+    const int nkey_blk = min(KB, tend - k0);
+    if (ph > 0) __syncthreads();  // every wave is done with the first key block's tiles
+    // V rows of the block's keys into LDS (4 waves x 8 instructions)
+    {
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc(v + kv_base + (size_t)k0 * D, (uint32_t)nkey_blk * (2 * D));
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        sacc = mfma32(fo.row(sq, 0, kk), kreg[kk], sacc);
-        pacc = mfma32(fo.row(sd, 0, kk), fo.row(vt, 0, kk), pacc);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int u = 0; u < 2 * NKK - 2; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      // C layout: lane = key lq, item r = query row 8(r/4)+4hi+(r%4) of the tile
-      const bool need_mask = (tq0 < kfirst + 31) || (nval < TQ) || (nkey < 32);
-      float pv[16];
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const float4 l4 = *reinterpret_cast<const float4*>(&sl[8 * r4 + 4 * hi]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pv[4 * r4 + e] = fast_exp2(fmaf(sacc[4 * r4 + e], a.c2, -lv[e] * kLog2e));
-      }
-      if (need_mask) {
-        // kept a branch (a fence with side effects): only diagonal and
-        // ragged pairs need it
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 8 * (r >> 2) + 4 * hi + (r & 3);
-          pv[r] = (key_ok && row < nval && tk <= tq0 + row) ? pv[r] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {  // dS
-        const float4 d4 = *reinterpret_cast<const float4*>(&sl[64 + 8 * r4 + 4 * hi]);
-        const float dv_[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sacc[4 * r4 + e] = pv[4 * r4 + e] * (pacc[4 * r4 + e] - dv_[e]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int r0 = 8 * ks;
-        const bf16x8 pb = to_bf16x8(pv[r0], pv[r0 + 1], pv[r0 + 2], pv[r0 + 3], pv[r0 + 4],
-                                    pv[r0 + 5], pv[r0 + 6], pv[r0 + 7]);
-        const bf16x8 sb = to_bf16x8(sacc[r0], sacc[r0 + 1], sacc[r0 + 2], sacc[r0 + 3],
-                                    sacc[r0 + 4], sacc[r0 + 5], sacc[r0 + 6], sacc[r0 + 7]);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dvacc[db] = mfma32(fo.tr(sd, 16 * ks, db), pb, dvacc[db]);
-          dkacc[db] = mfma32(fo.tr(sq, 16 * ks, db), sb, dkacc[db]);
-        }
+      for (int n = 0; n < KB / RPI / 4; ++n) {
+        const int i = wave + 4 * n;
+        const int row = i * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ swz<D>(row);
+        const int rr = row < nkey_blk ? row : nkey_blk - 1;
+        buffer_to_lds16(r, (uint32_t)rr * (2 * D) + c * 16, s_v + i * 1024);
       }
     }
-    drain_vmem_loads();  // the next pair's tiles have landed
+    // K rows of this wave's keys as B operands: lane (key lq, hi) holds
+    // K[key][16kk + 8hi .. +7]
+    bf16x8 kreg[NKK];
+    {
+      const int krow = key_ok ? tk : (nkey > 0 ? kfirst : tend - 1);
+      const __bf16* kp = k + kv_base + (size_t)krow * D + 8 * hi;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) kreg[kk] = *reinterpret_cast<const bf16x8*>(kp + 16 * kk);
+    }
+
+    const int qt0 = (kb * KB) / TQ;        // first query tile that sees any key
+    const int npairs = (nqt - qt0) * a.G;
+    auto tile_of = [&](int pi) { return down ? nqt - 1 - pi / a.G : qt0 + pi / a.G; };
+    // copies of pair pi's tiles (every wave a quarter of Q and dO; waves 0 / 1
+    // the lse / delta of its 32 queries) into stage buffer `st`
+    auto stage_pair = [&](int pi, int st) __attribute__((always_inline)) {
+      const bool ok = pi < npairs;
+      const int pc = ok ? pi : 0;
+      const int qt = tile_of(pc), h = g * a.G + pc % a.G;
+      const int tq0 = t0 + qt * TQ;
+      const int nval = min(TQ, tend - tq0);
+      const size_t hrow = (size_t)(b * a.Hq + h) * a.S;
+      const uint32_t nb = ok ? (uint32_t)nval * (2 * D) : 0u;
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + (hrow + tq0) * D, nb);
+      const __amdgpu_buffer_rsrc_t rd = make_rsrc(dO + (hrow + tq0) * D, nb);
+      unsigned char* sq = s_stage[st];
+      unsigned char* sd = sq + TILE_B;
+#pragma unroll
+      for (int n = 0; n < TQ / RPI / 4; ++n) {
+        const int i = wave + 4 * n;
+        const int row = i * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ swz<D>(row);
+        const int rr = row < nval ? row : nval - 1;
+        buffer_to_lds16(rq, (uint32_t)rr * (2 * D) + c * 16, sq + i * 1024);
+        buffer_to_lds16(rd, (uint32_t)rr * (2 * D) + c * 16, sd + i * 1024);
+      }
+      if (wave < 2) {
+        const float* base = wave == 0 ? lse + hrow + tq0
+                                      : dlt + (size_t)(b * a.Hq + h) * a.L + (tq0 - t0);
+        const __amdgpu_buffer_rsrc_t rl = make_rsrc(base, ok ? (uint32_t)nval * 4u : 0u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, to_lds(sq + 2 * TILE_B + wave * 256), 4,
+                                                 (int)((lane & 31) * 4), 0, 0, 0);
+      }
+    };
+
+    floatx16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) { dkacc[db] = floatx16{}; dvacc[db] = floatx16{}; }
+
+    stage_pair(0, 0);
+    drain_vmem_loads();
     __syncthreads();
-  }
 
-  if (!key_ok) return;
+    for (int pi = 0; pi < npairs; ++pi) {
+      stage_pair(pi + 1, (pi + 1) & 1);
+      const int tq0 = t0 + tile_of(pi) * TQ;
+      const int nval = min(TQ, tend - tq0);
+      // a wave whose keys all come after the tile's queries has nothing to do
+      if (nkey > 0 && tq0 + TQ - 1 >= kfirst) {
+        const unsigned char* sq = s_stage[pi & 1];
+        const unsigned char* sd = sq + TILE_B;
+        const float* sl = reinterpret_cast<const float*>(sq + 2 * TILE_B);
+        floatx16 sacc = floatx16{}, pacc = floatx16{};
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+        for (int kk = 0; kk < NKK; ++kk) {
+          sacc = mfma32(fo.row(sq, 0, kk), kreg[kk], sacc);
+          pacc = mfma32(fo.row(sd, 0, kk), fo.row(vt, 0, kk), pacc);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d = 32 * db + 8 * r4 + 4 * hi;
-      const size_t off = kv_base + (size_t)tk * D + d;
-      float4 hk = make_float4(0.f, 0.f, 0.f, 0.f), hv = hk;
-      if (a.hdk != nullptr) {
-        hk = *reinterpret_cast<const float4*>(a.hdk + off);
-        hv = *reinterpret_cast<const float4*>(a.hdv + off);
+        for (int u = 0; u < 2 * NKK - 2; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        // C layout: lane = key lq, item r = query row 8(r/4)+4hi+(r%4) of the tile
+        const bool need_mask = (tq0 < kfirst + 31) || (nval < TQ) || (nkey < 32);
+        float pv[16];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(&sl[8 * r4 + 4 * hi]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pv[4 * r4 + e] = fast_exp2(fmaf(sacc[4 * r4 + e], a.c2, -lv[e] * kLog2e));
+        }
+        if (need_mask) {
+          // kept a branch (a fence with side effects): only diagonal and
+          // ragged pairs need it
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * hi + (r & 3);
+            pv[r] = (key_ok && row < nval && tk <= tq0 + row) ? pv[r] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {  // dS
+          const float4 d4 = *reinterpret_cast<const float4*>(&sl[64 + 8 * r4 + 4 * hi]);
+          const float dv_[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sacc[4 * r4 + e] = pv[4 * r4 + e] * (pacc[4 * r4 + e] - dv_[e]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int r0 = 8 * ks;
+          const bf16x8 pb = to_bf16x8(pv[r0], pv[r0 + 1], pv[r0 + 2], pv[r0 + 3], pv[r0 + 4],
+                                      pv[r0 + 5], pv[r0 + 6], pv[r0 + 7]);
+          const bf16x8 sb = to_bf16x8(sacc[r0], sacc[r0 + 1], sacc[r0 + 2], sacc[r0 + 3],
+                                      sacc[r0 + 4], sacc[r0 + 5], sacc[r0 + 6], sacc[r0 + 7]);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            dvacc[db] = mfma32(fo.tr(sd, 16 * ks, db), pb, dvacc[db]);
+            dkacc[db] = mfma32(fo.tr(sq, 16 * ks, db), sb, dkacc[db]);
+          }
+        }
       }
-      const bf16x4 ko = {(__bf16)(dkacc[db][4 * r4] * a.scale + hk.x),
-                         (__bf16)(dkacc[db][4 * r4 + 1] * a.scale + hk.y),
-                         (__bf16)(dkacc[db][4 * r4 + 2] * a.scale + hk.z),
-                         (__bf16)(dkacc[db][4 * r4 + 3] * a.scale + hk.w)};
-      const bf16x4 vo = {(__bf16)(dvacc[db][4 * r4] + hv.x), (__bf16)(dvacc[db][4 * r4 + 1] + hv.y),
-                         (__bf16)(dvacc[db][4 * r4 + 2] + hv.z),
-                         (__bf16)(dvacc[db][4 * r4 + 3] + hv.w)};
-      *reinterpret_cast<bf16x4*>(dk + off) = ko;
-      *reinterpret_cast<bf16x4*>(dv + off) = vo;
+      drain_vmem_loads();  // the next pair's tiles have landed
+      __syncthreads();
     }
+
+    if (key_ok) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = 32 * db + 8 * r4 + 4 * hi;
+          const size_t off = kv_base + (size_t)tk * D + d;
+          float4 hk = make_float4(0.f, 0.f, 0.f, 0.f), hv = hk;
+          if (a.hdk != nullptr) {
+            hk = *reinterpret_cast<const float4*>(a.hdk + off);
+            hv = *reinterpret_cast<const float4*>(a.hdv + off);
+          }
+          const bf16x4 ko = {(__bf16)(dkacc[db][4 * r4] * a.scale + hk.x),
+                             (__bf16)(dkacc[db][4 * r4 + 1] * a.scale + hk.y),
+                             (__bf16)(dkacc[db][4 * r4 + 2] * a.scale + hk.z),
+                             (__bf16)(dkacc[db][4 * r4 + 3] * a.scale + hk.w)};
+          const bf16x4 vo = {(__bf16)(dvacc[db][4 * r4] + hv.x),
+                             (__bf16)(dvacc[db][4 * r4 + 1] + hv.y),
+                             (__bf16)(dvacc[db][4 * r4 + 2] + hv.z),
+                             (__bf16)(dvacc[db][4 * r4 + 3] + hv.w)};
+          *reinterpret_cast<bf16x4*>(dk + off) = ko;
+          *reinterpret_cast<bf16x4*>(dv + off) = vo;
+        }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1449,7 +1476,7 @@ hipError_t bwd_pass_bf16(const Prob& p, const void* q, const void* k, const void
   a.hdv = const_cast<float*>(hdv);
   {
     const int nkb = (p.L + 127) / 128;
-    const int nblocks = p.B * p.Hkv * nkb * nseg;
+    const int nblocks = p.B * p.Hkv * nseg * ((nkb + 1) / 2);
     HGA_LAUNCH(HGA_K_BWD_DKDV, (dkdv_pass_kernel<D>), dim3(nblocks), dim3(256), 0, st,
                (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dO,
                delta, (__bf16*)dk, (__bf16*)dv, a);
