@@ -617,10 +617,18 @@ def cpu_baseline(inp, shape, budget_s):
     t_full = elapsed / frac
     del np
     ngroups = len({(b, g) for b, g, _ in done})
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         "")
+    except OSError:
+        pass
     return {
         "value": shape.batch * shape.seq_len / t_full,
         "unit": "tokens/s",
         "cores": int(threads),
+        "cpu_model": model,
         "kind": "oracle",
         "sample": (f"fp64 numpy oracle, fwd{'+bwd' if shape.bwd else ''} of {len(done)} "
                    f"(segment, sequence, KV head) groups over {ngroups} KV heads, segment "
@@ -1020,6 +1028,12 @@ def main():
     if not args.no_dense_sdpa:
         log("[bench] torch SDPA dense causal comparator")
         extras.update(dense_sdpa(dev, shape, bwd, ms))
+    if bwd:
+        # the forward on its own (summaries, selection, forward: no dO, so no
+        # row sums for the backward either)
+        fms = event_timed(lambda: buf.run_pass(dev["q"], dev["k"], dev["v"], None, bwd=False),
+                          args.steps, 3)
+        extras["fwd_only_ms_per_pass"] = round(fms, 4)
     if not args.no_diverse and args.mode == "planted":
         # the same pass on inputs whose query blocks pick different history
         # sets (less reuse of K/V tiles across blocks); throughput only
@@ -1042,6 +1056,11 @@ def main():
         extras["workloads"] = {}
         for wname in ("infer_131k", "batch4_32k"):
             extras["workloads"][wname] = workload_bench(wname, max(3, args.steps // 4), 2)
+        if not args.no_dense_sdpa:
+            log("[bench] HGA against dense attention at 2K and 131K")
+            extras["dense_by_length"] = dense_by_length(
+                ms if bwd else None, extras.get("dense_sdpa_flash_ms"),
+                extras["workloads"]["infer_131k"]["ms_per_pass"])
     if not args.no_exact and bwd and shape.dtype == "bf16":
         log("[bench] exact-gradient pass")
         extras["exact_gradient"] = exact_bench(shape, dev, max(3, args.steps // 4), 1)
@@ -1143,6 +1162,47 @@ def measured_peaks(steps=20):
     del src, dst
     return {"bf16_gemm_tflops": round(gemm_tflops, 1), "gemm": f"torch.mm bf16 {n}^3",
             "copy_gbs": round(copy_gbs, 1), "copy": "1 GiB device-to-device, read + written"}
+
+
+def dense_by_length(hga_16k_ms, sdpa_16k_ms, hga_131k_fwd_ms):
+    """HGA against dense causal attention (torch SDPA, flash backend) as the
+    sequence grows: the 2K training workload (fwd + bwd, both timed here),
+    the 16K headline (the figures above) and the 131K inference workload
+    (forward only; the HGA figure is its pass, the dense one runs on
+    N(0,1) tensors of the same shape, its cost not depending on the
+    values)."""
+    import torch
+    import sparse_long_context_query_amd as hga
+    from synth import WORKLOADS, make_inputs
+    out = {}
+    shape = WORKLOADS["qwen3_2k"]
+    inp = make_inputs(shape, seed=0)
+    dev = {k: torch.from_numpy(inp[k]).cuda().to(torch.bfloat16) for k in ("q", "k", "v", "do")}
+    buf = hga.Buffers(hga.Config.from_shape(shape))
+    h2 = event_timed(lambda: buf.run_pass(dev["q"], dev["k"], dev["v"], dev["do"]), 20, 5)
+    d2 = dense_sdpa(dev, shape, True, h2)
+    out["2k_fwd_bwd"] = {"hga_ms": round(h2, 4), "dense_sdpa_flash_ms": d2["dense_sdpa_flash_ms"],
+                         "dense_over_hga": d2.get("speedup_vs_dense_sdpa")}
+    del buf, dev
+    if hga_16k_ms and sdpa_16k_ms:
+        out["16k_fwd_bwd"] = {"hga_ms": round(hga_16k_ms, 4), "dense_sdpa_flash_ms": sdpa_16k_ms,
+                              "dense_over_hga": round(sdpa_16k_ms / hga_16k_ms, 2)}
+    shape = WORKLOADS["infer_131k"]
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    qs = (shape.batch, shape.n_q_heads, shape.seq_len, shape.head_dim)
+    ks = (shape.batch, shape.n_kv_heads, shape.seq_len, shape.head_dim)
+    dev = {"q": torch.randn(qs, generator=gen, device="cuda").to(torch.bfloat16),
+           "k": torch.randn(ks, generator=gen, device="cuda").to(torch.bfloat16),
+           "v": torch.randn(ks, generator=gen, device="cuda").to(torch.bfloat16)}
+    d131 = dense_sdpa(dev, shape, False, hga_131k_fwd_ms)
+    out["131k_fwd"] = {"hga_ms": round(hga_131k_fwd_ms, 4),
+                       "dense_sdpa_flash_ms": d131["dense_sdpa_flash_ms"],
+                       "dense_over_hga": d131.get("speedup_vs_dense_sdpa")}
+    if d131.get("dense_sdpa_error"):
+        out["131k_fwd"]["dense_sdpa_error"] = d131["dense_sdpa_error"]
+    del dev
+    torch.cuda.empty_cache()
+    return out
 
 
 def dense_sdpa(dev, shape, bwd, hga_ms):
