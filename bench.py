@@ -196,6 +196,25 @@ def timed_passes(buf, dev, bwd, n, profile_classes=None, two_streams=True):
     return start.elapsed_time(end) / n, prof
 
 
+def single_passes(buf, dev, bwd, n, two_streams=True):
+    """Median, minimum and maximum of n passes, each timed between its own
+    pair of events on the current stream."""
+    import statistics
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        buf.run_pass(dev["q"], dev["k"], dev["v"], dev.get("do"), bwd=bwd,
+                     two_streams=two_streams)
+        b.record()
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in evs]
+    return {"median_ms": round(statistics.median(t), 4), "min_ms": round(min(t), 4),
+            "max_ms": round(max(t), 4), "passes": n}
+
+
 def exact_bench(shape, dev, steps, warmup):
     """The exact-gradient pass (hga_segment_pass_exact): summaries, selection
     and forward of every segment, then every segment's queries (last
@@ -974,6 +993,9 @@ def main():
     # value: K passes (hga_segment_pass), nothing profiled
     log(f"[bench] timing {args.steps} passes ({args.streams} stream(s))")
     ms, _ = timed_passes(buf, dev, bwd, args.steps, two_streams=args.streams == 2)
+    # the same passes one by one, each between its own pair of events: the
+    # median and the spread of single passes (ms_per_step stays the loop's)
+    per_pass = single_passes(buf, dev, bwd, args.steps, two_streams=args.streams == 2)
     # kernel times: a second loop of K one-stream passes in which every
     # kernel's own dispatch stamps HIP start / stop events (the stamps add a
     # little idle time between kernels, so the pass time above never comes
@@ -1083,6 +1105,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "single_pass_ms": per_pass,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

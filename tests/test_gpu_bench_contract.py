@@ -38,6 +38,9 @@ def test_bench_prints_one_contract_line():
     assert d["dtype"] == "bf16" and d["config"]["workload"] == "train_16k"
     # whole-job throughput: the 16,384 tokens of one pass over its time
     assert d["value"] == pytest.approx(16384 / (d["ms_per_step"] * 1e-3), rel=1e-3)
+    sp = d["single_pass_ms"]
+    assert sp["passes"] == 3 and sp["min_ms"] <= sp["median_ms"] <= sp["max_ms"]
+    assert sp["median_ms"] == pytest.approx(d["ms_per_step"], rel=0.25)
     rf = d["roofline"]
     assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 2500.0
     assert 0 < rf["achieved"] < rf["peak"]
