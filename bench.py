@@ -1135,6 +1135,10 @@ def main():
                        f"stamps); kernels_ms_per_pass averages the same loop"),
         },
     }
+    props = torch.cuda.get_device_properties(0)
+    out["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                     "compute_units": props.multi_processor_count,
+                     "memory_gib": round(props.total_memory / 2**30, 1)}
     out.update(extras)
     if not args.no_peaks:
         log("[bench] measured peaks (bf16 GEMM, device copy)")

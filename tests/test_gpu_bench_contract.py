@@ -36,6 +36,7 @@ def test_bench_prints_one_contract_line():
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
     assert d["unit"] == "tokens/s" and d["higher_is_better"] is True
     assert d["dtype"] == "bf16" and d["config"]["workload"] == "train_16k"
+    assert d["device"]["compute_units"] > 0 and "gfx950" in d["device"]["arch"]
     # whole-job throughput: the 16,384 tokens of one pass over its time
     assert d["value"] == pytest.approx(16384 / (d["ms_per_step"] * 1e-3), rel=1e-3)
     sp = d["single_pass_ms"]
