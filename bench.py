@@ -1080,9 +1080,13 @@ def main():
             extras["workloads"][wname] = workload_bench(wname, max(3, args.steps // 4), 2)
         if not args.no_dense_sdpa:
             log("[bench] HGA against dense attention at 2K and 131K")
-            extras["dense_by_length"] = dense_by_length(
-                ms if bwd else None, extras.get("dense_sdpa_flash_ms"),
-                extras["workloads"]["infer_131k"]["ms_per_pass"])
+            try:
+                extras["dense_by_length"] = dense_by_length(
+                    ms if bwd else None, extras.get("dense_sdpa_flash_ms"),
+                    extras["workloads"]["infer_131k"]["ms_per_pass"])
+            except Exception as ex:  # noqa: BLE001 -- a comparator, never the result
+                extras["dense_by_length"] = {"error": str(ex)[:200]}
+                torch.cuda.empty_cache()
     if not args.no_exact and bwd and shape.dtype == "bf16":
         log("[bench] exact-gradient pass")
         extras["exact_gradient"] = exact_bench(shape, dev, max(3, args.steps // 4), 1)
