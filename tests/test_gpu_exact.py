@@ -72,6 +72,7 @@ EXACT_SHAPES = [
     shp(hist_block=16, query_block=16, top_k=5),                # 16-row blocks (half tiles)
     shp(hist_block=64, query_block=64, top_k=2, n_q_heads=16),  # 2 key tiles per block, G = 8
     shp(head_dim=64, seq_len=384, seg_len=96, hist_block=48, query_block=48, top_k=2),
+    shp(head_dim=64, seq_len=768, seg_len=256, hist_block=64, query_block=64, top_k=2),
     shp(batch=2, seq_len=256, n_q_heads=2, n_kv_heads=2, top_k=2),  # G = 1, batch 2
     shp(seq_len=128, seg_len=128),                              # one segment: no history
 ]

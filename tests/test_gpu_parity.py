@@ -73,6 +73,7 @@ def test_workload_pass_full_parity(name):
     shp(seq_len=1024, seg_len=256, hist_block=16, query_block=64, top_k=24),  # many candidates
     shp(seq_len=1152, seg_len=384, hist_block=64, query_block=64, top_k=3),  # 3 key blocks
     shp(seq_len=960, seg_len=320, top_k=4),                    # 3 key blocks, last one ragged
+    shp(head_dim=64, seq_len=1152, seg_len=384, hist_block=64, query_block=64, top_k=2),  # D=64
     shp(dtype="f32", head_dim=64, n_q_heads=4, n_kv_heads=2),
     shp(dtype="f32", head_dim=128, query_block=16, hist_block=8, top_k=5, seq_len=256),
 ])
