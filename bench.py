@@ -74,6 +74,8 @@ def parse():
                     help="skip the exact-gradient (history not detached) pass timing")
     ap.add_argument("--no-tier-131k", action="store_true",
                     help="skip the host-tier pass at the 131K inference shape")
+    ap.add_argument("--no-fwd-only", action="store_true",
+                    help="skip the forward-only pass timing (fwd_only_ms_per_pass)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured bf16 GEMM and copy rates (measured_peaks)")
     ap.add_argument("--no-hbm", action="store_true",
@@ -1050,7 +1052,7 @@ def main():
     if not args.no_dense_sdpa:
         log("[bench] torch SDPA dense causal comparator")
         extras.update(dense_sdpa(dev, shape, bwd, ms))
-    if bwd:
+    if bwd and not args.no_fwd_only:
         # the forward on its own (summaries, selection, forward: no dO, so no
         # row sums for the backward either)
         fms = event_timed(lambda: buf.run_pass(dev["q"], dev["k"], dev["v"], None, bwd=False),

@@ -292,7 +292,8 @@ int hga_segment_pass_noalloc(const hga_config* cfg, int32_t flags, const void* q
  * Requirements: bf16 (else HGA_ERR_UNSUPPORTED); L/Bq <= 64 and
  * (L/Bq)*k <= 8192 (else HGA_ERR_UNSUPPORTED).  ws:
  * hga_workspace_size(cfg, HGA_OP_PASS_EXACT) bytes (every segment's delta
- * rows, the fp32 history sums of dK and dV, the history block list).
+ * rows, the fp32 history sums of dK and dV, every segment's history block
+ * list).
  * Results are deterministic (every sum has one writer at a time; no
  * atomics on floats). */
 int hga_segment_pass_exact(const hga_config* cfg, const void* q, const void* k, const void* v,

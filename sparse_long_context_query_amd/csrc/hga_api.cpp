@@ -167,10 +167,11 @@ size_t pass_workspace_bytes(const hga::Prob& p) {
 }
 
 // Workspace of hga_segment_pass_exact: every segment's delta rows, the fp32
-// history sums of dK and dV ([B, Hkv, S, D] each), the history block list.
+// history sums of dK and dV ([B, Hkv, S, D] each), every segment's history
+// block list.
 size_t pass_exact_workspace_bytes(const hga::Prob& p) {
   const size_t sums = round256((size_t)p.B * p.Hkv * p.S * p.D * sizeof(float));
-  return (size_t)(p.S / p.L) * hga::bwd_delta_bytes(p) + 2 * sums + hga::hist_ws_bytes(p);
+  return (size_t)(p.S / p.L) * hga::bwd_delta_bytes(p) + 2 * sums + hga::hist_lists_bytes(p);
 }
 
 }  // namespace
@@ -873,6 +874,9 @@ int hga_segment_pass_exact(const hga_config* cfg, const void* q, const void* k, 
   // blocks they selected, from the last segment to the first (a fixed order)
   if ((e = hga::launch_zero(hist_dk, nsum, st)) != hipSuccess) return hip_fail(e, "zero launch");
   if ((e = hga::launch_zero(hist_dv, nsum, st)) != hipSuccess) return hip_fail(e, "zero launch");
+  // every segment's list of selected blocks in one launch
+  if ((e = hga::launch_hist_lists(p, sel, list_ws, st)) != hipSuccess)
+    return hip_fail(e, "history list launch");
   for (int seg = nseg - 1; seg >= 1; --seg) {
     e = hga::launch_hist_exact(p, q, k, v, lse, dO, sel, seg,
                                (const float*)((const char*)delta + (size_t)seg * dstride),

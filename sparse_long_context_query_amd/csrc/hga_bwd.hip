@@ -1116,18 +1116,26 @@ struct HistEntry {
 };
 
 
+// One block of threads per (sequence, KV head) and segment a.seg +
+// blockIdx.y; segment a.seg + y writes its list and counts at list +
+// y * list_stride and counts + y * count_stride (whole-pass form: every
+// segment's list in one launch).
 __global__ __launch_bounds__(256) void hist_blocks_kernel(const int32_t* __restrict__ sel,
                                                           HistEntry* __restrict__ list,
                                                           int* __restrict__ counts, BwdArgs a,
-                                                          int maxd) {
+                                                          int maxd, size_t list_stride,
+                                                          int count_stride) {
   __shared__ unsigned long long s_mask[kMaxCandidates];  // per history block
   __shared__ int s_wtot[4];
   const int bg = blockIdx.x;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int seg = a.seg + (int)blockIdx.y;
+  list += blockIdx.y * list_stride;
+  counts += blockIdx.y * count_stride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nb = a.seg * a.L / a.Bh;
+  const int nb = seg * a.L / a.Bh;
   const int n_ent = a.nqb * a.K;
-  const int32_t* rows = sel + ((size_t)(b * a.Hkv + g) * a.nqb_all + (size_t)a.seg * a.nqb) * a.K;
+  const int32_t* rows = sel + ((size_t)(b * a.Hkv + g) * a.nqb_all + (size_t)seg * a.nqb) * a.K;
   for (int i = tid; i < nb; i += 256) s_mask[i] = 0ull;
   __syncthreads();
   // bit j of block x's mask: query block j chose x (integer OR: the result
@@ -1442,7 +1450,7 @@ hipError_t bwd_bf16(const Prob& p, const void* q, const void* k, const void* v,
     HistEntry* list =
         reinterpret_cast<HistEntry*>(base + round256((size_t)p.B * p.Hkv * sizeof(int)));
     HGA_LAUNCH(HGA_K_BWD_HIST, hist_blocks_kernel, dim3(p.B * p.Hkv), dim3(256), 0, st, sel, list,
-                       counts, a, maxd);
+               counts, a, maxd, (size_t)0, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int ntpb = (p.Bh + 31) / 32;
@@ -1544,26 +1552,51 @@ hipError_t launch_zero(float* p, size_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
-size_t hist_ws_bytes(const Prob& p) { return hist_list_bytes(p); }
+
+
+// Segment seg's list in the lists workspace (hist_lists_bytes): segments
+// 1 .. S/L-1, each hist_list_bytes, counts first.
+static void hist_list_of(const Prob& p, void* lists_ws, int seg, int** counts,
+                         HistEntry** list) {
+  char* base = reinterpret_cast<char*>(lists_ws) + (size_t)(seg - 1) * hist_list_bytes(p);
+  *counts = reinterpret_cast<int*>(base);
+  *list = reinterpret_cast<HistEntry*>(base + round256((size_t)p.B * p.Hkv * sizeof(int)));
+}
+
+size_t hist_lists_bytes(const Prob& p) {
+  return (size_t)(p.S / p.L > 1 ? p.S / p.L - 1 : 1) * hist_list_bytes(p);
+}
+
+hipError_t launch_hist_lists(const Prob& p, const int32_t* sel, void* lists_ws,
+                             hipStream_t st) {
+  const int maxd = hist_max_entries(p);
+  const int nseg = p.S / p.L;
+  if (nseg <= 1 || maxd <= 0) return hipSuccess;
+  BwdArgs a = make_args(p, 1);
+  int* counts;
+  HistEntry* list;
+  hist_list_of(p, lists_ws, 1, &counts, &list);
+  const size_t stride = hist_list_bytes(p);  // bytes; both strides below in elements
+  HGA_LAUNCH(HGA_K_BWD_HIST, hist_blocks_kernel, dim3(p.B * p.Hkv, nseg - 1), dim3(256), 0, st,
+             sel, list, counts, a, maxd, stride / sizeof(HistEntry),
+             (int)(stride / sizeof(int)));
+  return hipGetLastError();
+}
 
 hipError_t launch_hist_exact(const Prob& p, const void* q, const void* k, const void* v,
                              const float* lse, const void* dO, const int32_t* sel, int seg,
-                             const float* delta_seg, float* hist_dk, float* hist_dv, void* list_ws,
-                             hipStream_t st) {
+                             const float* delta_seg, float* hist_dk, float* hist_dv,
+                             void* lists_ws, hipStream_t st) {
+  (void)sel;
   if (p.dtype != HGA_BF16 || p.kv_rows != p.S) return hipErrorInvalidValue;
   const int maxd = hist_max_entries(p);
   if (seg <= 0 || maxd <= 0) return hipSuccess;
   BwdArgs a = make_args(p, seg);
   a.hdk = hist_dk;
   a.hdv = hist_dv;
-  char* base = reinterpret_cast<char*>(list_ws);
-  int* counts = reinterpret_cast<int*>(base);
-  HistEntry* list =
-      reinterpret_cast<HistEntry*>(base + round256((size_t)p.B * p.Hkv * sizeof(int)));
-  HGA_LAUNCH(HGA_K_BWD_HIST, hist_blocks_kernel, dim3(p.B * p.Hkv), dim3(256), 0, st, sel, list,
-             counts, a, maxd);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  int* counts;
+  HistEntry* list;
+  hist_list_of(p, lists_ws, seg, &counts, &list);
   const int ntpb = (p.Bh + 31) / 32;
   if (p.D == 64)
     HGA_LAUNCH(HGA_K_BWD_HIST, (dkdv_hist_kernel<64>), dim3(256), dim3(512), 0, st,

@@ -83,14 +83,18 @@ hipError_t launch_bwd_pass(const Prob& p, const void* q, const void* k, const vo
                            int nseg, void* dq, void* dk, void* dv, const float* delta,
                            size_t dstride, hipStream_t st, const float* hist_dk = nullptr,
                            const float* hist_dv = nullptr);
-// Exact gradient, segment seg: its queries' dK/dV for the history blocks
-// they selected, added into the fp32 sums hist_dk / hist_dv (segment seg's
-// delta rows at delta_seg; list_ws: hist_ws_bytes of scratch).
+// Exact gradient over a whole pass: launch_hist_lists lists, for every
+// segment 1 .. S/L-1 at once, the distinct history blocks its query blocks
+// selected (into lists_ws, hist_lists_bytes); launch_hist_exact then adds
+// segment seg's queries' dK/dV for those blocks into the fp32 sums hist_dk /
+// hist_dv (segment seg's delta rows at delta_seg).
+hipError_t launch_hist_lists(const Prob& p, const int32_t* sel, void* lists_ws,
+                             hipStream_t st);
 hipError_t launch_hist_exact(const Prob& p, const void* q, const void* k, const void* v,
                              const float* lse, const void* dO, const int32_t* sel, int seg,
-                             const float* delta_seg, float* hist_dk, float* hist_dv, void* list_ws,
-                             hipStream_t st);
-size_t hist_ws_bytes(const Prob& p);
+                             const float* delta_seg, float* hist_dk, float* hist_dv,
+                             void* lists_ws, hipStream_t st);
+size_t hist_lists_bytes(const Prob& p);
 // Stores zeros into n floats (n % 4 == 0, 16-byte aligned).
 hipError_t launch_zero(float* p, size_t n, hipStream_t st);
 size_t bwd_workspace_bytes(const Prob& p);

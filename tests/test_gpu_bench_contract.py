@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 LEGS_OFF = ["--no-dense-self", "--no-dense-sdpa", "--no-decode", "--no-diverse",
             "--no-host-tier", "--no-hbm", "--no-sequential", "--no-workloads", "--no-exact",
-            "--no-tier-131k", "--no-peaks"]
+            "--no-tier-131k", "--no-peaks", "--no-fwd-only"]
 
 
 def test_bench_prints_one_contract_line():
