@@ -339,7 +339,11 @@ int hga_segment_step_host(const hga_config* cfg, int32_t seg, int32_t flags, con
  * seg+1 runs while the attention of segment seg does (the selection of
  * seg+1 comes before that attention starts), and waits only for the
  * attention of seg-1, the last reader of its window (stream2 NULL:
- * everything on stream, in order).  Results equal the steps' bit for bit.  When the call returns,
+ * everything on stream, in order).  The overlap needs the two streams on
+ * different hardware queues: HIP runs streams on a few of them
+ * (GPU_MAX_HW_QUEUES, four by default), and streams that share one run one
+ * after the other (results are the same, only slower).  Results equal the
+ * steps' bit for bit.  When the call returns,
  * everything it enqueued is ordered before later work on `stream`; both
  * streams at default priority.  flags: HGA_STEP_BWD or 0.  ws:
  * hga_workspace_size(cfg, HGA_OP_PASS_HOST) bytes.  The library keeps five

@@ -441,7 +441,7 @@ def segment_pass_host(cfg: Config, q, k_host, v_host, summ, sel, o, lse=None, do
 class Buffers:
     """Device tensors of one layer's segmented pass (allocated with torch)."""
 
-    def __init__(self, cfg: Config, device="cuda", bwd: bool = True):
+    def __init__(self, cfg: Config, device="cuda", bwd: bool = True, stream2=None):
         torch = _torch()
         s = Shapes(cfg)
         self.cfg = cfg
@@ -458,7 +458,9 @@ class Buffers:
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         else:
             self.dq = self.dk = self.dv = self.ws = None
-        self.stream2 = torch.cuda.Stream(device=device)  # default priority
+        # the second stream of the two-stream forms (default priority); a new
+        # one unless the caller passes its own
+        self.stream2 = stream2 if stream2 is not None else torch.cuda.Stream(device=device)
 
     def run_pass(self, q, k, v, do=None, bwd: bool = True, segments=None,
                  two_streams: bool = True, per_step: bool = False) -> None:
