@@ -47,7 +47,9 @@
  *  (f32) and hga_segment_pass_host use to hand work between their two
  *  streams -- created on a calling thread's first such call on a device,
  *  kept for that thread and device and reused by its later calls, never
- *  freed.  Every other entry point keeps nothing.  Scratch space comes from
+ *  freed; and the scratch array of hga_segment_pass_noalloc, one per GPU,
+ *  which holds the last call's intermediate values.  Every other entry
+ *  point keeps nothing.  Scratch space comes from
  *  `ws`, of at least hga_workspace_size() bytes.  Results are bitwise deterministic
  *  (no floating-point atomics).
  *
