@@ -16,6 +16,7 @@ namespace hga {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMultiThreads = 512;  // select_multi_kernel: two mean slices
 
 // Where the query rows of selection unit j are and where its k indices go:
 // q rows qS*(b*Hq + h) + q0 + j*qstep + [0, nrows) (q holds qS rows per
@@ -108,18 +109,23 @@ __device__ void bitonic_desc(unsigned long long* a, int n) {
 // qbar[d] = mean over the G heads of group g and the nrows query rows of
 // unit j of q (float32): every row load of a thread in flight at once, then
 // an LDS fold over the R row slots.  Ends with a barrier (qbar is ready).
+// Run by kThreads threads (tid = 0 .. kThreads-1); a block of several such
+// slices forms one mean per slice, each with its own part, and a slice with
+// active = false only joins the barriers.  A mean depends only on the unit,
+// never on the slice or block that forms it.
 template <typename T, int D>
-__device__ __forceinline__ void group_query_mean(const T* __restrict__ q, const SelGeom& geo,
-                                                 int b, int g, int j, int Hq, int G,
-                                                 float (*part)[D + 1], float* qbar) {
+__device__ __forceinline__ void group_query_mean_slice(const T* __restrict__ q,
+                                                       const SelGeom& geo, int b, int g, int j,
+                                                       int Hq, int G, float (*part)[D + 1],
+                                                       float* qbar, int tid, bool active) {
   constexpr int EL = Vec16<T>::N;
   constexpr int C = D / EL;
   constexpr int R = kThreads / C;
-  const int c = threadIdx.x % C, r = threadIdx.x / C;
+  const int c = tid % C, r = tid / C;
   float acc[EL];
 #pragma unroll
   for (int e = 0; e < EL; ++e) acc[e] = 0.f;
-  const int rows = G * geo.nrows;
+  const int rows = active ? G * geo.nrows : 0;
   constexpr int U = 16;  // row loads in flight per thread (raw 16-byte vectors)
   for (int row0 = r; row0 < rows; row0 += U * R) {
     uint4 f[U];
@@ -143,17 +149,29 @@ __device__ __forceinline__ void group_query_mean(const T* __restrict__ q, const 
       for (int e = 0; e < EL; ++e) acc[e] += x[e];
     }
   }
+  if (active) {
 #pragma unroll
-  for (int e = 0; e < EL; ++e) part[r][c * EL + e] = acc[e];
-  __syncthreads();
-  const float inv = 1.0f / (float)rows;
-  for (int d = threadIdx.x; d < D; d += kThreads) {
-    float sum = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) sum += part[rr][d];
-    qbar[d] = sum * inv;
+    for (int e = 0; e < EL; ++e) part[r][c * EL + e] = acc[e];
   }
   __syncthreads();
+  if (active) {
+    const float inv = 1.0f / (float)rows;
+    for (int d = tid; d < D; d += kThreads) {
+      float sum = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) sum += part[rr][d];
+      qbar[d] = sum * inv;
+    }
+  }
+  __syncthreads();
+}
+
+// The mean of unit j formed by a whole block of kThreads threads.
+template <typename T, int D>
+__device__ __forceinline__ void group_query_mean(const T* __restrict__ q, const SelGeom& geo,
+                                                 int b, int g, int j, int Hq, int G,
+                                                 float (*part)[D + 1], float* qbar) {
+  group_query_mean_slice<T, D>(q, geo, b, g, j, Hq, G, part, qbar, (int)threadIdx.x, true);
 }
 
 // Scores of summary rows, 8 lanes per row: a wave covers 8 rows per pass and
@@ -165,37 +183,37 @@ __device__ __forceinline__ void group_query_mean(const T* __restrict__ q, const 
 // leaves the same value in the 8 lanes of the row.  Every selection kernel
 // scores through these two functions, so a row's fp32 score is the same
 // whichever kernel forms it.
-template <int D>
+template <int D, int NP = 8>
 struct RowPieces {
   static constexpr int F = D / 32;  // pieces per lane and row
-  float4 x[8][F];
+  float4 x[NP][F];                  // NP passes of 8 rows
 };
 
-// Requests the pieces of rows row0 + 8p + lane / 8 (p < 8) of sbase; rows at
-// or past nrows read row 0 instead (their scores are not used).
-template <int D>
-__device__ __forceinline__ void load_rows64(RowPieces<D>& rp, const float* __restrict__ sbase,
+// Requests the pieces of rows row0 + 8p + lane / 8 (p < NP) of sbase; rows
+// at or past nrows read row 0 instead (their scores are not used).
+template <int D, int NP = 8>
+__device__ __forceinline__ void load_rows64(RowPieces<D, NP>& rp, const float* __restrict__ sbase,
                                             int row0, int nrows, int lane) {
   const int rr = lane >> 3, sub = lane & 7;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
+  for (int p = 0; p < NP; ++p) {
     const int r = row0 + 8 * p + rr;
     const float4* rowp =
         reinterpret_cast<const float4*>(sbase + (size_t)(r < nrows ? r : 0) * D);
 #pragma unroll
-    for (int u = 0; u < RowPieces<D>::F; ++u) rp.x[p][u] = rowp[8 * u + sub];
+    for (int u = 0; u < RowPieces<D, NP>::F; ++u) rp.x[p][u] = rowp[8 * u + sub];
   }
 }
 
 // Score of the row of pass p against the query mean qm (D floats in LDS).
 // Called by whole waves (the butterfly needs every lane).
-template <int D>
-__device__ __forceinline__ float row_score8(const RowPieces<D>& rp, int p,
+template <int D, int NP = 8>
+__device__ __forceinline__ float row_score8(const RowPieces<D, NP>& rp, int p,
                                             const float* qm, int lane) {
   const int sub = lane & 7;
   float s = 0.f;
 #pragma unroll
-  for (int u = 0; u < RowPieces<D>::F; ++u) {
+  for (int u = 0; u < RowPieces<D, NP>::F; ++u) {
     const float4 qv = *reinterpret_cast<const float4*>(&qm[4 * (8 * u + sub)]);
     const float4 x = rp.x[p][u];
     s = fmaf(qv.x, x.x, s);
@@ -318,20 +336,23 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 // j0+nu-1 of segment seg share the segment's candidate blocks, so each
 // thread reads a candidate's summary row once and forms the nu scores from
 // it (the per-unit kernel reads every summary row once per query block).
-//   1. qbar of each of the nu query blocks (group_query_mean, one after the
-//      other, float32, the same sums as select_kernel's);
-//   2. score[u][i] = qbar_u . summ_i, one candidate per thread;
-//   3. + 4. wave w picks the k best of query blocks w, w+4, ... (wave_topk).
+//   1. qbar of each of the nu query blocks: the block's two halves of 256
+//      threads form two means side by side (group_query_mean_slice,
+//      float32, the same sums as select_kernel's);
+//   2. score[u][i] = qbar_u . summ_i, 8 lanes per candidate row;
+//   3. + 4. wave w picks the k best of query block w (wave_topk).
 // ---------------------------------------------------------------------------
 template <typename T, int D, int E, int U>
-__global__ __launch_bounds__(kThreads) void select_multi_kernel(
+__global__ __launch_bounds__(kMultiThreads, 4) void select_multi_kernel(
     const T* __restrict__ q, const float* __restrict__ summ,
     int32_t* __restrict__ sel, SelGeom geo, int K, int Hq, int Hkv, int G, int nblk) {
   constexpr int EL = Vec16<T>::N;
   constexpr int C = D / EL;
   constexpr int R = kThreads / C;
   constexpr int NC = 64 * E;  // candidates a wave's search holds
-  __shared__ float part[R][D + 1];
+  constexpr int NS = kMultiThreads / kThreads;  // slices forming means side by side
+  static_assert(U % NS == 0, "every slice reaches the same barriers");
+  __shared__ float part[NS][R][D + 1];
   __shared__ __attribute__((aligned(16))) float qbar[U][D];
   __shared__ float s_score[U][NC];
 
@@ -346,32 +367,39 @@ __global__ __launch_bounds__(kThreads) void select_multi_kernel(
   int32_t* out = sel + ((size_t)(b * Hkv + g) * geo.out_units + geo.out_j0 + j0) * K;
 
   if (nb <= K) {  // every history block is taken (none at seg 0)
-    for (int t = threadIdx.x; t < nu * K; t += kThreads) {
+    for (int t = threadIdx.x; t < nu * K; t += kMultiThreads) {
       const int kk = t % K;
       out[t] = kk < nb ? kk : -1;
     }
     return;
   }
 
-  // 1. the query-block means
-  for (int u = 0; u < nu; ++u) group_query_mean<T, D>(q, geo, b, g, j0 + u, Hq, G, part, qbar[u]);
+  // 1. the query-block means, NS at a time (slice s forms unit u0 + s)
+  {
+    const int s = threadIdx.x / kThreads, tid = threadIdx.x % kThreads;
+    for (int u0 = 0; u0 < nu; u0 += NS) {
+      const int u = u0 + s;  // < U, since u0 <= U - NS
+      group_query_mean_slice<T, D>(q, geo, b, g, j0 + u, Hq, G, part[s], qbar[u], tid, u < nu);
+    }
+  }
 
-  // 2. scores, 64 candidates per wave and round (8 lanes per row), every
+  // 2. scores, 32 candidates per wave and round (8 lanes per row), every
   // unit from one read of the row
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const float* sbase = summ + (size_t)(b * Hkv + g) * nblk * D;
-  for (int c0 = 0; c0 < nb; c0 += kThreads) {
-    const int row0 = c0 + wave * 64;
+  constexpr int NP = 4;  // passes of 8 rows per wave and round
+  for (int c0 = 0; c0 < nb; c0 += kMultiThreads / 64 * 8 * NP) {
+    const int row0 = c0 + wave * 8 * NP;
     if (row0 < nb) {  // uniform over the wave
-      RowPieces<D> rp;
-      load_rows64<D>(rp, sbase, row0, nb, lane);
+      RowPieces<D, NP> rp;
+      load_rows64<D, NP>(rp, sbase, row0, nb, lane);
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
+      for (int p = 0; p < NP; ++p) {
         const int r = row0 + 8 * p + (lane >> 3);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           if (u < nu) {  // uniform
-            const float sc = row_score8<D>(rp, p, qbar[u], lane);
+            const float sc = row_score8<D, NP>(rp, p, qbar[u], lane);
             if ((lane & 7) == 0 && r < nb) s_score[u][r] = sc;
           }
         }
@@ -381,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void select_multi_kernel(
   __syncthreads();
 
   // 3. + 4. the k best of each query block, one wave per query block
-  for (int u = wave; u < nu; u += kThreads / 64)
+  for (int u = wave; u < nu; u += kMultiThreads / 64)
     wave_topk<E>(s_score[u], nb, K, out + (size_t)u * K, lane);
 }
 
@@ -562,7 +590,7 @@ hipError_t select_multi_launch(const Prob& p, const void* q, const float* summ,
   constexpr int U = 8;
   const int gps = (geo.per_seg + U - 1) / U;
   dim3 grid(nseg * gps, p.Hkv, p.B);
-  HGA_LAUNCH(HGA_K_SELECT, (select_multi_kernel<T, D, E, U>), grid, dim3(kThreads), 0, st,
+  HGA_LAUNCH(HGA_K_SELECT, (select_multi_kernel<T, D, E, U>), grid, dim3(kMultiThreads), 0, st,
              (const T*)q, summ, sel, geo, p.K, p.Hq, p.Hkv, p.G, p.nblk);
   return hipGetLastError();
 }
